@@ -1,0 +1,188 @@
+"""CPU oracle for the N-gram embedding forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of
+bench.py may import this module. The library (gram_embedding_layer_amd) never imports it and
+shares no code, table or helper with it.
+
+Source: the deep-notes page on "Scaling Embeddings Outperforms Scaling Experts in Language
+Models" (Meituan LongCat team), section A2 "N-gram embedding layer":
+  * the polynomial rolling hash  H_n(t_{i-n+1..i}) = (sum_{j=0}^{n-1} t_{i-j} * V0^j) mod V_n;
+  * the final (Over-Encoding) form
+        e_i = ( E_0(t_i) + sum_{n=2}^{N} sum_{k=1}^{K} W_{n,k} E_{n,k}(H_{n,k}(t_{i-n+1..i})) )
+              / ((N-1)K + 1),
+    with E_{n,k} in R^{V_{n,k} x D/((N-1)K)} and W_{n,k} in R^{D x D/((N-1)K)};
+  * K hash functions per order that differ only in their modulus V_{n,k} (same section, and
+    section 3.2.3 on K as the number of distinct hash functions).
+Section 4.2 (N-gram cache) motivates the decode oracle; its semantics are a reading:
+the cache holds committed ids, a decode step's outputs equal a prefill over the whole
+history followed by the new ids, and a commit appends accepted ids.
+
+Readings where the pages are silent:
+  * positions before a sequence's first token take the pad id 0, never ids of another
+    sequence packed in the same batch;
+  * sub-table order s = (n-2)*K + (k-1), n-major;
+  * N = 1 has no sub-tables: e_i = E_0(t_i);
+  * token ids must lie in [0, V0) (the hash reads them as base-V0 digits).
+
+Arithmetic: hashes are exact Python integers (the n-gram value is formed as a sum of powers,
+not by Horner's rule, and reduced once); embeddings are computed in float64.
+Parity pins: tests/test_oracle_pins.py. Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Callable, List, Sequence
+
+import numpy as np
+
+PAD_ID = 0
+
+
+def num_subtables(N: int, K: int) -> int:
+    """(N-1)K sub-tables: K for each order n = 2..N (section A2, final form)."""
+    return (N - 1) * K
+
+
+def subtable_order(N: int, K: int) -> List[tuple]:
+    """(n, k) for s = 0..S-1, n-major."""
+    return [(n, k) for n in range(2, N + 1) for k in range(1, K + 1)]
+
+
+def check_config(V0: int, D: int, N: int, K: int, V: Sequence[int]) -> None:
+    if N < 1 or K < 1 or V0 < 1 or D < 1:
+        raise ValueError("N, K, V0 and D must be positive")
+    S = num_subtables(N, K)
+    if len(V) != S:
+        raise ValueError(f"need {S} sub-table sizes, got {len(V)}")
+    if any(int(v) < 1 for v in V):
+        raise ValueError("sub-table sizes must be positive")
+    if S and D % S:
+        raise ValueError("D must be a multiple of (N-1)K (sub-table width D/((N-1)K))")
+
+
+def context(seq: Sequence[int], i: int, n: int) -> List[int]:
+    """[t_i, t_{i-1}, ..., t_{i-n+1}] of one sequence, pad id 0 before its start."""
+    return [int(seq[i - j]) if i - j >= 0 else PAD_ID for j in range(n)]
+
+
+def ngram_value(ctx: Sequence[int], n: int, V0: int) -> int:
+    """sum_{j=0}^{n-1} t_{i-j} * V0^j as an unbounded integer (t_i is the lowest digit)."""
+    return sum(int(ctx[j]) * V0 ** j for j in range(n))
+
+
+def hash_indices(V0: int, N: int, K: int, V: Sequence[int], tokens: Sequence[int],
+                 cu_seqlens: Sequence[int]) -> np.ndarray:
+    """int64 [T, (N-1)K]: H_{n,k} of every position of every packed sequence.
+
+    tokens: all sequences back to back; cu_seqlens: offsets [B+1], cu_seqlens[0] = 0."""
+    S = num_subtables(N, K)
+    tokens = [int(t) for t in tokens]
+    T = len(tokens)
+    if any(t < 0 or t >= V0 for t in tokens):
+        raise ValueError("token id outside [0, V0)")
+    if int(cu_seqlens[0]) != 0 or int(cu_seqlens[-1]) != T:
+        raise ValueError("cu_seqlens must run from 0 to the token count")
+    idx = np.zeros((T, S), dtype=np.int64)
+    order = subtable_order(N, K)
+    for b in range(len(cu_seqlens) - 1):
+        lo, hi = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if hi < lo:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        seq = tokens[lo:hi]
+        for i in range(hi - lo):
+            ctx = context(seq, i, N)
+            for s, (n, k) in enumerate(order):
+                idx[lo + i, s] = ngram_value(ctx, n, V0) % int(V[s])
+    return idx
+
+
+RowFetch = Callable[[int, np.ndarray], np.ndarray]
+"""fetch(s, rows) -> float array [len(rows), width]; s = -1 means E_0, else sub-table s."""
+
+
+def embed_from_indices(D: int, N: int, K: int, tokens: Sequence[int], idx: np.ndarray,
+                       fetch: RowFetch, W_blocks: Sequence[np.ndarray]) -> np.ndarray:
+    """float64 [T, D]: the final form of section A2 given the hash indices.
+
+    W_blocks[s] is W_{n,k} [D, d] for s = (n-2)K + (k-1)."""
+    S = num_subtables(N, K)
+    tok = np.asarray(tokens, dtype=np.int64)
+    acc = np.asarray(fetch(-1, tok), dtype=np.float64).copy()              # E_0(t_i)
+    if acc.shape != (len(tok), D):
+        raise ValueError("E_0 rows must be [T, D]")
+    for s in range(S):
+        rows = np.asarray(fetch(s, idx[:, s]), dtype=np.float64)           # E_{n,k}(H_{n,k})
+        Wnk = np.asarray(W_blocks[s], dtype=np.float64)                     # [D, d]
+        if rows.shape[1] != D // S or Wnk.shape != (D, D // S):
+            raise ValueError("sub-table rows must be [T, D/S] and W_{n,k} [D, D/S]")
+        acc += rows @ Wnk.T                                                 # W_{n,k} E_{n,k}(.)
+    return acc / float(S + 1)                                               # / ((N-1)K + 1)
+
+
+def table_fetch(E0, E_list) -> RowFetch:
+    """Row fetch over in-memory tables (numpy arrays or anything np.asarray accepts)."""
+    E0 = np.asarray(E0, dtype=np.float64)
+    E_list = [np.asarray(e, dtype=np.float64) for e in E_list]
+
+    def fetch(s: int, rows: np.ndarray) -> np.ndarray:
+        table = E0 if s < 0 else E_list[s]
+        return table[np.asarray(rows, dtype=np.int64)]
+    return fetch
+
+
+def prefill(V0: int, D: int, N: int, K: int, V: Sequence[int], tokens: Sequence[int],
+            cu_seqlens: Sequence[int], fetch: RowFetch, W_blocks: Sequence[np.ndarray]):
+    """(idx int64 [T, S], e float64 [T, D]) for packed sequences."""
+    check_config(V0, D, N, K, V)
+    idx = hash_indices(V0, N, K, V, tokens, cu_seqlens)
+    return idx, embed_from_indices(D, N, K, tokens, idx, fetch, W_blocks)
+
+
+class DecodeOracle:
+    """Decode with an N-gram cache, as plain bookkeeping over each sequence's full history.
+
+    step(new) gives, for each sequence b, the indices and embeddings of the positions that
+    `new[b]` would occupy after the history, as a prefill of history + new would.
+    commit(new, n_accept) appends the first n_accept[b] of them to the history."""
+
+    def __init__(self, V0: int, D: int, N: int, K: int, V: Sequence[int],
+                 histories: Sequence[Sequence[int]]):
+        check_config(V0, D, N, K, V)
+        self.V0, self.D, self.N, self.K, self.V = V0, D, N, K, [int(v) for v in V]
+        self.hist = [[int(t) for t in h] for h in histories]
+
+    def step_indices(self, new: Sequence[Sequence[int]]) -> List[np.ndarray]:
+        out = []
+        order = subtable_order(self.N, self.K)
+        for b, toks in enumerate(new):
+            seq = self.hist[b] + [int(t) for t in toks]
+            if any(t < 0 or t >= self.V0 for t in toks):
+                raise ValueError("token id outside [0, V0)")
+            base = len(self.hist[b])
+            idx = np.zeros((len(toks), len(order)), dtype=np.int64)
+            for j in range(len(toks)):
+                ctx = context(seq, base + j, self.N)
+                for s, (n, k) in enumerate(order):
+                    idx[j, s] = ngram_value(ctx, n, self.V0) % self.V[s]
+            out.append(idx)
+        return out
+
+    def step(self, new: Sequence[Sequence[int]], fetch: RowFetch,
+             W_blocks: Sequence[np.ndarray]):
+        idxs = self.step_indices(new)
+        embs = [embed_from_indices(self.D, self.N, self.K, list(toks), idx, fetch, W_blocks)
+                for toks, idx in zip(new, idxs)]
+        return idxs, embs
+
+    def commit(self, new: Sequence[Sequence[int]], n_accept: Sequence[int]) -> None:
+        for b, toks in enumerate(new):
+            a = int(n_accept[b])
+            if a < 0 or a > len(toks):
+                raise ValueError("n_accept outside [0, n_new]")
+            self.hist[b].extend(int(t) for t in toks[:a])
+
+
+def param_count(V0: int, D: int, N: int, K: int, V: Sequence[int]) -> dict:
+    """Parameter counts of the layer's tables (section A2: E_0, E_{n,k}, W_{n,k} shapes)."""
+    S = num_subtables(N, K)
+    d = D // S if S else 0
+    return {"E0": V0 * D, "ngram_tables": sum(int(v) * d for v in V), "projections": S * D * d}

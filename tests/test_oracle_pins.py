@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics, not by itself.
+
+Hash (section A2, polynomial rolling hash): hand-worked values, decimal and binary digit
+strings, an exhaustive base-7 count, Horner's rule as an independent algorithm, the pad
+convention at sequence starts, and packing independence.
+Final form (section A2): hand-worked rational values, special cases that reduce to plain
+indexing (N = 1, identity and zero projections), the stacked-matrix form, linearity,
+locality, the parameter-count identity, and decode == prefill.
+test_pins_catch_planted_mistakes plants plausible mistakes in the oracle and checks that
+these pins fail.
+"""
+import json
+import os
+from collections import Counter
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import ngram_oracle as O
+from workloads import cu_seqlens_from_lengths
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _one_seq(tokens):
+    return [0, len(tokens)]
+
+
+# ------------------------------------------------------------------ hash
+
+def check_hash_golden():
+    g = _load("hash_handworked_v1000.json")
+    idx = oracle.hash_indices(g["V0"], g["N"], g["K"], g["V"], g["tokens"], _one_seq(g["tokens"]))
+    np.testing.assert_array_equal(idx, np.array(g["idx"]))
+
+
+def test_hash_handworked_v1000():
+    check_hash_golden()
+
+
+def _digits_to_int(digits, base):
+    """Most significant digit first; uses Python's own base parser (no arithmetic of ours)."""
+    alphabet = "0123456789abcdefghijklmnopqrstuvwxyz"
+    return int("".join(alphabet[d] for d in digits), base)
+
+
+def check_hash_decimal():
+    # V0 = 10: the n-gram ending at t_i is the decimal number t_{i-n+1} ... t_{i-1} t_i.
+    rng = np.random.default_rng(1)
+    seq = [int(x) for x in rng.integers(0, 10, size=40)]
+    seq[10:13] = [3, 1, 4]
+    N, K = 4, 1
+    V = [10 ** n + 7 for n in range(2, N + 1)]      # larger than any n-digit value
+    idx = oracle.hash_indices(10, N, K, V, seq, _one_seq(seq))
+    assert idx[12, 1] == 314                         # 3-gram (3, 1, 4)
+    for i in range(len(seq)):
+        for n in range(2, N + 1):
+            window = [seq[i - j] if i - j >= 0 else 0 for j in range(n - 1, -1, -1)]
+            assert idx[i, n - 2] == _digits_to_int(window, 10) % V[n - 2]
+
+
+def test_hash_decimal_digits():
+    check_hash_decimal()
+
+
+def test_hash_power_of_two_base_is_bit_packing():
+    bits, N, K = 5, 4, 2
+    V0 = 1 << bits
+    V = [(1 << 40) + 15, (1 << 40) + 21, (1 << 40) + 31, (1 << 40) + 33, 97, 101]
+    rng = np.random.default_rng(2)
+    seq = [int(x) for x in rng.integers(0, V0, size=30)]
+    idx = oracle.hash_indices(V0, N, K, V, seq, _one_seq(seq))
+    for i in range(len(seq)):
+        for s, (n, k) in enumerate(oracle.subtable_order(N, K)):
+            x = 0
+            for j in range(n):
+                if i - j >= 0:
+                    x |= seq[i - j] << (bits * j)
+            assert idx[i, s] == x % V[s]
+
+
+def test_hash_exhaustive_base7_trigrams():
+    # All 343 trigrams over V0 = 7 as separate length-3 sequences: with a large modulus the
+    # 3-gram index is the base-7 number (a bijection onto 0..342); with modulus 13 the bucket
+    # counts equal a direct count.
+    trigrams = [(a, b, c) for a in range(7) for b in range(7) for c in range(7)]
+    tokens = [t for tri in trigrams for t in tri]
+    cu = cu_seqlens_from_lengths([3] * len(trigrams))
+    idx = oracle.hash_indices(7, 3, 1, [101, 1000], tokens, cu)
+    last = idx[2::3, 1]
+    assert sorted(last.tolist()) == list(range(343))
+    for tri, v in zip(trigrams, last):
+        assert v == _digits_to_int(list(tri), 7)
+    idx13 = oracle.hash_indices(7, 3, 1, [101, 13], tokens, cu)[2::3, 1]
+    direct = Counter(_digits_to_int(list(tri), 7) % 13 for tri in trigrams)
+    assert Counter(idx13.tolist()) == direct
+
+
+def _horner_mod(ctx_oldest_first, V0, m):
+    x = 0
+    for t in ctx_oldest_first:
+        x = (x * V0 + t) % m
+    return x
+
+
+@settings(max_examples=60, deadline=None)
+@given(V0=st.integers(2, 300), N=st.integers(1, 5), K=st.integers(1, 4),
+       data=st.data())
+def test_hash_matches_horner(V0, N, K, data):
+    S = (N - 1) * K
+    V = data.draw(st.lists(st.integers(1, 5000), min_size=S, max_size=S))
+    lengths = data.draw(st.lists(st.integers(0, 9), min_size=1, max_size=4))
+    tokens = data.draw(st.lists(st.integers(0, V0 - 1), min_size=sum(lengths),
+                                max_size=sum(lengths)))
+    cu = cu_seqlens_from_lengths(lengths)
+    idx = oracle.hash_indices(V0, N, K, V, tokens, cu)
+    assert idx.shape == (len(tokens), S)
+    for b in range(len(lengths)):
+        lo = cu[b]
+        for i in range(lengths[b]):
+            for s, (n, k) in enumerate(oracle.subtable_order(N, K)):
+                ctx = [tokens[lo + i - j] if i - j >= 0 else 0 for j in range(n - 1, -1, -1)]
+                assert idx[lo + i, s] == _horner_mod(ctx, V0, V[s])
+
+
+def test_hash_sequence_start_uses_pad_zero():
+    V0, N, K, V = 50, 4, 2, [7, 11, 13, 17, 19, 23]
+    seqs = [[9, 3, 48], [1], [0, 0, 5, 7, 49]]
+    cu = cu_seqlens_from_lengths([len(s) for s in seqs])
+    idx = oracle.hash_indices(V0, N, K, V, sum(seqs, []), cu)
+    for b, seq in enumerate(seqs):
+        first = idx[cu[b]]
+        # every n-gram at position 0 is (pad, ..., pad, t_0) = t_0
+        assert first.tolist() == [seq[0] % v for v in V]
+
+
+def test_hash_packing_independence():
+    V0, N, K, V = 1000, 3, 2, [5003, 7001, 6007, 8009]
+    rng = np.random.default_rng(3)
+    seqs = [[int(x) for x in rng.integers(0, V0, size=L)] for L in (5, 1, 12, 0, 3)]
+    cu = cu_seqlens_from_lengths([len(s) for s in seqs])
+    packed = oracle.hash_indices(V0, N, K, V, sum(seqs, []), cu)
+    for b, seq in enumerate(seqs):
+        alone = oracle.hash_indices(V0, N, K, V, seq, _one_seq(seq))
+        np.testing.assert_array_equal(packed[cu[b]:cu[b + 1]], alone)
+
+
+def test_hash_rejects_bad_ids():
+    with pytest.raises(ValueError):
+        oracle.hash_indices(10, 2, 1, [7], [3, 10], [0, 2])
+    with pytest.raises(ValueError):
+        oracle.hash_indices(10, 2, 1, [7], [3, -1], [0, 2])
+
+
+# ------------------------------------------------------------------ final form
+
+def _case_arrays(c):
+    E0 = np.array(c["E0"], dtype=np.float64)
+    E = [np.array(e, dtype=np.float64) for e in c["E"]]
+    W = [np.array(w, dtype=np.float64) for w in c["W"]]
+    return E0, E, W
+
+
+def check_embed_golden():
+    g = _load("embed_handworked_small.json")
+    for c in g["cases"]:
+        E0, E, W = _case_arrays(c)
+        idx, e = oracle.prefill(c["V0"], c["D"], c["N"], c["K"], c["V"], c["tokens"],
+                                _one_seq(c["tokens"]), oracle.table_fetch(E0, E), W)
+        np.testing.assert_array_equal(idx, np.array(c["idx"]))
+        want = np.array([[float(Fraction(p, q)) for p, q in row] for row in c["e"]])
+        np.testing.assert_allclose(e, want, rtol=0, atol=1e-14)
+
+
+def test_embed_handworked():
+    check_embed_golden()
+
+
+def _random_case(rng, V0=40, D=24, N=3, K=2, lengths=(7, 1, 5)):
+    S = (N - 1) * K
+    d = D // S if S else 0
+    V = [int(v) for v in rng.integers(3, 200, size=S)]
+    E0 = rng.standard_normal((V0, D))
+    E = [rng.standard_normal((v, d)) for v in V]
+    W = [rng.standard_normal((D, d)) for _ in range(S)]
+    tokens = [int(x) for x in rng.integers(0, V0, size=sum(lengths))]
+    return V0, D, N, K, V, E0, E, W, tokens, cu_seqlens_from_lengths(lengths)
+
+
+def test_embed_N1_is_plain_lookup():
+    rng = np.random.default_rng(4)
+    E0 = rng.standard_normal((30, 8))
+    tokens = [int(x) for x in rng.integers(0, 30, size=17)]
+    idx, e = oracle.prefill(30, 8, 1, 3, [], tokens, [0, 17], oracle.table_fetch(E0, []), [])
+    assert idx.shape == (17, 0)
+    np.testing.assert_array_equal(e, np.take(E0, tokens, axis=0))
+
+
+def test_embed_identity_projection_is_concatenation():
+    # W_{n,k} = the s-th column block of I_D: the final form becomes
+    # (E_0[t] + [E_s[idx_s] for s in order]) / (S+1), pure indexing (exact in float64).
+    rng = np.random.default_rng(5)
+    V0, D, N, K, V, E0, E, _, tokens, cu = _random_case(rng, D=24, N=4, K=2)
+    S, d = (N - 1) * K, D // ((N - 1) * K)
+    I = np.eye(D)
+    W = [I[:, s * d:(s + 1) * d] for s in range(S)]
+    idx, e = oracle.prefill(V0, D, N, K, V, tokens, cu, oracle.table_fetch(E0, E), W)
+    concat = np.concatenate([np.take(E[s], idx[:, s], axis=0) for s in range(S)], axis=1)
+    np.testing.assert_array_equal(e, (np.take(E0, tokens, axis=0) + concat) / (S + 1))
+
+
+def test_embed_zero_projection():
+    rng = np.random.default_rng(6)
+    V0, D, N, K, V, E0, E, W, tokens, cu = _random_case(rng)
+    W = [np.zeros_like(w) for w in W]
+    _, e = oracle.prefill(V0, D, N, K, V, tokens, cu, oracle.table_fetch(E0, E), W)
+    np.testing.assert_array_equal(e, np.take(E0, tokens, axis=0) / ((N - 1) * K + 1))
+
+
+def test_embed_equals_stacked_matrix_form():
+    # sum_s W_{n,k} row_s == [W_{2,1} | W_{2,2} | ...] @ concat(row_s)
+    rng = np.random.default_rng(7)
+    V0, D, N, K, V, E0, E, W, tokens, cu = _random_case(rng, D=32, N=5, K=2)
+    S = (N - 1) * K
+    idx, e = oracle.prefill(V0, D, N, K, V, tokens, cu, oracle.table_fetch(E0, E), W)
+    g = np.concatenate([E[s][idx[:, s]] for s in range(S)], axis=1)
+    stacked = np.concatenate(W, axis=1)
+    np.testing.assert_allclose(e, (E0[tokens] + g @ stacked.T) / (S + 1), rtol=1e-12, atol=1e-12)
+
+
+def test_embed_linearity_exact():
+    rng = np.random.default_rng(8)
+    V0, D, N, K, V, E0, E, W, tokens, cu = _random_case(rng)
+    _, e1 = oracle.prefill(V0, D, N, K, V, tokens, cu, oracle.table_fetch(E0, E), W)
+    _, e2 = oracle.prefill(V0, D, N, K, V, tokens, cu,
+                           oracle.table_fetch(2 * E0, [2 * x for x in E]), W)
+    np.testing.assert_array_equal(e2, 2 * e1)
+
+
+def test_embed_locality():
+    # Changing t_j may change only e_j .. e_{j+N-1} of the same sequence, and changes e_j.
+    rng = np.random.default_rng(9)
+    V0, D, N, K, V, E0, E, W, tokens, cu = _random_case(rng, N=3, lengths=(12, 9))
+    fetch = oracle.table_fetch(E0, E)
+    _, base = oracle.prefill(V0, D, N, K, V, tokens, cu, fetch, W)
+    for j in (0, 4, 11, 12, 15):
+        t2 = list(tokens)
+        t2[j] = (t2[j] + 1) % V0
+        _, e = oracle.prefill(V0, D, N, K, V, t2, cu, fetch, W)
+        changed = np.nonzero(np.any(e != base, axis=1))[0].tolist()
+        seq_end = 12 if j < 12 else 21
+        allowed = set(range(j, min(j + N, seq_end)))
+        assert set(changed) <= allowed and j in changed
+
+
+def test_param_count_invariant_in_N_and_K():
+    # Sub-table width D/((N-1)K): with every V_{n,k} = V the n-gram tables hold V*D
+    # parameters and the projections D*D, whatever N and K (section A2).
+    D, V = 240, 1009
+    for N in range(2, 7):
+        for K in range(1, 6):
+            S = (N - 1) * K
+            if D % S:
+                continue
+            pc = oracle.param_count(100, D, N, K, [V] * S)
+            assert pc["ngram_tables"] == V * D
+            assert pc["projections"] == D * D
+            assert pc["E0"] == 100 * D
+
+
+# ------------------------------------------------------------------ decode
+
+def test_decode_equals_prefill():
+    rng = np.random.default_rng(10)
+    V0, D, N, K, V, E0, E, W, _, _ = _random_case(rng, N=4, K=1, D=12)
+    fetch = oracle.table_fetch(E0, E)
+    full = [[int(x) for x in rng.integers(0, V0, size=L)] for L in (14, 2, 9)]
+    hist_len = [5, 0, 1]
+    dec = oracle.DecodeOracle(V0, D, N, K, V, [f[:h] for f, h in zip(full, hist_len)])
+    pos = list(hist_len)
+    want = [oracle.prefill(V0, D, N, K, V, f, _one_seq(f), fetch, W) for f in full]
+    while any(p < len(f) for p, f in zip(pos, full)):
+        take = [min(int(rng.integers(1, 6)), len(f) - p) for p, f in zip(pos, full)]
+        new = [f[p:p + t] for f, p, t in zip(full, pos, take)]
+        idxs, embs = dec.step(new, fetch, W)
+        for b in range(3):
+            np.testing.assert_array_equal(idxs[b], want[b][0][pos[b]:pos[b] + take[b]])
+            np.testing.assert_allclose(embs[b], want[b][1][pos[b]:pos[b] + take[b]],
+                                       rtol=0, atol=1e-13)
+        # accept a prefix only, then re-propose the rest: rejected drafts leave no trace
+        acc = [int(rng.integers(0, t + 1)) for t in take]
+        dec.commit(new, acc)
+        pos = [p + a for p, a in zip(pos, acc)]
+
+
+def test_decode_handworked():
+    g = _load("embed_handworked_small.json")
+    c = [c for c in g["cases"] if c["name"] == "N3_K1"][0]
+    E0, E, W = _case_arrays(c)
+    dec = oracle.DecodeOracle(c["V0"], c["D"], c["N"], c["K"], c["V"], [c["tokens"][:1]])
+    idxs, embs = dec.step([c["tokens"][1:]], oracle.table_fetch(E0, E), W)
+    np.testing.assert_array_equal(idxs[0], np.array(c["idx"][1:]))
+    want = np.array([[float(Fraction(p, q)) for p, q in row] for row in c["e"][1:]])
+    np.testing.assert_allclose(embs[0], want, rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("mistake", ["digits_reversed", "drop_high_digit", "norm_over_N",
+                                     "drop_E0", "no_pad", "transpose_W"])
+def test_pins_catch_planted_mistakes(monkeypatch, mistake):
+    if mistake == "digits_reversed":
+        monkeypatch.setattr(O, "ngram_value",
+                            lambda ctx, n, V0: sum(int(ctx[n - 1 - j]) * V0 ** j for j in range(n)))
+    elif mistake == "drop_high_digit":
+        monkeypatch.setattr(O, "ngram_value",
+                            lambda ctx, n, V0: sum(int(ctx[j]) * V0 ** j for j in range(n - 1)))
+    elif mistake == "no_pad":
+        monkeypatch.setattr(O, "context",
+                            lambda seq, i, n: [int(seq[(i - j) % len(seq)]) for j in range(n)])
+    else:
+        real = O.embed_from_indices
+
+        def planted(D, N, K, tokens, idx, fetch, W_blocks):
+            S = (N - 1) * K
+            if mistake == "norm_over_N":
+                return real(D, N, K, tokens, idx, fetch, W_blocks) * (S + 1) / N
+            if mistake == "drop_E0":
+                zero = lambda s, rows: (np.zeros((len(rows), D)) if s < 0 else fetch(s, rows))
+                return real(D, N, K, tokens, idx, zero, W_blocks)
+            if mistake == "transpose_W":
+                Wt = [np.asarray(w)[::-1] for w in W_blocks]
+                return real(D, N, K, tokens, idx, fetch, Wt)
+            raise AssertionError
+        # oracle.prefill resolves embed_from_indices in its module at call time
+        monkeypatch.setattr(O, "embed_from_indices", planted)
+    if mistake in ("digits_reversed", "drop_high_digit", "no_pad"):
+        assert _fails(check_hash_golden) or _fails(check_hash_decimal)
+    else:
+        assert _fails(check_embed_golden)
