@@ -1,0 +1,316 @@
+"""Benchmark of the N-gram embedding forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-decode]
+
+A step is one pass of the whole path over one 64K-token batch of the 30B-parameter layer
+(V0=131072, D=3072, N=4, K=4: 12 sub-tables of width 256, ~60 GB, Zipf(1.1) ids, 8 x 8192):
+kernel 1 (hash) then kernels 2+3 (gather fused into the bf16 matrix-core projection, E_0
+epilogue), the two launches ngram_embed_prefill makes. Inputs are resident in HBM; four
+pre-drawn id batches rotate so no batch finds its rows cached.
+Besides the JSON line's `value` (tokens/s) it reports:
+  roofline      the projection kernel (dominant) against the bf16 matrix-core peak, with
+                HIP-event kernel times taken on the launch stream inside the timed region;
+  gather        the stand-alone gather kernel against the 8 TB/s HBM peak;
+  decode        1000 speculative-verify steps (256 sequences x 5 ids) replayed as a HIP graph;
+  cpu_baseline  the CPU oracle timed on this host's cores on a bounded sample.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "N-gram embed tokens/sec + achieved HBM GB/s (64K-tok prefill, spec decode)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+WORKLOAD = "prefill_64k_30b"
+DECODE_WORKLOAD = "decode_spec5_30b"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_project_prefill_64k_30b.txt")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(name):
+    p = os.path.join(ROOT, "gram_embedding_layer_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(per_launch_rows):
+    """HBM bytes per launch of the projection from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("project.hip sha256[:16]") != source_digest("project.hip"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, E0, E, W, tokens2d, nseq_sample):
+    """The oracle as it stands, on the first `nseq_sample` sequences of the batch. Table rows
+    the oracle asks for are copied from HBM beforehand (not timed)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    seqs = tokens2d[:nseq_sample]
+    tokens = seqs.reshape(-1)
+    cu = np.arange(nseq_sample + 1, dtype=np.int64) * seqs.shape[1]
+    t0 = time.perf_counter()
+    idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
+    t_hash = time.perf_counter() - t0
+    # copy the named rows to host (excluded from the timing)
+    c0 = time.perf_counter()
+    rows = {-1: E0.index_select(0, torch.as_tensor(tokens.astype(np.int64), device="cuda"))
+            .float().cpu().numpy().astype(np.float64)}
+    for s in range(w.S):
+        r = torch.as_tensor(idx[:, s], device="cuda")
+        rows[s] = E[s].index_select(0, r).float().cpu().numpy().astype(np.float64)
+    Wh = W.float().cpu().numpy().astype(np.float64)
+    Wb = [Wh[:, s * w.d:(s + 1) * w.d] for s in range(w.S)]
+    t_copy = time.perf_counter() - c0
+
+    def fetch(s, r):
+        return rows[s]          # rows already in the oracle's order
+    t1 = time.perf_counter()
+    oracle.embed_from_indices(w.D, w.N, w.K, tokens, idx, fetch, Wb)
+    t_embed = time.perf_counter() - t1
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                        if p.get("user_api") == "blas"] or [1])
+    n = len(tokens)
+    return {
+        "value": n / (t_hash + t_embed),
+        "unit": "tokens/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{nseq_sample} of {tokens2d.shape[0]} sequences ({n} tokens) of the "
+                   f"benchmark batch; python-int hash {t_hash:.2f} s (1 thread) + float64 "
+                   f"contraction {t_embed:.2f} s ({blas_threads} BLAS threads); "
+                   f"host copy of the named rows {t_copy:.2f} s not timed"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer's data-parallel path needs no second GPU "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gram_embedding_layer_amd as g
+    import workloads as WL
+
+    g.load()
+    dev = torch.device("cuda:0")
+    w = WL.workload(WORKLOAD)
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    T = w.T
+    log(f"generating tables: {sum(w.V) * w.d * 2 / 1e9:.1f} GB sub-tables + E0 + W")
+    E0, E, W = WL.device_tables(w, device=dev)
+    tables = g.Tables(E0, E, W)
+    nrot = 4
+    tok_host = [WL.token_batch(w, purpose=p) for p in range(nrot)]
+    toks = [torch.as_tensor(t.reshape(-1)).to(dev) for t in tok_host]
+    cu = torch.as_tensor(np.arange(w.batch + 1, dtype=np.int32) * w.seqlen).to(dev)
+    out = torch.empty((T, w.D), dtype=torch.bfloat16, device=dev)
+    ws = g.alloc_workspace(cfg, T, device=dev)
+    _, idx_off = g.ngram_embed_workspace_layout(cfg, T)
+    idx_ws = ws[idx_off:].view(torch.int32)
+    idx_rot = [torch.empty((T, w.S), dtype=torch.int32, device=dev) for _ in range(nrot)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k, ev=None):
+        r = k % nrot
+        if ev is not None:
+            ev[0].record(stream)
+        g.ngram_embed_hash(cfg, toks[r], cu, idx_ws, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        g.ngram_embed_project(cfg, tables, idx_ws, toks[r], out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+        raise RuntimeError("device error flags set during the benchmark")
+    t_hash = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_proj = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    ms_per_step = wall / args.steps * 1e3
+    value = T * args.steps / wall
+
+    esz = 2
+    flops = 2.0 * T * w.D * w.D
+    alg_bytes_proj = T * (w.S * w.d * esz + w.D * esz + w.D * esz + w.S * 4 + 4) + w.D * w.D * esz
+    tflops = flops / t_proj / 1e12
+    traffic = counter_traffic(T)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "proj_mfma_kernel<256>",
+                "kernel_us": round(t_proj * 1e6, 1),
+                "algorithmic_hbm_GBps": round(alg_bytes_proj / t_proj / 1e9, 1)}
+    log(f"step {ms_per_step:.3f} ms: hash {t_hash*1e6:.1f} us, project {t_proj*1e6:.1f} us "
+        f"({tflops:.0f} TFLOP/s)")
+
+    # stand-alone gather: HBM gate (read T*S*d*2 bytes of random rows, write the same)
+    G = torch.empty((T, w.D), dtype=torch.bfloat16, device=dev)
+    for r in range(nrot):
+        g.ngram_embed_hash(cfg, toks[r], cu, idx_rot[r], None, stream=stream)
+    for k in range(3):
+        g.ngram_embed_gather(cfg, tables, idx_rot[k % nrot], G, stream=stream)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for k in range(args.steps):
+        gev[k][0].record(stream)
+        g.ngram_embed_gather(cfg, tables, idx_rot[k % nrot], G, stream=stream)
+        gev[k][1].record(stream)
+    torch.cuda.synchronize(dev)
+    t_g = float(np.mean([a.elapsed_time(b) for a, b in gev])) * 1e-3
+    read_b = T * w.S * w.d * esz
+    gather = {"kernel": "gather_kernel", "kernel_us": round(t_g * 1e6, 1),
+              "read_GBps": round(read_b / t_g / 1e9, 1),
+              "read_write_GBps": round(2 * read_b / t_g / 1e9, 1),
+              "frac_of_hbm_peak": round(2 * read_b / t_g / 1e9 / HBM_PEAK_GBS, 4),
+              "bytes_read": read_b, "bytes_written": read_b}
+    log(f"gather {t_g*1e6:.1f} us: {2*read_b/t_g/1e9:.0f} GB/s read+write")
+    del G
+
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(g, WL, cfg, tables, dev, stream, args.decode_steps)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_seqs} sequences")
+        cpu = cpu_baseline(w, E0, E, W, tok_host[0], args.cpu_sample_seqs)
+        log(f"cpu baseline {cpu['value']:.0f} tokens/s")
+
+    step_bytes = alg_bytes_proj + T * 4 * (1 + w.S)   # + hash: ids in, indices out
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "V0": w.V0, "D": w.D, "N": w.N, "K": w.K,
+                   "subtables": w.S, "subtable_width": w.d, "ngram_params": sum(w.V) * w.d,
+                   "batch": w.batch, "seq_len": w.seqlen, "tokens_per_step": T,
+                   "ids": "zipf1.1"},
+        "hbm_GBps_algorithmic": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernels_us": {"hash": round(t_hash * 1e6, 1), "project": round(t_proj * 1e6, 1)},
+        "roofline": roofline,
+        "gather": gather,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
+    """Speculative-verify decode: 256 sequences with 8192-token histories in the device
+    cache; each step proposes 5 ids per sequence (1 + 4 drafts), all committed. The loop is
+    captured once as a HIP graph and replayed; the cache is restored before each replay."""
+    import numpy as np
+    import torch
+
+    wd = WL.workload(DECODE_WORKLOAD)
+    nseq, tmax = wd.batch, wd.decode_new
+    log(f"decode: {nsteps} steps x {nseq} sequences x {tmax} ids")
+    hist = torch.as_tensor(WL.token_batch(wd, purpose=0).reshape(-1)).to(dev)
+    cu = torch.as_tensor(np.arange(nseq + 1, dtype=np.int32) * wd.seqlen).to(dev)
+    cache = g.Cache.empty(cfg, nseq, device=dev)
+    g.ngram_cache_init(cfg, cache, hist, cu, stream=stream)
+    ring0, len0 = cache.ring.clone(), cache.len.clone()
+    ids = torch.as_tensor(WL.token_batch(wd, purpose=1, batch=nsteps * nseq, seqlen=tmax)
+                          .reshape(nsteps, nseq, tmax)).to(dev)
+    n_new = torch.full((nseq,), tmax, dtype=torch.int32, device=dev)
+    out = torch.empty((nseq, tmax, cfg.D), dtype=torch.bfloat16, device=dev)
+    ws = g.alloc_workspace(cfg, nseq * tmax, device=dev)
+    # eager warmup of a few steps, then restore the cache
+    for s in range(3):
+        g.ngram_embed_decode(cfg, tables, cache, ids[s], n_new, out, ws, n_commit=n_new,
+                             stream=stream)
+    torch.cuda.synchronize(dev)
+    eager_steps = 50
+    cache.ring.copy_(ring0)
+    cache.len.copy_(len0)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(eager_steps):
+        g.ngram_embed_decode(cfg, tables, cache, ids[s], n_new, out, ws, n_commit=n_new,
+                             stream=stream)
+    torch.cuda.synchronize(dev)
+    eager_us = (time.perf_counter() - t0) / eager_steps * 1e6
+    graph = torch.cuda.CUDAGraph()
+    cache.ring.copy_(ring0)
+    cache.len.copy_(len0)
+    torch.cuda.synchronize(dev)
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        for s in range(nsteps):
+            g.ngram_embed_decode(cfg, tables, cache, ids[s], n_new, out, ws, n_commit=n_new,
+                                 stream=cs)
+    times = []
+    for rep in range(3):
+        cache.ring.copy_(ring0)
+        cache.len.copy_(len0)
+        torch.cuda.synchronize(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.median(times))
+    if int(cache.len[0].item()) != wd.seqlen + nsteps * tmax:
+        raise RuntimeError("decode cache length mismatch after the graph replay")
+    if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+        raise RuntimeError("device error flags set during decode")
+    toks = nsteps * nseq * tmax
+    log(f"decode graph: {t/nsteps*1e6:.1f} us/step, eager {eager_us:.1f} us/step")
+    return {"workload": DECODE_WORKLOAD, "steps": nsteps, "seqs": nseq, "ids_per_step": tmax,
+            "tokens_per_s": round(toks / t, 1), "us_per_step_graph": round(t / nsteps * 1e6, 2),
+            "us_per_step_eager": round(eager_us, 2), "replays": len(times)}
+
+
+if __name__ == "__main__":
+    main()

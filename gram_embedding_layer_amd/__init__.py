@@ -1,0 +1,283 @@
+"""MI355X (gfx950) N-gram embedding forward pass: Python binding of libngram_embed.so.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind the C ABI
+declared in include/ngram_embed.h; PyTorch supplies device memory and streams. There is no
+fallback: if the library is missing, load() raises.
+
+The layer (section A2 of the deep-notes page on "Scaling Embeddings Outperforms Scaling
+Experts in Language Models"): e_i = (E_0(t_i) + sum_{n,k} W_{n,k} E_{n,k}(H_{n,k})) / ((N-1)K+1)
+with H_{n,k} the polynomial rolling hash modulo V_{n,k}.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+__all__ = [
+    "LIB_PATH", "NgramError", "Config", "Tables", "Cache", "load",
+    "NGRAM_OK", "NGRAM_F32", "NGRAM_BF16",
+    "NGRAM_FLAG_BAD_TOKEN", "NGRAM_FLAG_BAD_SEQLENS", "NGRAM_FLAG_BAD_COUNT",
+    "ngram_embed_workspace_size", "ngram_embed_workspace_layout", "ngram_embed_hash",
+    "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
+    "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
+    "ngram_embed_clear_error_flag", "ngram_embed_status_string", "alloc_workspace",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libngram_embed.so")
+
+NGRAM_OK = 0
+NGRAM_F32, NGRAM_BF16 = 0, 1
+NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS, NGRAM_FLAG_BAD_COUNT = 1, 2, 4
+NGRAM_MAX_DECODE_TOKENS = 8
+
+
+class NgramError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({ngram_embed_status_string(status)})")
+
+
+class _CConfig(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("V0", ctypes.c_int64),
+                ("V", ctypes.POINTER(ctypes.c_int64))]
+
+
+class _CTables(ctypes.Structure):
+    _fields_ = [("E0", ctypes.c_void_p), ("E", ctypes.POINTER(ctypes.c_void_p)),
+                ("W", ctypes.c_void_p)]
+
+
+class _CCache(ctypes.Structure):
+    _fields_ = [("ring", ctypes.c_void_p), ("len", ctypes.c_void_p), ("nseq", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libngram_embed.so (after torch, so both use the same HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    try:
+        import torch  # noqa: F401  (binds libamdhip64 first)
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gram_embedding_layer_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(_CConfig)
+    tabp = ctypes.POINTER(_CTables)
+    cachep = ctypes.POINTER(_CCache)
+    sig = {
+        "ngram_embed_workspace_size": (SZ, [cfgp, I64]),
+        "ngram_embed_workspace_layout": (ctypes.c_int, [cfgp, I64, ctypes.POINTER(SZ),
+                                                        ctypes.POINTER(SZ)]),
+        "ngram_embed_hash": (ctypes.c_int, [cfgp, P, P, I32, I64, P, P, P]),
+        "ngram_embed_gather": (ctypes.c_int, [cfgp, tabp, P, I64, P, P]),
+        "ngram_embed_project": (ctypes.c_int, [cfgp, tabp, P, P, I64, P, P]),
+        "ngram_embed_prefill": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, P, SZ, P]),
+        "ngram_cache_init": (ctypes.c_int, [cfgp, cachep, P, P, I64, P]),
+        "ngram_embed_decode": (ctypes.c_int, [cfgp, tabp, cachep, P, P, I32, P, P, P, SZ, P]),
+        "ngram_cache_commit": (ctypes.c_int, [cfgp, cachep, P, P, I32, P, P]),
+        "ngram_embed_read_error_flag": (ctypes.c_int, [P, ctypes.POINTER(I32), P]),
+        "ngram_embed_clear_error_flag": (ctypes.c_int, [P, P]),
+        "ngram_embed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ argument objects
+
+@dataclass
+class Config:
+    """Mirror of ngram_embed_config: N, K, D, dtype ("f32"/"bf16" or 0/1), V0, V_{n,k}."""
+    N: int
+    K: int
+    D: int
+    dtype: object
+    V0: int
+    V: Sequence[int]
+
+    @property
+    def S(self) -> int:
+        return (self.N - 1) * self.K
+
+    @property
+    def d(self) -> int:
+        return self.D // self.S if self.S else 0
+
+    @property
+    def dtype_code(self) -> int:
+        if self.dtype in ("f32", "float32", NGRAM_F32):
+            return NGRAM_F32
+        if self.dtype in ("bf16", "bfloat16", NGRAM_BF16):
+            return NGRAM_BF16
+        return int(self.dtype) if isinstance(self.dtype, int) else -1
+
+    def _c(self):
+        arr = (ctypes.c_int64 * max(1, len(self.V)))(*[int(v) for v in self.V])
+        c = _CConfig(int(self.N), int(self.K), int(self.D), self.dtype_code, int(self.V0),
+                     ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+        return c, arr
+
+
+@dataclass
+class Tables:
+    """E0 [V0, D], E = S sub-tables [V_s, d], W [D, D] stacked (device tensors)."""
+    E0: object
+    E: Sequence[object]
+    W: object
+
+    def _c(self):
+        arr = (ctypes.c_void_p * max(1, len(self.E)))(*[_ptr(e) for e in self.E])
+        return _CTables(_ptr(self.E0), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+                        _ptr(self.W)), arr
+
+
+@dataclass
+class Cache:
+    """N-gram cache: ring int32 [nseq, N-1], len int64 [nseq] (device tensors)."""
+    ring: object
+    len: object
+
+    @staticmethod
+    def empty(cfg: Config, nseq: int, device="cuda") -> "Cache":
+        import torch
+        return Cache(torch.zeros((nseq, max(cfg.N - 1, 0)), dtype=torch.int32, device=device),
+                     torch.zeros((nseq,), dtype=torch.int64, device=device))
+
+    @property
+    def nseq(self) -> int:
+        return int(self.len.shape[0])
+
+    def _c(self):
+        ring = _ptr(self.ring) if self.ring is not None and self.ring.numel() else None
+        return _CCache(ring, _ptr(self.len), self.nseq)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(getattr(stream, "cuda_stream", stream))
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != NGRAM_OK:
+        raise NgramError(fn, rc)
+
+
+# ------------------------------------------------------------------ entry points
+
+def ngram_embed_status_string(status: int) -> str:
+    return load().ngram_embed_status_string(int(status)).decode()
+
+
+def ngram_embed_workspace_size(cfg: Config, max_rows: int) -> int:
+    c, keep = cfg._c()
+    return int(load().ngram_embed_workspace_size(ctypes.byref(c), int(max_rows)))
+
+
+def ngram_embed_workspace_layout(cfg: Config, max_rows: int):
+    c, keep = cfg._c()
+    tok, idx = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("ngram_embed_workspace_layout", load().ngram_embed_workspace_layout(
+        ctypes.byref(c), int(max_rows), ctypes.byref(tok), ctypes.byref(idx)))
+    return tok.value, idx.value
+
+
+def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
+    """Zero-filled uint8 device workspace for up to max_rows rows."""
+    import torch
+    n = ngram_embed_workspace_size(cfg, max_rows)
+    if n == 0:
+        raise NgramError("ngram_embed_workspace_size", -1)
+    return torch.zeros((n,), dtype=torch.uint8, device=device)
+
+
+def ngram_embed_hash(cfg: Config, tokens, cu_seqlens, idx, err_flags=None, stream=None):
+    c, keep = cfg._c()
+    _check("ngram_embed_hash", load().ngram_embed_hash(
+        ctypes.byref(c), _ptr(tokens), _ptr(cu_seqlens), int(cu_seqlens.numel()) - 1,
+        int(tokens.numel()), _ptr(idx), _ptr(err_flags), _stream(stream)))
+
+
+def ngram_embed_gather(cfg: Config, tables: Tables, idx, G, stream=None):
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    _check("ngram_embed_gather", load().ngram_embed_gather(
+        ctypes.byref(c), ctypes.byref(t), _ptr(idx), int(G.shape[0]), _ptr(G), _stream(stream)))
+
+
+def ngram_embed_project(cfg: Config, tables: Tables, idx, tok, out, stream=None):
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    _check("ngram_embed_project", load().ngram_embed_project(
+        ctypes.byref(c), ctypes.byref(t), _ptr(idx), _ptr(tok), int(out.shape[0]), _ptr(out),
+        _stream(stream)))
+
+
+def ngram_embed_prefill(cfg: Config, tables: Tables, tokens, cu_seqlens, out, ws,
+                        stream=None):
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    _check("ngram_embed_prefill", load().ngram_embed_prefill(
+        ctypes.byref(c), ctypes.byref(t), _ptr(tokens), _ptr(cu_seqlens),
+        int(cu_seqlens.numel()) - 1, int(tokens.numel()), _ptr(out), _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def ngram_cache_init(cfg: Config, cache: Cache, tokens, cu_seqlens, stream=None):
+    c, keep = cfg._c()
+    cc = cache._c()
+    _check("ngram_cache_init", load().ngram_cache_init(
+        ctypes.byref(c), ctypes.byref(cc), _ptr(tokens), _ptr(cu_seqlens), int(tokens.numel()),
+        _stream(stream)))
+
+
+def ngram_embed_decode(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_new, out, ws,
+                       n_commit=None, stream=None):
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    cc = cache._c()
+    _check("ngram_embed_decode", load().ngram_embed_decode(
+        ctypes.byref(c), ctypes.byref(t), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
+        int(new_tokens.shape[1]), _ptr(n_commit), _ptr(out), _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def ngram_cache_commit(cfg: Config, cache: Cache, new_tokens, n_accept, err_flags=None,
+                       stream=None):
+    c, keep = cfg._c()
+    cc = cache._c()
+    _check("ngram_cache_commit", load().ngram_cache_commit(
+        ctypes.byref(c), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_accept),
+        int(new_tokens.shape[1]), _ptr(err_flags), _stream(stream)))
+
+
+def ngram_embed_read_error_flag(ws, stream=None) -> int:
+    v = ctypes.c_int32(0)
+    _check("ngram_embed_read_error_flag", load().ngram_embed_read_error_flag(
+        _ptr(ws), ctypes.byref(v), _stream(stream)))
+    return int(v.value)
+
+
+def ngram_embed_clear_error_flag(ws, stream=None):
+    _check("ngram_embed_clear_error_flag",
+           load().ngram_embed_clear_error_flag(_ptr(ws), _stream(stream)))

@@ -1,0 +1,221 @@
+// C-ABI entry points: host validation, then stream-ordered kernel launches.
+// Declarations and the contract of every function: include/ngram_embed.h.
+#include "kernels.h"
+
+using ngram::LayerDesc;
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
+
+// Tables: E0 and W always; the S sub-table pointers when S > 0. All 16-byte aligned.
+int check_tables(const LayerDesc& L, const ngram_embed_tables* T, bool need_e0_w) {
+  if (T == nullptr) return NGRAM_EALIGN;
+  if (need_e0_w && (!ngram::aligned(T->E0, 16) || !ngram::aligned(T->W, 16)))
+    return NGRAM_EALIGN;
+  if (L.S > 0) {
+    if (T->E == nullptr) return NGRAM_EALIGN;
+    for (int s = 0; s < L.S; ++s)
+      if (!ngram::aligned(T->E[s], 16)) return NGRAM_EALIGN;
+  }
+  return NGRAM_OK;
+}
+
+int check_ws(const LayerDesc& L, const void* ws, size_t ws_bytes, int64_t rows,
+             ngram::WsLayout* lay) {
+  if (!ngram::ws_layout(L, rows, lay)) return NGRAM_EINVAL;
+  if (!ngram::aligned(ws, 256) || ws_bytes < lay->total) return NGRAM_EWORKSPACE;
+  return NGRAM_OK;
+}
+
+int32_t* ws_flags(void* ws) { return static_cast<int32_t*>(ws); }
+
+}  // namespace
+
+extern "C" {
+
+size_t ngram_embed_workspace_size(const ngram_embed_config* cfg, int64_t max_rows) {
+  LayerDesc L;
+  ngram::WsLayout lay;
+  if (ngram::describe(cfg, &L) != NGRAM_OK || !ngram::ws_layout(L, max_rows, &lay)) return 0;
+  return lay.total;
+}
+
+int ngram_embed_workspace_layout(const ngram_embed_config* cfg, int64_t max_rows,
+                                 size_t* tok_off, size_t* idx_off) {
+  LayerDesc L;
+  const int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  ngram::WsLayout lay;
+  if (!ngram::ws_layout(L, max_rows, &lay)) return NGRAM_EINVAL;
+  if (tok_off) *tok_off = lay.tok_off;
+  if (idx_off) *idx_off = lay.idx_off;
+  return NGRAM_OK;
+}
+
+int ngram_embed_hash(const ngram_embed_config* cfg, const int32_t* tokens,
+                     const int32_t* cu_seqlens, int32_t nseq, int64_t ntok, int32_t* idx,
+                     int32_t* err_flags, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
+  if (ntok == 0) return NGRAM_OK;
+  if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+  if (L.S > 0 && !ngram::aligned(idx, 4)) return NGRAM_EALIGN;
+  if (err_flags != nullptr && !ngram::aligned(err_flags, 4)) return NGRAM_EALIGN;
+  if (L.S == 0) return NGRAM_OK;  // N = 1: nothing to hash
+  return hip_status(ngram::launch_hash_prefill(L, tokens, cu_seqlens, nseq, ntok, idx,
+                                               err_flags, static_cast<hipStream_t>(stream)));
+}
+
+int ngram_embed_gather(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                       const int32_t* idx, int64_t nrows, void* G, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (nrows < 0) return NGRAM_EINVAL;
+  if (nrows == 0 || L.S == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, false)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(idx, 4) || !ngram::aligned(G, 16)) return NGRAM_EALIGN;
+  return hip_status(ngram::launch_gather(L, tables->E, idx, nrows, G,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                        const int32_t* idx, const int32_t* tok, int64_t nrows, void* out,
+                        void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (nrows < 0) return NGRAM_EINVAL;
+  if (nrows == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
+  if ((L.S > 0 && !ngram::aligned(idx, 4)) || !ngram::aligned(tok, 4) ||
+      !ngram::aligned(out, 16))
+    return NGRAM_EALIGN;
+  return hip_status(ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tok, nrows,
+                                          out, static_cast<hipStream_t>(stream)));
+}
+
+int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                        const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
+                        int64_t ntok, void* out, void* ws, size_t ws_bytes, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
+  ngram::WsLayout lay;
+  if ((rc = check_ws(L, ws, ws_bytes, ntok, &lay)) != NGRAM_OK) return rc;
+  if (ntok == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4) || !ngram::aligned(out, 16))
+    return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.idx_off);
+  if (L.S > 0) {
+    rc = hip_status(ngram::launch_hash_prefill(L, tokens, cu_seqlens, nseq, ntok, idx,
+                                               ws_flags(ws), st));
+    if (rc != NGRAM_OK) return rc;
+  }
+  return hip_status(
+      ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tokens, ntok, out, st));
+}
+
+int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const int32_t* tokens,
+                     const int32_t* cu_seqlens, int64_t ntok, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0 || ntok < 0) return NGRAM_EINVAL;
+  if (cache->nseq == 0) return NGRAM_OK;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if (ntok > 0 && !ngram::aligned(tokens, 4)) return NGRAM_EALIGN;
+  return hip_status(ngram::launch_cache_init(L, cache->ring, cache->len, tokens, cu_seqlens,
+                                             cache->nseq, ntok, nullptr,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                       ngram_cache* cache, const int32_t* new_tokens, const int32_t* n_new,
+                       int32_t tmax, const int32_t* n_commit, void* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0) return NGRAM_EINVAL;
+  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
+  const int64_t rows = int64_t(cache->nseq) * tmax;
+  ngram::WsLayout lay;
+  if ((rc = check_ws(L, ws, ws_bytes, rows, &lay)) != NGRAM_OK) return rc;
+  if (rows == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
+      !ngram::aligned(n_new, 4) || !ngram::aligned(out, 16))
+    return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if (n_commit != nullptr && !ngram::aligned(n_commit, 4)) return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* tok = reinterpret_cast<int32_t*>(w + lay.tok_off);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
+  rc = hip_status(ngram::launch_hash_decode(L, cache->ring, cache->len, new_tokens, n_new,
+                                            cache->nseq, tmax, tok, idx, ws_flags(ws), st));
+  if (rc != NGRAM_OK) return rc;
+  // The projection reads only tok/idx, so the cache may advance before it runs.
+  if (n_commit != nullptr) {
+    rc = hip_status(ngram::launch_cache_commit(L, cache->ring, cache->len, new_tokens, n_commit,
+                                               n_new, cache->nseq, tmax, ws_flags(ws), st));
+    if (rc != NGRAM_OK) return rc;
+  }
+  return hip_status(
+      ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tok, rows, out, st));
+}
+
+int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
+                       const int32_t* new_tokens, const int32_t* n_accept, int32_t tmax,
+                       int32_t* err_flags, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0) return NGRAM_EINVAL;
+  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
+  if (cache->nseq == 0) return NGRAM_OK;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
+      !ngram::aligned(n_accept, 4))
+    return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if (err_flags != nullptr && !ngram::aligned(err_flags, 4)) return NGRAM_EALIGN;
+  return hip_status(ngram::launch_cache_commit(L, cache->ring, cache->len, new_tokens, n_accept,
+                                               nullptr, cache->nseq, tmax, err_flags,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ngram_embed_read_error_flag(const void* ws, int32_t* flags, void* stream) {
+  if (!ngram::aligned(ws, 256) || flags == nullptr) return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(flags, ws, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return hip_status(e);
+}
+
+int ngram_embed_clear_error_flag(void* ws, void* stream) {
+  if (!ngram::aligned(ws, 256)) return NGRAM_EALIGN;
+  return hip_status(ngram::launch_clear_flags(ws_flags(ws), static_cast<hipStream_t>(stream)));
+}
+
+const char* ngram_embed_status_string(int status) {
+  switch (status) {
+    case NGRAM_OK: return "ok";
+    case NGRAM_EINVAL: return "invalid size, count or configuration";
+    case NGRAM_EDTYPE: return "unknown dtype";
+    case NGRAM_EALIGN: return "null or misaligned pointer";
+    case NGRAM_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case NGRAM_EOVERFLOW: return "V0 * max V_{n,k} exceeds the exact 64-bit hash range";
+    case NGRAM_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// Kernel 1 (rolling hash) and the N-gram cache kernels of the decode path.
+//
+// The hash is the polynomial rolling hash of section A2 of the deep-notes page on "Scaling
+// Embeddings Outperforms Scaling Experts in Language Models":
+//   H_{n,k}(t_{i-n+1..i}) = (sum_{j<n} t_{i-j} V0^j) mod V_{n,k}.
+// The raw polynomial needs up to n*31 bits (more than 64 for n >= 3 at V0 = 2^17), so it is
+// evaluated by Horner's rule from the oldest id to the newest, reducing modulo V_{n,k} after
+// every step: x <- (x*V0 + t) mod V. With x < V < 2^31 and t < 2^32 every intermediate is
+// below 2^63 and the result equals the exact residue.
+#include "kernels.h"
+
+namespace ngram {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Hash one position. c[j] = t_{i-j} (pad 0 before the sequence start), j < NMAX.
+template <int NMAX>
+__device__ __forceinline__ void hash_position(const LayerDesc& L, const uint32_t (&c)[NMAX],
+                                              int32_t* __restrict__ out) {
+  const uint64_t V0 = uint64_t(L.V0);
+  for (int s = 0; s < L.S; ++s) {
+    const int n = 2 + s / L.K;             // order of sub-table s = (n-2)K + (k-1)
+    const uint64_t V = L.V[s];
+    uint64_t x = 0;
+#pragma unroll
+    for (int j = NMAX - 1; j >= 0; --j)
+      if (j < n) x = (x * V0 + c[j]) % V;
+    out[s] = int32_t(x);
+  }
+}
+
+template <int NMAX>
+__global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
+    const LayerDesc L, const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu,
+    int32_t nseq, int64_t ntok, int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (flags != nullptr && i <= nseq) {
+    // cu_seqlens must run 0 = c_0 <= c_1 <= ... <= c_nseq = ntok
+    const int64_t ci = cu[i];
+    const bool bad = (i == 0 && ci != 0) || (i == nseq && ci != ntok) ||
+                     (i < nseq && ci > cu[i + 1]);
+    if (bad) atomicOr(flags, NGRAM_FLAG_BAD_SEQLENS);
+  }
+  if (i >= ntok) return;
+  // sequence of position i: the last b with cu[b] <= i
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  int64_t start = cu[lo];
+  start = start < 0 ? 0 : (start > i ? i : start);   // never read outside [0, i]
+  const int32_t t = tokens[i];
+  if (flags != nullptr && uint32_t(t) >= uint32_t(L.V0)) atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
+  uint32_t c[NMAX];
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j)
+    c[j] = (j < L.N && i - j >= start) ? uint32_t(tokens[i - j]) : 0u;
+  hash_position<NMAX>(L, c, idx + i * L.S);
+}
+
+template <int NMAX>
+__global__ __launch_bounds__(kThreads) void hash_decode_kernel(
+    const LayerDesc L, const int32_t* __restrict__ ring, const int64_t* __restrict__ len,
+    const int32_t* __restrict__ newtok, const int32_t* __restrict__ n_new, int32_t nseq,
+    int32_t tmax, int32_t* __restrict__ tok, int32_t* __restrict__ idx,
+    int32_t* __restrict__ flags) {
+  const int64_t r = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (r >= int64_t(nseq) * tmax) return;
+  const int b = int(r / tmax), j = int(r % tmax);
+  int nn = n_new[b];
+  if (nn < 0 || nn > tmax) {
+    if (flags != nullptr && j == 0) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
+    nn = nn < 0 ? 0 : tmax;
+  }
+  int32_t* out = idx + r * L.S;
+  if (j >= nn) {  // unused slot: E_0 token -1 makes the projection write a zero row
+    tok[r] = -1;
+    for (int s = 0; s < L.S; ++s) out[s] = 0;
+    return;
+  }
+  const int32_t* nt = newtok + int64_t(b) * tmax;
+  const int32_t t = nt[j];
+  if (flags != nullptr && uint32_t(t) >= uint32_t(L.V0)) atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
+  tok[r] = t;
+  const int nm1 = L.N - 1;
+  const int64_t committed = len[b];
+  uint32_t c[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    uint32_t v = 0;
+    if (i < L.N) {
+      if (j - i >= 0) {
+        v = uint32_t(nt[j - i]);                 // a new id of this step
+      } else {
+        const int64_t q = committed + (j - i);   // committed position, from the cache
+        if (q >= 0) v = uint32_t(ring[int64_t(b) * nm1 + q % nm1]);
+      }
+    }
+    c[i] = v;
+  }
+  hash_position<NMAX>(L, c, out);
+}
+
+__global__ __launch_bounds__(kThreads) void cache_init_kernel(
+    int32_t nm1, int32_t* __restrict__ ring, int64_t* __restrict__ len,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu, int32_t nseq,
+    int64_t ntok, int32_t* __restrict__ flags) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nseq) return;
+  int64_t lo = cu[b], hi = cu[b + 1];
+  if (lo < 0 || hi < lo || hi > ntok) {
+    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_SEQLENS);
+    lo = lo < 0 ? 0 : (lo > ntok ? ntok : lo);
+    hi = hi < lo ? lo : (hi > ntok ? ntok : hi);
+  }
+  const int64_t n = hi - lo;
+  len[b] = n;
+  if (nm1 <= 0) return;
+  int32_t* rb = ring + int64_t(b) * nm1;
+  for (int s = 0; s < nm1; ++s) rb[s] = 0;
+  for (int64_t q = (n > nm1 ? n - nm1 : 0); q < n; ++q) rb[q % nm1] = tokens[lo + q];
+}
+
+__global__ __launch_bounds__(kThreads) void cache_commit_kernel(
+    int32_t nm1, int32_t* __restrict__ ring, int64_t* __restrict__ len,
+    const int32_t* __restrict__ newtok, const int32_t* __restrict__ n_accept,
+    const int32_t* __restrict__ n_new, int32_t nseq, int32_t tmax,
+    int32_t* __restrict__ flags) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nseq) return;
+  int a = n_accept[b];
+  const int cap = n_new != nullptr ? min(max(n_new[b], 0), tmax) : tmax;
+  if (a < 0 || a > cap) {
+    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
+    a = a < 0 ? 0 : cap;
+  }
+  int64_t committed = len[b];
+  if (committed < 0) committed = 0;
+  if (nm1 > 0) {
+    int32_t* rb = ring + int64_t(b) * nm1;
+    const int32_t* nt = newtok + int64_t(b) * tmax;
+    for (int q = (a > nm1 ? a - nm1 : 0); q < a; ++q) rb[(committed + q) % nm1] = nt[q];
+  }
+  len[b] = committed + a;
+}
+
+__global__ void clear_flags_kernel(int32_t* flags) { flags[0] = 0; }
+
+template <int NMAX>
+hipError_t hash_prefill_n(const LayerDesc& L, const int32_t* tokens, const int32_t* cu,
+                          int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
+                          hipStream_t st) {
+  const int64_t work = ntok > int64_t(nseq) + 1 ? ntok : int64_t(nseq) + 1;
+  const unsigned blocks = unsigned((work + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(hash_prefill_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, L, tokens,
+                     cu, nseq, ntok, idx, flags);
+  return hipGetLastError();
+}
+
+template <int NMAX>
+hipError_t hash_decode_n(const LayerDesc& L, const int32_t* ring, const int64_t* len,
+                         const int32_t* newtok, const int32_t* n_new, int32_t nseq,
+                         int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
+                         hipStream_t st) {
+  const int64_t rows = int64_t(nseq) * tmax;
+  const unsigned blocks = unsigned((rows + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(hash_decode_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, L, ring,
+                     len, newtok, n_new, nseq, tmax, tok, idx, flags);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The context length N is a template bound so the id window lives in registers.
+hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const int32_t* cu,
+                               int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
+                               hipStream_t st) {
+  if (L.N <= 2) return hash_prefill_n<2>(L, tokens, cu, nseq, ntok, idx, flags, st);
+  if (L.N <= 4) return hash_prefill_n<4>(L, tokens, cu, nseq, ntok, idx, flags, st);
+  if (L.N <= 8) return hash_prefill_n<8>(L, tokens, cu, nseq, ntok, idx, flags, st);
+  return hash_prefill_n<NGRAM_MAX_ORDER>(L, tokens, cu, nseq, ntok, idx, flags, st);
+}
+
+hipError_t launch_hash_decode(const LayerDesc& L, const int32_t* ring, const int64_t* len,
+                              const int32_t* newtok, const int32_t* n_new, int32_t nseq,
+                              int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
+                              hipStream_t st) {
+  if (L.N <= 2)
+    return hash_decode_n<2>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx, flags, st);
+  if (L.N <= 4)
+    return hash_decode_n<4>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx, flags, st);
+  if (L.N <= 8)
+    return hash_decode_n<8>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx, flags, st);
+  return hash_decode_n<NGRAM_MAX_ORDER>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx,
+                                        flags, st);
+}
+
+hipError_t launch_cache_init(const LayerDesc& L, int32_t* ring, int64_t* len,
+                             const int32_t* tokens, const int32_t* cu, int32_t nseq,
+                             int64_t ntok, int32_t* flags, hipStream_t st) {
+  const unsigned blocks = unsigned((nseq + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(cache_init_kernel, dim3(blocks), dim3(kThreads), 0, st, L.N - 1, ring, len,
+                     tokens, cu, nseq, ntok, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_commit(const LayerDesc& L, int32_t* ring, int64_t* len,
+                               const int32_t* newtok, const int32_t* n_accept,
+                               const int32_t* n_new, int32_t nseq, int32_t tmax,
+                               int32_t* flags, hipStream_t st) {
+  const unsigned blocks = unsigned((nseq + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(cache_commit_kernel, dim3(blocks), dim3(kThreads), 0, st, L.N - 1, ring,
+                     len, newtok, n_accept, n_new, nseq, tmax, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_flags(int32_t* flags, hipStream_t st) {
+  hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(1), 0, st, flags);
+  return hipGetLastError();
+}
+
+}  // namespace ngram

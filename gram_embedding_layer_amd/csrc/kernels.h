@@ -1,0 +1,40 @@
+// Internal launch interface between the C-ABI entry points and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "layer_desc.h"
+
+namespace ngram {
+
+// kernel 1: rolling-hash indices of packed prefill positions
+hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const int32_t* cu,
+                               int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
+                               hipStream_t st);
+
+// kernel 4 (front half): context from the N-gram cache + new ids -> tok, idx
+hipError_t launch_hash_decode(const LayerDesc& L, const int32_t* ring, const int64_t* len,
+                              const int32_t* newtok, const int32_t* n_new, int32_t nseq,
+                              int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
+                              hipStream_t st);
+
+// kernel 4 (cache upkeep)
+hipError_t launch_cache_init(const LayerDesc& L, int32_t* ring, int64_t* len,
+                             const int32_t* tokens, const int32_t* cu, int32_t nseq,
+                             int64_t ntok, int32_t* flags, hipStream_t st);
+hipError_t launch_cache_commit(const LayerDesc& L, int32_t* ring, int64_t* len,
+                               const int32_t* newtok, const int32_t* n_accept,
+                               const int32_t* n_new, int32_t nseq, int32_t tmax,
+                               int32_t* flags, hipStream_t st);
+hipError_t launch_clear_flags(int32_t* flags, hipStream_t st);
+
+// kernel 2: stand-alone gather of sub-table rows into G [nrows, D]
+hipError_t launch_gather(const LayerDesc& L, const void* const* E, const int32_t* idx,
+                         int64_t nrows, void* G, hipStream_t st);
+
+// kernels 2+3: fused gather + projection + E_0 epilogue
+hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
+                          const void* W, const int32_t* idx, const int32_t* tok,
+                          int64_t nrows, void* out, hipStream_t st);
+
+}  // namespace ngram

@@ -1,0 +1,38 @@
+// Host-checked description of one N-gram embedding layer, passed by value to kernels.
+// HIP-free so the host validation can be built and tested with a plain C++ compiler.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ngram_embed.h"
+
+namespace ngram {
+
+struct LayerDesc {
+  int32_t N;       // largest order
+  int32_t K;       // sub-tables per order
+  int32_t S;       // (N-1)K
+  int32_t D;       // hidden size
+  int32_t d;       // sub-table width D/S (0 when S == 0)
+  int32_t dtype;   // NGRAM_F32 / NGRAM_BF16
+  int32_t esz;     // bytes per element
+  int32_t V0;      // base vocabulary
+  uint32_t V[NGRAM_MAX_SUBTABLES];  // V_{n,k} in sub-table order
+};
+
+// Checks the config (section A2 shapes, the 64-bit Horner bound) and fills `out`.
+// Returns NGRAM_OK or a negative status.
+int describe(const ngram_embed_config* cfg, LayerDesc* out);
+
+// Workspace layout for `rows` output rows; false when rows < 0.
+struct WsLayout {
+  size_t tok_off, idx_off, total;
+};
+bool ws_layout(const LayerDesc& L, int64_t rows, WsLayout* out);
+
+inline bool aligned(const void* p, size_t a) {
+  return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+}  // namespace ngram

@@ -1,0 +1,396 @@
+// Kernels 2+3: gather the sub-table rows and project them, with the E_0 epilogue.
+//
+// Computes the final form of section A2 of the deep-notes page on "Scaling Embeddings
+// Outperforms Scaling Experts in Language Models" for a batch of rows r:
+//   out[r] = ( E_0[tok[r]] + sum_s W_{n,k} E_{n,k}[idx[r, s]] ) / ((N-1)K + 1).
+// Stacking the W_{n,k} side by side into W [D, D] (W[o, s*d + c] = W_{n,k}[o, c]) and the
+// gathered rows into g_r = [E_{2,1}[.], E_{2,2}[.], ...] (length D) turns the double sum
+// into one product W g_r, so the whole batch is a single [rows, D] x [D, D]^T contraction:
+// the only dense work on the path. Both operands are contiguous along the contraction
+// axis, which is the layout the matrix cores want.
+//
+// bf16 path (D % 256 == 0, d % 64 == 0): tiles of BM rows x 256 outputs x 64-deep slices.
+// A 64-deep slice never straddles two sub-tables, so the A-loader reads, for each of the
+// BM rows, one 128-byte piece of one sub-table row straight from HBM (no gathered copy of
+// the batch is ever written). Slices are staged through registers into a double-buffered,
+// XOR-swizzled LDS tile and fed to v_mfma_f32_32x32x16_bf16 (fp32 accumulation). The
+// epilogue adds the E_0 row, scales by 1/(S+1) in fp32 and rounds once to bf16.
+// Blocks are numbered so that the 32 blocks resident on one XCD at a time cover 8 row
+// tiles x 4 output tiles, which keeps their A rows and W panels in that XCD's L2.
+#include "kernels.h"
+
+namespace ngram {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte vector
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+struct ProjArgs {
+  const void* E[NGRAM_MAX_SUBTABLES];
+  uint32_t Vm1[NGRAM_MAX_SUBTABLES];  // V_{n,k} - 1: indices are clamped to their table
+  const int32_t* idx;                 // [nrows, S]
+  const int32_t* tok;                 // [nrows]; outside [0, V0) -> zero row
+  const void* E0;                     // [V0, D]
+  const void* W;                      // [D, D]
+  void* out;                          // [nrows, D]
+  int64_t nrows;
+  int32_t D, S, d, V0;
+  float inv;                          // 1 / (S + 1)
+  int32_t tiles_m, tiles_n;
+};
+
+// ------------------------------------------------------------------ bf16 matrix-core path
+
+constexpr int kBN = 256;
+constexpr int kBK = 64;
+
+template <int BM>
+__global__ __launch_bounds__(256, 1) void proj_mfma_kernel(const ProjArgs a) {
+  constexpr int WM = BM / 2;        // rows per wave (2 x 2 waves)
+  constexpr int TI = WM / 32;       // 32-row MFMA blocks per wave
+  constexpr int TJ = 4;             // 32-output MFMA blocks per wave (128 outputs)
+  constexpr int RA = BM / 32;       // A rows loaded per thread per slice
+  constexpr int RB = kBN / 32;      // W rows loaded per thread per slice
+  constexpr int A_ELEMS = BM * kBK;
+  constexpr int B_ELEMS = kBN * kBK;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (A_ELEMS + B_ELEMS)];
+
+  // -- XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous range
+  //    of virtual tiles and walk a range 8 row tiles at a time, outputs slowest.
+  const int nb = a.tiles_m * a.tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int v = xcd * per + (xcd < rem ? xcd : rem) + local;
+  constexpr int GM = 8;
+  const int group = v / (GM * a.tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(GM, a.tiles_m - first_m);
+  const int in_group = v - group * GM * a.tiles_n;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+  const int64_t m0 = int64_t(tm) * BM;
+  const int n0 = tn * kBN;
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int lrow = t >> 3, lc = t & 7;
+  const int swz = (lc ^ (lrow & 7)) * 8;  // swizzled 16-byte chunk of this thread's rows
+
+  const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E);
+  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
+
+  // -- A loader: rows m0 + lrow + 32 i (clamped into the batch; extra rows are not stored)
+  int64_t arow[RA];
+#pragma unroll
+  for (int i = 0; i < RA; ++i) {
+    const int64_t m = m0 + lrow + 32 * i;
+    arow[i] = m < a.nrows ? m : a.nrows - 1;
+  }
+  int32_t nid[RA];                // indices of the next sub-table, fetched one table early
+  const uint16_t* ap[RA];         // row pointers into the current sub-table
+#pragma unroll
+  for (int i = 0; i < RA; ++i) nid[i] = a.idx[arow[i] * a.S];
+#pragma unroll
+  for (int i = 0; i < RA; ++i) {
+    const uint32_t id = min(uint32_t(nid[i]), a.Vm1[0]);
+    ap[i] = E[0] + int64_t(id) * a.d + lc * 8;
+  }
+  if (a.S > 1) {
+#pragma unroll
+    for (int i = 0; i < RA; ++i) nid[i] = a.idx[arow[i] * a.S + 1];
+  }
+  const uint16_t* bp = W + int64_t(n0 + lrow) * a.D + lc * 8;
+
+  const int KT = a.D / kBK;      // slices
+  const int kps = a.d / kBK;     // slices per sub-table
+  int s_cur = 0;
+  u32x4_t ra[RA], rb[RB];
+
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+    if (kt > 0 && kt == (s_cur + 1) * kps) {   // first slice of the next sub-table
+      ++s_cur;
+#pragma unroll
+      for (int i = 0; i < RA; ++i) {
+        const uint32_t id = min(uint32_t(nid[i]), a.Vm1[s_cur]);
+        ap[i] = E[s_cur] + int64_t(id) * a.d + lc * 8;
+      }
+      if (s_cur + 1 < a.S) {
+#pragma unroll
+        for (int i = 0; i < RA; ++i) nid[i] = a.idx[arow[i] * a.S + s_cur + 1];
+      }
+    }
+    const int koff = (kt - s_cur * kps) * kBK;
+#pragma unroll
+    for (int i = 0; i < RA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + koff);
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      rb[i] = *reinterpret_cast<const u32x4_t*>(bp + int64_t(32 * i) * a.D + kt * kBK);
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* As = lds + buf * (A_ELEMS + B_ELEMS);
+    uint16_t* Bs = As + A_ELEMS;
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+      *reinterpret_cast<u32x4_t*>(As + (lrow + 32 * i) * kBK + swz) = ra[i];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      *reinterpret_cast<u32x4_t*>(Bs + (lrow + 32 * i) * kBK + swz) = rb[i];
+  };
+
+  f32x16_t acc[TJ][TI];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 31, fk = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const uint16_t* As = lds + cur * (A_ELEMS + B_ELEMS);
+    const uint16_t* Bs = As + A_ELEMS;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      // lane (fr, fk) holds 8 consecutive k of row fr: chunk 2*kk + fk of the slice
+      const int ch = kk * 2 + fk;
+      bf16x8_t wf[TJ], xf[TI];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int row = wn * 128 + j * 32 + fr;
+        wf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + row * kBK + ((ch ^ (row & 7)) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int row = wm * WM + i * 32 + fr;
+        xf[i] = *reinterpret_cast<const bf16x8_t*>(As + row * kBK + ((ch ^ (row & 7)) * 8));
+      }
+      // W block as the first operand: each lane's results are 4 consecutive outputs of
+      // one row, which makes the epilogue's E_0 reads and stores 8 bytes wide.
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[j][i], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*128 + 32j + 8g + 4fk + q of
+  //    row m = m0 + wm*WM + 32i + fr.
+  const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0);
+  uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int64_t m = m0 + wm * WM + i * 32 + fr;
+    if (m >= a.nrows) continue;
+    const int32_t tk = a.tok[m];
+    const bool ok = uint32_t(tk) < uint32_t(a.V0);
+    const uint16_t* e0 = E0 + int64_t(ok ? tk : 0) * a.D;
+    uint16_t* o = out + m * a.D;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + j * 32 + g * 8 + fk * 4;
+        u32x2_t res = {0u, 0u};
+        if (ok) {
+          const u32x2_t ev = *reinterpret_cast<const u32x2_t*>(e0 + n);
+          const float y0 = (acc[j][i][4 * g + 0] + bf16_to_f32(ev.x & 0xffffu)) * a.inv;
+          const float y1 = (acc[j][i][4 * g + 1] + bf16_to_f32(ev.x >> 16)) * a.inv;
+          const float y2 = (acc[j][i][4 * g + 2] + bf16_to_f32(ev.y & 0xffffu)) * a.inv;
+          const float y3 = (acc[j][i][4 * g + 3] + bf16_to_f32(ev.y >> 16)) * a.inv;
+          res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+          res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
+        }
+        *reinterpret_cast<u32x2_t*>(o + n) = res;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ generic path
+// Any dtype and shape (used for fp32 and for bf16 shapes the tiles above do not cover):
+// 64 x 64 output tiles, 16-deep slices gathered element by element into LDS, fp32 FMA.
+
+template <typename T> __device__ __forceinline__ float ld(const T* p);
+template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) {
+  return bf16_to_f32(*p);
+}
+template <typename T> __device__ __forceinline__ void st(T* p, float v);
+template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float v) {
+  *p = uint16_t(f32_to_bf16_rne(v));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  __shared__ const T* Etab[NGRAM_MAX_SUBTABLES];
+  __shared__ uint32_t Vtab[NGRAM_MAX_SUBTABLES];
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  if (t < a.S) {
+    Etab[t] = static_cast<const T*>(a.E[t]);
+    Vtab[t] = a.Vm1[t];
+  }
+  const int64_t m0 = int64_t(blockIdx.x) * 64;
+  const int n0 = blockIdx.y * 64;
+  const T* __restrict__ W = static_cast<const T*>(a.W);
+  float acc[4][4] = {};
+  __syncthreads();
+  for (int k0 = 0; k0 < a.D; k0 += 16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int lin = t + 256 * e, r = lin >> 4, kk = lin & 15;
+      const int k = k0 + kk;
+      const int64_t m = m0 + r;
+      float v = 0.f;
+      if (m < a.nrows && k < a.D) {
+        const int s = k / a.d, c = k - s * a.d;
+        const uint32_t id = min(uint32_t(a.idx[m * a.S + s]), Vtab[s]);
+        v = ld<T>(Etab[s] + int64_t(id) * a.d + c);
+      }
+      As[kk][r] = v;
+      const int n = n0 + r;
+      Bs[kk][r] = (n < a.D && k < a.D) ? ld<T>(W + int64_t(n) * a.D + k) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += As[kk][ty + 16 * i] * Bs[kk][tx + 16 * j];
+    __syncthreads();
+  }
+  const T* __restrict__ E0 = static_cast<const T*>(a.E0);
+  T* __restrict__ out = static_cast<T*>(a.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty + 16 * i;
+    if (m >= a.nrows) continue;
+    const int32_t tk = a.tok[m];
+    const bool ok = uint32_t(tk) < uint32_t(a.V0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n >= a.D) continue;
+      const float y = ok ? (acc[i][j] + ld<T>(E0 + int64_t(tk) * a.D + n)) * a.inv : 0.f;
+      st<T>(out + m * a.D + n, y);
+    }
+  }
+}
+
+// N = 1: no sub-tables, e = E_0(t). 16-byte vectors, one per thread.
+__global__ __launch_bounds__(256) void e0_lookup_kernel(const ProjArgs a, int32_t row_bytes) {
+  const int64_t cpr = row_bytes / 16;
+  const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= a.nrows * cpr) return;
+  const int64_t r = item / cpr, c = item - r * cpr;
+  const int32_t tk = a.tok[r];
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (uint32_t(tk) < uint32_t(a.V0))
+    v = reinterpret_cast<const uint4*>(static_cast<const char*>(a.E0) + int64_t(tk) * row_bytes)[c];
+  reinterpret_cast<uint4*>(static_cast<char*>(a.out) + r * row_bytes)[c] = v;
+}
+
+template <int BM>
+hipError_t run_mfma(ProjArgs a, int64_t nrows, int32_t S, int32_t D, int esz,
+                    hipStream_t st) {
+  // at most 2^20 row tiles per launch keeps the tile numbering in 32-bit ints
+  const int64_t chunk = int64_t(BM) << 20;
+  const int32_t* idx = a.idx;
+  const int32_t* tok = a.tok;
+  char* out = static_cast<char*>(a.out);
+  for (int64_t r0 = 0; r0 < nrows; r0 += chunk) {
+    const int64_t n = nrows - r0 < chunk ? nrows - r0 : chunk;
+    a.idx = idx + r0 * S;
+    a.tok = tok + r0;
+    a.out = out + r0 * D * esz;
+    a.nrows = n;
+    a.tiles_m = int32_t((n + BM - 1) / BM);
+    a.tiles_n = D / kBN;
+    hipLaunchKernelGGL(proj_mfma_kernel<BM>, dim3(unsigned(a.tiles_m * a.tiles_n)), dim3(256),
+                       0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
+                          const void* W, const int32_t* idx, const int32_t* tok,
+                          int64_t nrows, void* out, hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  ProjArgs a{};
+  for (int s = 0; s < L.S; ++s) {
+    a.E[s] = E[s];
+    a.Vm1[s] = L.V[s] - 1u;
+  }
+  a.idx = idx;
+  a.tok = tok;
+  a.E0 = E0;
+  a.W = W;
+  a.out = out;
+  a.nrows = nrows;
+  a.D = L.D;
+  a.S = L.S;
+  a.d = L.d;
+  a.V0 = L.V0;
+  a.inv = 1.0f / float(L.S + 1);
+  if (L.S == 0) {
+    const int32_t row_bytes = L.D * L.esz;
+    const int64_t items = nrows * (row_bytes / 16);
+    hipLaunchKernelGGL(e0_lookup_kernel, dim3(unsigned((items + 255) / 256)), dim3(256), 0, st,
+                       a, row_bytes);
+    return hipGetLastError();
+  }
+  if (L.dtype == NGRAM_BF16 && L.D % kBN == 0 && L.d % kBK == 0) {
+    // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
+    // shorter tiles so that enough blocks exist to occupy the 256 CUs.
+    const int64_t tiles_n = L.D / kBN;
+    if (((nrows + 255) / 256) * tiles_n >= 512) return run_mfma<256>(a, nrows, L.S, L.D, 2, st);
+    if (((nrows + 127) / 128) * tiles_n >= 256) return run_mfma<128>(a, nrows, L.S, L.D, 2, st);
+    return run_mfma<64>(a, nrows, L.S, L.D, 2, st);
+  }
+  const unsigned gy = unsigned((L.D + 63) / 64);
+  for (int64_t r0 = 0; r0 < nrows; r0 += (int64_t(1) << 30)) {
+    ProjArgs b = a;
+    const int64_t n = nrows - r0 < (int64_t(1) << 30) ? nrows - r0 : (int64_t(1) << 30);
+    b.idx = idx + r0 * L.S;
+    b.tok = tok + r0;
+    b.out = static_cast<char*>(out) + r0 * L.D * L.esz;
+    b.nrows = n;
+    const dim3 grid(unsigned((n + 63) / 64), gy);
+    if (L.dtype == NGRAM_F32)
+      hipLaunchKernelGGL(proj_generic_kernel<float>, grid, dim3(256), 0, st, b);
+    else
+      hipLaunchKernelGGL(proj_generic_kernel<uint16_t>, grid, dim3(256), 0, st, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace ngram

@@ -1,0 +1,188 @@
+/*
+ * ngram_embed.h - C ABI of the MI355X (gfx950) N-gram embedding forward pass.
+ *
+ * The layer is the final ("Over-Encoding") form of the N-gram embedding described in
+ * section A2 of the deep-notes page on "Scaling Embeddings Outperforms Scaling Experts in
+ * Language Models" (Meituan LongCat team):
+ *
+ *   e_i = ( E_0(t_i) + sum_{n=2}^{N} sum_{k=1}^{K} W_{n,k} E_{n,k}(H_{n,k}(t_{i-n+1..i})) )
+ *         / ((N-1)K + 1)
+ *
+ * with the polynomial rolling hash of the same section
+ *
+ *   H_{n,k}(t_{i-n+1..i}) = ( sum_{j=0}^{n-1} t_{i-j} * V0^j ) mod V_{n,k},
+ *
+ * sub-tables E_{n,k} of shape [V_{n,k}, d], d = D/((N-1)K), and projections W_{n,k} of
+ * shape [D, d]. Section 4.2 of that page (N-gram cache, KV-cache-like management of n-gram
+ * ids on the device) motivates the decode entry points.
+ *
+ * Conventions used throughout:
+ *  - S = (N-1)K sub-tables, ordered s = (n-2)*K + (k-1) (n-major, k-minor).
+ *  - Positions before the first token of a sequence hash as the pad id 0. Ids of another
+ *    sequence packed in the same batch are never used.
+ *  - N = 1 is accepted: there are no sub-tables and e_i = E_0(t_i).
+ *  - All matrices are row-major. "device" pointers are HIP device memory, "host" pointers
+ *    are ordinary host memory read only during the call. The library allocates no memory
+ *    and keeps no state between calls; the caller owns every buffer.
+ *  - Every entry point that takes a stream only enqueues work on that stream (a hipStream_t,
+ *    or NULL for the null stream) and returns without waiting, except
+ *    ngram_embed_read_error_flag, which waits for the stream.
+ *  - Arguments are validated on the host before any work is enqueued; a failed check
+ *    returns a negative status and enqueues nothing. Entry points never throw.
+ *  - Floating-point: bf16 paths read bf16 tables, multiply on the matrix cores with fp32
+ *    accumulation, add E_0 and scale in fp32, and round once (to nearest even) to bf16.
+ *    fp32 paths compute in fp32 throughout.
+ */
+#ifndef NGRAM_EMBED_H
+#define NGRAM_EMBED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+enum {
+  NGRAM_OK = 0,
+  NGRAM_EINVAL = -1,     /* a size or count is out of range or inconsistent */
+  NGRAM_EDTYPE = -2,     /* unknown dtype */
+  NGRAM_EALIGN = -3,     /* a required pointer is NULL or misaligned */
+  NGRAM_EWORKSPACE = -4, /* workspace missing, misaligned or too small */
+  NGRAM_EOVERFLOW = -5,  /* V0 * max V_{n,k} does not fit the exact 64-bit hash */
+  NGRAM_EHIP = -6        /* the HIP runtime reported an error at launch */
+};
+
+/* dtype of E_0, E_{n,k}, W and of every output */
+enum { NGRAM_F32 = 0, NGRAM_BF16 = 1 };
+
+/* device error flags, OR-ed into the int32 at the start of the workspace */
+enum {
+  NGRAM_FLAG_BAD_TOKEN = 1,   /* a token id outside [0, V0) was hashed */
+  NGRAM_FLAG_BAD_SEQLENS = 2, /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_nseq = ntok */
+  NGRAM_FLAG_BAD_COUNT = 4    /* n_new or n_accept outside [0, tmax] */
+};
+
+#define NGRAM_MAX_ORDER 16         /* largest accepted N */
+#define NGRAM_MAX_SUBTABLES 64     /* largest accepted (N-1)K */
+#define NGRAM_MAX_DECODE_TOKENS 8  /* largest accepted tmax (1 + speculative drafts) */
+
+/* Layer hyper-parameters (section A2). */
+typedef struct ngram_embed_config {
+  int32_t N;         /* largest n-gram order, 1 <= N <= NGRAM_MAX_ORDER */
+  int32_t K;         /* sub-tables (hash functions) per order, K >= 1, (N-1)K <= 64 */
+  int32_t D;         /* hidden size; D % ((N-1)K) == 0 and the sub-table row
+                        d * sizeof(dtype) is a multiple of 16 bytes */
+  int32_t dtype;     /* NGRAM_F32 or NGRAM_BF16 */
+  int64_t V0;        /* base vocabulary, 1 <= V0 < 2^31 */
+  const int64_t* V;  /* host, S entries: V_{n,k} in sub-table order, 1 <= V < 2^31,
+                        and V0 * max V < 2^63 (else NGRAM_EOVERFLOW) */
+} ngram_embed_config;
+
+/* Parameters of the layer, all in device memory, in the config's dtype. Every device
+ * pointer here must be 16-byte aligned. */
+typedef struct ngram_embed_tables {
+  const void* E0;        /* [V0, D] base embedding E_0 */
+  const void* const* E;  /* host array of S device pointers; E[s] is E_{n,k} [V_{n,k}, d] */
+  const void* W;         /* [D, D] stacked projection: W[o, s*d + c] = W_{n,k}[o, c] */
+} ngram_embed_tables;
+
+/* N-gram cache of a batch of sequences in decode (section 4.2): the last N-1 committed ids
+ * of every sequence, kept on the device. Committed position p of sequence b sits in
+ * ring[b*(N-1) + p mod (N-1)]; positions before 0 read as the pad id 0. */
+typedef struct ngram_cache {
+  int32_t* ring;  /* device [nseq, N-1] int32 (may be NULL when N = 1) */
+  int64_t* len;   /* device [nseq] int64: ids committed so far */
+  int32_t nseq;   /* sequences, >= 0 */
+} ngram_cache;
+
+/* ---------------------------------------------------------------- workspace
+ * Scratch for up to `max_rows` output rows: the error flags (int32 at offset 0), the E_0
+ * token of every row (int32 [max_rows] at *tok_off) and the hash indices (int32
+ * [max_rows, S] at *idx_off). Must be 256-byte aligned and zero-filled once before first
+ * use (the flags are sticky until cleared). Returns the size in bytes, 0 on a bad config. */
+size_t ngram_embed_workspace_size(const ngram_embed_config* cfg, int64_t max_rows);
+int ngram_embed_workspace_layout(const ngram_embed_config* cfg, int64_t max_rows,
+                                 size_t* tok_off, size_t* idx_off);
+
+/* ---------------------------------------------------------------- kernel 1: hash
+ * idx[i*S + s] = H_{n,k} of position i (section A2 rolling hash), for ntok packed tokens
+ * split into nseq sequences by cu_seqlens (device int32 [nseq+1], c_0 = 0, c_nseq = ntok).
+ * tokens: device int32 [ntok]; idx: device int32 [ntok, S]. The reduction is Horner's rule
+ * modulo V_{n,k} in exact 64-bit integers, so no intermediate overflows.
+ * err_flags: device int32 or NULL; bad ids and bad cu_seqlens are OR-ed into it (their
+ * rows hold unspecified but in-range indices). */
+int ngram_embed_hash(const ngram_embed_config* cfg, const int32_t* tokens,
+                     const int32_t* cu_seqlens, int32_t nseq, int64_t ntok, int32_t* idx,
+                     int32_t* err_flags, void* stream);
+
+/* ---------------------------------------------------------------- kernel 2: gather
+ * G[r, s*d + c] = E_{n,k}[idx[r*S + s], c] for nrows rows: the concatenation of the S
+ * sub-table rows that the final form reads (section A2). G: device [nrows, D] in the
+ * config's dtype, 16-byte aligned. Indices are clamped into [0, V_{n,k}) so a bad index
+ * never reads outside its table. Stand-alone form of the gather that ngram_embed_project
+ * fuses into its matrix-core loads. */
+int ngram_embed_gather(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                       const int32_t* idx, int64_t nrows, void* G, void* stream);
+
+/* ---------------------------------------------------------------- kernels 2+3: projection
+ * out[r, :] = ( E_0[tok[r], :] + sum_s W_{n,k} E_{n,k}[idx[r*S + s], :] ) / (S + 1)
+ * for nrows rows: the sub-table rows are gathered straight into on-chip memory and
+ * multiplied by the stacked W on the matrix cores, with the E_0 add and the scale in the
+ * epilogue. tok: device int32 [nrows]; rows whose tok is outside [0, V0) are written as
+ * zeros (decode uses -1 for unused slots). idx as produced by ngram_embed_hash (clamped
+ * like ngram_embed_gather). out: device [nrows, D] in the config's dtype. */
+int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                        const int32_t* idx, const int32_t* tok, int64_t nrows, void* out,
+                        void* stream);
+
+/* ---------------------------------------------------------------- prefill
+ * The whole forward pass over packed sequences: ngram_embed_hash into the workspace, then
+ * ngram_embed_project with tok = tokens. out: device [ntok, D]. ws: workspace of at least
+ * ngram_embed_workspace_size(cfg, ntok) bytes; bad ids set NGRAM_FLAG_BAD_TOKEN there. */
+int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                        const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
+                        int64_t ntok, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- kernel 4: decode
+ * Fill a cache from prefilled sequences: len[b] = sequence length, ring = its last N-1 ids
+ * (slots of positions before 0 hold the pad id 0). tokens/cu_seqlens as in
+ * ngram_embed_hash with nseq = cache->nseq. */
+int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const int32_t* tokens,
+                     const int32_t* cu_seqlens, int64_t ntok, void* stream);
+
+/* One decode / speculative-verify step. new_tokens: device int32 [nseq, tmax]; sequence b
+ * proposes its first n_new[b] entries (device int32 [nseq], 0 <= n_new <= tmax <= 8) as the
+ * positions len[b], len[b]+1, ... . out[b, j, :] (device [nseq, tmax, D]) is the embedding
+ * that a prefill of (committed history, new_tokens[b, 0..j]) gives its last position; rows
+ * j >= n_new[b] are zeros. The context comes from the cache (the last N-1 committed ids),
+ * never from the host. If n_commit (device int32 [nseq], 0 <= n_commit <= n_new) is not
+ * NULL, the first n_commit[b] new ids are then appended to the cache, as by
+ * ngram_cache_commit. ws: at least ngram_embed_workspace_size(cfg, nseq * tmax) bytes; the
+ * step's indices stay there (layout above) until the next call. */
+int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                       ngram_cache* cache, const int32_t* new_tokens, const int32_t* n_new,
+                       int32_t tmax, const int32_t* n_commit, void* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Append the first n_accept[b] (device int32 [nseq], 0 <= n_accept <= tmax) ids of
+ * new_tokens[b, :] (device int32 [nseq, tmax]) to sequence b's cache and advance len[b].
+ * err_flags: device int32 or NULL (NGRAM_FLAG_BAD_COUNT; such counts are clamped). */
+int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
+                       const int32_t* new_tokens, const int32_t* n_accept, int32_t tmax,
+                       int32_t* err_flags, void* stream);
+
+/* ---------------------------------------------------------------- errors
+ * Wait for `stream`, then copy the workspace's error flags to *flags (host). */
+int ngram_embed_read_error_flag(const void* ws, int32_t* flags, void* stream);
+/* Enqueue a reset of the workspace's error flags to 0 (a kernel, not a memset, so it may be
+ * captured in a HIP graph). */
+int ngram_embed_clear_error_flag(void* ws, void* stream);
+/* Static English text for a status code. */
+const char* ngram_embed_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NGRAM_EMBED_H */

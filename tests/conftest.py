@@ -26,3 +26,11 @@ def lib():
     """The HIP library binding; GPU tests fail loudly when it is missing."""
     import gram_embedding_layer_amd as g
     return g.load()
+
+
+@pytest.fixture(scope="session")
+def tables_30b():
+    """Device tables of the 30B-parameter layer (about 61 GB), shared by the prefill and
+    decode tests of that layer."""
+    import workloads as WL
+    return WL.device_tables(WL.workload("prefill_64k_30b"))

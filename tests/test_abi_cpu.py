@@ -1,0 +1,200 @@
+"""CPU checks of the C ABI: the library loads, exports what include/ngram_embed.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU is touched here: every
+call below carries at least one argument that validation refuses)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import gram_embedding_layer_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ngram_embed.h")
+
+FAKE = 0x100000  # 1 MiB: aligned, never dereferenced because validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(g.LIB_PATH):
+        pytest.fail("libngram_embed.so not built (python -m gram_embedding_layer_amd.build)")
+    return g.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ngram_[a-z_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ngram_embed_prefill", "ngram_embed_decode", "ngram_embed_hash",
+              "ngram_embed_gather", "ngram_embed_project", "ngram_cache_init",
+              "ngram_cache_commit"):
+        assert n in names
+    assert len(names) == 12
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_binding_names_match_header():
+    for n in declared_functions():
+        assert callable(getattr(g, n)), n
+
+
+def tiny_cfg(**kw):
+    args = dict(N=3, K=2, D=64, dtype="bf16", V0=1000, V=[5003, 7001, 6007, 8009])
+    args.update(kw)
+    return g.Config(**args)
+
+
+def test_status_strings(lib):
+    assert g.ngram_embed_status_string(0) == "ok"
+    for s in range(-6, 0):
+        assert g.ngram_embed_status_string(s) != "unknown status"
+    assert g.ngram_embed_status_string(-99) == "unknown status"
+
+
+def test_workspace_size_and_layout(lib):
+    cfg = tiny_cfg()
+    rows = 1000
+    tok_off, idx_off = g.ngram_embed_workspace_layout(cfg, rows)
+    assert tok_off == 256
+    assert idx_off == 256 + ((rows * 4 + 255) // 256) * 256
+    size = g.ngram_embed_workspace_size(cfg, rows)
+    assert size == idx_off + ((rows * cfg.S * 4 + 255) // 256) * 256
+    assert size % 256 == 0
+    assert g.ngram_embed_workspace_size(cfg, -1) == 0
+    assert g.ngram_embed_workspace_size(tiny_cfg(D=63), 10) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=62), -1),                       # D not a multiple of (N-1)K
+    (dict(D=36, V=[5, 7, 11, 13]), -1),     # d = 9 bf16 = 18 bytes: not whole 16-byte rows
+    (dict(N=0), -1),
+    (dict(K=0), -1),
+    (dict(N=17), -1),
+    (dict(N=3, K=33, D=66 * 64, V=[7] * 66), -1),   # more than 64 sub-tables
+    (dict(dtype=7), -2),
+    (dict(V0=0), -1),
+    (dict(V0=2 ** 31), -1),
+    (dict(V=[5003, 0, 6007, 8009]), -1),
+    (dict(V=[5003, 2 ** 31, 6007, 8009]), -1),
+])
+def test_config_validation(lib, kw, status):
+    cfg = tiny_cfg(**kw)
+    c, keep = cfg._c()
+    rc = lib.ngram_embed_prefill(ctypes.byref(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, 1 << 20, 0)
+    assert rc == status
+    assert lib.ngram_embed_workspace_size(ctypes.byref(c), 16) == 0
+
+
+def _tables_c(n_sub, e0=FAKE, w=FAKE, sub=FAKE):
+    arr = (ctypes.c_void_p * max(1, n_sub))(*([sub] * n_sub))
+    return g._CTables(e0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), w), arr
+
+
+def test_prefill_argument_checks(lib):
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    ws_need = g.ngram_embed_workspace_size(cfg, 16)
+    P = ctypes.byref
+    # workspace too small / misaligned
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need - 1, 0) == -4
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE + 64, ws_need, 0) == -4
+    # negative sizes, no sequences for tokens
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, -1, FAKE, FAKE, ws_need, 0) == -1
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 0, 16, FAKE, FAKE, ws_need, 0) == -1
+    # misaligned table / output / token pointers
+    Tb, k3 = _tables_c(4, e0=FAKE + 8)
+    assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+    Tb, k4 = _tables_c(4, sub=FAKE + 2)
+    assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE + 8, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE + 1, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+
+
+def test_decode_and_cache_argument_checks(lib):
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    P = ctypes.byref
+    cache = g._CCache(FAKE, FAKE, 4)
+    ws_need = g.ngram_embed_workspace_size(cfg, 4 * 5)
+    for tmax in (0, 9):
+        assert lib.ngram_embed_decode(P(c), P(T), P(cache), FAKE, FAKE, tmax, None, FAKE, FAKE,
+                                      ws_need, 0) == -1
+    assert lib.ngram_embed_decode(P(c), P(T), P(cache), FAKE, FAKE, 5, None, FAKE, FAKE,
+                                  ws_need - 256, 0) == -4
+    assert lib.ngram_embed_decode(P(c), P(T), None, FAKE, FAKE, 5, None, FAKE, FAKE,
+                                  ws_need, 0) == -1
+    bad_len = g._CCache(FAKE, FAKE + 4, 4)
+    assert lib.ngram_embed_decode(P(c), P(T), P(bad_len), FAKE, FAKE, 5, None, FAKE, FAKE,
+                                  ws_need, 0) == -3
+    assert lib.ngram_embed_decode(P(c), P(T), P(cache), FAKE, FAKE, 5, FAKE + 2, FAKE, FAKE,
+                                  ws_need, 0) == -3
+    assert lib.ngram_cache_commit(P(c), P(cache), FAKE, FAKE, 9, None, 0) == -1
+    assert lib.ngram_cache_commit(P(c), P(bad_len), FAKE, FAKE, 5, None, 0) == -3
+    assert lib.ngram_cache_init(P(c), None, FAKE, FAKE, 10, 0) == -1
+    assert lib.ngram_cache_init(P(c), P(bad_len), FAKE, FAKE, 10, 0) == -3
+    neg = g._CCache(FAKE, FAKE, -1)
+    assert lib.ngram_cache_init(P(c), P(neg), FAKE, FAKE, 10, 0) == -1
+
+
+def test_hash_gather_project_argument_checks(lib):
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    P = ctypes.byref
+    assert lib.ngram_embed_hash(P(c), FAKE, FAKE, 1, -5, FAKE, None, 0) == -1
+    assert lib.ngram_embed_hash(P(c), FAKE + 2, FAKE, 1, 5, FAKE, None, 0) == -3
+    assert lib.ngram_embed_hash(P(c), FAKE, FAKE, 1, 5, FAKE, FAKE + 1, 0) == -3
+    assert lib.ngram_embed_gather(P(c), P(T), FAKE, -1, FAKE, 0) == -1
+    assert lib.ngram_embed_gather(P(c), P(T), FAKE, 5, FAKE + 4, 0) == -3
+    assert lib.ngram_embed_project(P(c), P(T), FAKE, FAKE, 5, FAKE + 4, 0) == -3
+    Tb, k3 = _tables_c(4, w=0)
+    assert lib.ngram_embed_project(P(c), P(Tb), FAKE, FAKE, 5, FAKE, 0) == -3
+    assert lib.ngram_embed_read_error_flag(FAKE + 16, None, 0) == -3
+    assert lib.ngram_embed_clear_error_flag(FAKE + 16, 0) == -3
+
+
+def test_zero_sized_calls_enqueue_nothing(lib):
+    # ntok = 0 / nrows = 0 / nseq = 0 succeed without touching the device.
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    P = ctypes.byref
+    ws = g.ngram_embed_workspace_size(cfg, 0)
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 0, 0, FAKE, FAKE, ws, 0) == 0
+    assert lib.ngram_embed_hash(P(c), FAKE, FAKE, 0, 0, FAKE, None, 0) == 0
+    assert lib.ngram_embed_gather(P(c), P(T), FAKE, 0, FAKE, 0) == 0
+    assert lib.ngram_embed_project(P(c), P(T), FAKE, FAKE, 0, FAKE, 0) == 0
+    empty = g._CCache(FAKE, FAKE, 0)
+    assert lib.ngram_embed_decode(P(c), P(T), P(empty), FAKE, FAKE, 5, None, FAKE, FAKE, ws, 0) == 0
+    assert lib.ngram_cache_commit(P(c), P(empty), FAKE, FAKE, 5, None, 0) == 0
+    assert lib.ngram_cache_init(P(c), P(empty), FAKE, FAKE, 0, 0) == 0
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not installed")
+def test_host_validation_under_sanitizers(tmp_path):
+    """The HIP-free validation unit, built with g++ under ASan/UBSan and exercised."""
+    csrc = os.path.join(ROOT, "gram_embedding_layer_amd", "csrc")
+    exe = tmp_path / "validate_test"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}",
+           os.path.join(csrc, "validate.cpp"), os.path.join(ROOT, "tests", "validate_test.cpp"),
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "all passed" in res.stdout

@@ -1,0 +1,65 @@
+// Host unit test of the HIP-free config validation (built with g++ under sanitizers).
+#include <cstdio>
+#include <cstdlib>
+
+#include "layer_desc.h"
+
+static int failures = 0;
+#define EXPECT(cond)                                              \
+  do {                                                            \
+    if (!(cond)) {                                                \
+      std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #cond);  \
+      ++failures;                                                 \
+    }                                                             \
+  } while (0)
+
+int main() {
+  using ngram::LayerDesc;
+  int64_t V[64];
+  for (int i = 0; i < 64; ++i) V[i] = 1009 + 2 * i;
+  ngram_embed_config c{3, 2, 64, NGRAM_BF16, 1000, V};
+  LayerDesc L{};
+  EXPECT(ngram::describe(&c, &L) == NGRAM_OK);
+  EXPECT(L.S == 4 && L.d == 16 && L.esz == 2 && L.V0 == 1000 && L.V[3] == 1015u);
+
+  // N = 1: no sub-tables, V may be NULL
+  ngram_embed_config c1{1, 4, 64, NGRAM_F32, 50, nullptr};
+  EXPECT(ngram::describe(&c1, &L) == NGRAM_OK && L.S == 0 && L.d == 0);
+
+  ngram_embed_config bad = c;
+  bad.D = 60;                      // 60 % 4 != 0
+  EXPECT(ngram::describe(&bad, &L) == NGRAM_EINVAL);
+  bad = c;
+  bad.D = 4 * 12;                  // d = 12 bf16 = 24 bytes: not whole 16-byte vectors
+  EXPECT(ngram::describe(&bad, &L) == NGRAM_EINVAL);
+  bad = c;
+  bad.dtype = 3;
+  EXPECT(ngram::describe(&bad, &L) == NGRAM_EDTYPE);
+  bad = c;
+  bad.V = nullptr;
+  EXPECT(ngram::describe(&bad, &L) == NGRAM_EINVAL);
+  bad = c;
+  bad.N = 17;
+  EXPECT(ngram::describe(&bad, &L) == NGRAM_EINVAL);
+  bad = c;
+  bad.K = 33;                      // (N-1)K = 66 > 64
+  EXPECT(ngram::describe(&bad, &L) == NGRAM_EINVAL);
+  EXPECT(ngram::describe(nullptr, &L) == NGRAM_EINVAL);
+
+  // largest accepted sizes: V0 and V just below 2^31 keep V * V0 < 2^62
+  int64_t Vbig[4] = {(int64_t(1) << 31) - 1, 3, 5, 7};
+  ngram_embed_config big{3, 2, 64, NGRAM_F32, (int64_t(1) << 31) - 1, Vbig};
+  EXPECT(ngram::describe(&big, &L) == NGRAM_OK && L.V[0] == 2147483647u);
+
+  ngram::WsLayout w;
+  EXPECT(ngram::describe(&c, &L) == NGRAM_OK);
+  EXPECT(ngram::ws_layout(L, 1000, &w) && w.tok_off == 256 && w.idx_off == 256 + 4096 &&
+         w.total == w.idx_off + 16128);
+  EXPECT(!ngram::ws_layout(L, -1, &w));
+  EXPECT(ngram::aligned(reinterpret_cast<void*>(0x1000), 256));
+  EXPECT(!ngram::aligned(reinterpret_cast<void*>(0x1004), 16));
+  EXPECT(!ngram::aligned(nullptr, 4));
+
+  if (failures == 0) std::printf("all passed\n");
+  return failures == 0 ? 0 : 1;
+}
