@@ -53,19 +53,59 @@ struct ProjArgs {
 
 // ------------------------------------------------------------------ bf16 matrix-core path
 
-constexpr int kBN = 256;
-constexpr int kBK = 64;
+constexpr int kBN = 256;          // outputs per tile
+constexpr int kBK = 64;           // contraction depth of one slice: 128 bytes of a row, one
+                                  // full L2 line per row per load
+constexpr int kIdxBytes = 16384;  // LDS for the tile's hash indices (BM * S int32)
+
+// LDS slice buffers per tile height (160 KB of LDS per CU, 16 KB of it for indices):
+// 256-row tiles double-buffer, shorter tiles keep two slices in flight.
+template <int BM> struct Stages { static constexpr int value = BM >= 256 ? 2 : 3; };
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (global_load_lds_dwordx4). Written as asm so that its completion is waited for only by
+// the explicit vmcnt waits below (the compiler would otherwise drain every load in flight
+// before each LDS read); it has no register result.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\t"
+               "s_nop 0\n\t"
+               "global_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's global loads are in flight (they complete in issue
+// order), then meet the other waves. The memory clobber keeps LDS accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_meet() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\t"
+               "s_waitcnt lgkmcnt(0)\n\t"
+               "s_barrier" :: "n"(N) : "memory");
+}
+
+// Wave grid of a tile: 8 waves (2 per SIMD, so one can issue while the other waits on
+// memory), WGM along rows x 8/WGM along outputs; each wave owns a WM x WN block of
+// 32x32 matrix-core tiles.
+template <int BM> struct WaveGrid { static constexpr int WGM = BM >= 128 ? 4 : 2; };
 
 template <int BM>
-__global__ __launch_bounds__(256, 1) void proj_mfma_kernel(const ProjArgs a) {
-  constexpr int WM = BM / 2;        // rows per wave (2 x 2 waves)
-  constexpr int TI = WM / 32;       // 32-row MFMA blocks per wave
-  constexpr int TJ = 4;             // 32-output MFMA blocks per wave (128 outputs)
-  constexpr int RA = BM / 32;       // A rows loaded per thread per slice
-  constexpr int RB = kBN / 32;      // W rows loaded per thread per slice
-  constexpr int A_ELEMS = BM * kBK;
-  constexpr int B_ELEMS = kBN * kBK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (A_ELEMS + B_ELEMS)];
+__global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
+  constexpr int NST = Stages<BM>::value;
+  constexpr int WGM = WaveGrid<BM>::WGM;
+  constexpr int WGN = 8 / WGM;
+  constexpr int WM = BM / WGM;           // rows per wave
+  constexpr int WN = kBN / WGN;          // outputs per wave
+  constexpr int TI = WM / 32;            // 32-row MFMA blocks per wave
+  constexpr int TJ = WN / 32;            // 32-output MFMA blocks per wave
+  constexpr int A_BYTES = BM * kBK * 2;  // rows of 128 bytes, XOR-swizzled 16-byte chunks
+  constexpr int B_BYTES = kBN * kBK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int QA = BM / 64;            // A loads per wave per slice (8 rows each)
+  constexpr int QB = kBN / 64;           // W loads per wave per slice
+  constexpr int PER_SLICE = QA + QB;
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+  __shared__ int32_t sidx[kIdxBytes / 4];
 
   // -- XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous range
   //    of virtual tiles and walk a range 8 row tiles at a time, outputs slowest.
@@ -84,70 +124,49 @@ __global__ __launch_bounds__(256, 1) void proj_mfma_kernel(const ProjArgs a) {
   const int64_t m0 = int64_t(tm) * BM;
   const int n0 = tn * kBN;
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int lrow = t >> 3, lc = t & 7;
-  const int swz = (lc ^ (lrow & 7)) * 8;  // swizzled 16-byte chunk of this thread's rows
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w / WGN, wn = w % WGN;
 
+  // -- hash indices of the tile's rows (rows past the batch repeat the last row)
+  for (int e = t; e < BM * a.S; e += 512) {
+    const int r = e / a.S, s = e - r * a.S;
+    const int64_t m = m0 + r < a.nrows ? m0 + r : a.nrows - 1;
+    sidx[e] = a.idx[m * a.S + s];
+  }
+  __syncthreads();
+
+  // -- loads: lane p fills LDS chunk (row p/8, chunk p%8) of an 8-row group with logical
+  //    16-byte chunk c = (p%8) ^ (row%8), so that fragment reads (8 lanes = 8 rows, one
+  //    logical chunk) hit 8 different bank groups; 8 lanes read one 128-byte row piece.
+  const int prow = lane >> 3;
+  const int pchunk = (lane & 7) ^ prow;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)lds));
   const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E);
-  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
-
-  // -- A loader: rows m0 + lrow + 32 i (clamped into the batch; extra rows are not stored)
-  int64_t arow[RA];
-#pragma unroll
-  for (int i = 0; i < RA; ++i) {
-    const int64_t m = m0 + lrow + 32 * i;
-    arow[i] = m < a.nrows ? m : a.nrows - 1;
-  }
-  int32_t nid[RA];                // indices of the next sub-table, fetched one table early
-  const uint16_t* ap[RA];         // row pointers into the current sub-table
-#pragma unroll
-  for (int i = 0; i < RA; ++i) nid[i] = a.idx[arow[i] * a.S];
-#pragma unroll
-  for (int i = 0; i < RA; ++i) {
-    const uint32_t id = min(uint32_t(nid[i]), a.Vm1[0]);
-    ap[i] = E[0] + int64_t(id) * a.d + lc * 8;
-  }
-  if (a.S > 1) {
-#pragma unroll
-    for (int i = 0; i < RA; ++i) nid[i] = a.idx[arow[i] * a.S + 1];
-  }
-  const uint16_t* bp = W + int64_t(n0 + lrow) * a.D + lc * 8;
-
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.D + pchunk * 8;
+  const uint16_t* ap[QA];
   const int KT = a.D / kBK;      // slices
   const int kps = a.d / kBK;     // slices per sub-table
-  int s_cur = 0;
-  u32x4_t ra[RA], rb[RB];
+  int s_cur = -1;
 
-  auto gload = [&](int kt) __attribute__((always_inline)) {
-    if (kt > 0 && kt == (s_cur + 1) * kps) {   // first slice of the next sub-table
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    if (kt == (s_cur + 1) * kps) {          // first slice of the next sub-table
       ++s_cur;
 #pragma unroll
-      for (int i = 0; i < RA; ++i) {
-        const uint32_t id = min(uint32_t(nid[i]), a.Vm1[s_cur]);
-        ap[i] = E[s_cur] + int64_t(id) * a.d + lc * 8;
-      }
-      if (s_cur + 1 < a.S) {
-#pragma unroll
-        for (int i = 0; i < RA; ++i) nid[i] = a.idx[arow[i] * a.S + s_cur + 1];
+      for (int q = 0; q < QA; ++q) {
+        const int r = w * (BM / 8) + q * 8 + prow;
+        const uint32_t id = min(uint32_t(sidx[r * a.S + s_cur]), a.Vm1[s_cur]);
+        ap[q] = E[s_cur] + int64_t(id) * a.d + pchunk * 8;
       }
     }
+    const uint32_t sb = lds0 + uint32_t(kt % NST) * STAGE;
     const int koff = (kt - s_cur * kps) * kBK;
 #pragma unroll
-    for (int i = 0; i < RA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + koff);
+    for (int q = 0; q < QA; ++q) dma16(ap[q] + koff, sb + w * (BM * 16) + q * 1024);
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
-      rb[i] = *reinterpret_cast<const u32x4_t*>(bp + int64_t(32 * i) * a.D + kt * kBK);
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* As = lds + buf * (A_ELEMS + B_ELEMS);
-    uint16_t* Bs = As + A_ELEMS;
-#pragma unroll
-    for (int i = 0; i < RA; ++i)
-      *reinterpret_cast<u32x4_t*>(As + (lrow + 32 * i) * kBK + swz) = ra[i];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-      *reinterpret_cast<u32x4_t*>(Bs + (lrow + 32 * i) * kBK + swz) = rb[i];
+    for (int q = 0; q < QB; ++q)
+      dma16(bp + int64_t(q * 8) * a.D + kt * kBK, sb + A_BYTES + w * 4096 + q * 1024);
   };
 
   f32x16_t acc[TJ][TI];
@@ -158,43 +177,54 @@ __global__ __launch_bounds__(256, 1) void proj_mfma_kernel(const ProjArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // fragment lane (fr, fk): 8 consecutive k (logical chunk 2*kk + fk) of row fr
   const int fr = lane & 31, fk = lane >> 5;
+  const int arow0 = (wm * WM + fr) * 128;          // byte offset of the lane's first A row
+  const int brow0 = A_BYTES + (wn * WN + fr) * 128;
+  int pcs[4];                                      // physical chunk byte offset per k-step
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) pcs[kk] = ((2 * kk + fk) ^ (fr & 7)) * 16;
+
+  bf16x8_t wf[2][TJ], xf[2][TI];
+  auto frags = [&](const char* sp, int kk, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      wf[buf][j] = *reinterpret_cast<const bf16x8_t*>(sp + brow0 + j * 32 * 128 + pcs[kk]);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+      xf[buf][i] = *reinterpret_cast<const bf16x8_t*>(sp + arow0 + i * 32 * 128 + pcs[kk]);
+  };
+  // W block as the first operand: each lane's results are 4 consecutive outputs of one
+  // row, which makes the epilogue's E_0 reads and stores 8 bytes wide.
+  auto mma = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], xf[buf][i], acc[j][i],
+                                                            0, 0, 0);
+  };
+
+  for (int p = 0; p < NST - 1 && p < KT; ++p) issue(p);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint16_t* As = lds + cur * (A_ELEMS + B_ELEMS);
-    const uint16_t* Bs = As + A_ELEMS;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      // lane (fr, fk) holds 8 consecutive k of row fr: chunk 2*kk + fk of the slice
-      const int ch = kk * 2 + fk;
-      bf16x8_t wf[TJ], xf[TI];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int row = wn * 128 + j * 32 + fr;
-        wf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + row * kBK + ((ch ^ (row & 7)) * 8));
-      }
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int row = wm * WM + i * 32 + fr;
-        xf[i] = *reinterpret_cast<const bf16x8_t*>(As + row * kBK + ((ch ^ (row & 7)) * 8));
-      }
-      // W block as the first operand: each lane's results are 4 consecutive outputs of
-      // one row, which makes the epilogue's E_0 reads and stores 8 bytes wide.
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[j][i], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
+    // own loads of slice kt done (later slices may stay in flight), then all waves meet:
+    // slice kt is complete in LDS and every wave is past slice kt-1, whose buffer the
+    // load of slice kt+NST-1 reuses.
+    if (NST == 3 && kt + 1 < KT) wait_loads_and_meet<PER_SLICE>();
+    else wait_loads_and_meet<0>();
+    const char* sp = lds + (kt % NST) * STAGE;
+    frags(sp, 0, 0);
+    frags(sp, 1, 1);
+    if (kt + NST - 1 < KT) issue(kt + NST - 1);
+    mma(0);
+    frags(sp, 2, 0);
+    mma(1);
+    frags(sp, 3, 1);
+    mma(0);
+    mma(1);
   }
 
-  // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*128 + 32j + 8g + 4fk + q of
+  // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*WN + 32j + 8g + 4fk + q of
   //    row m = m0 + wm*WM + 32i + fr.
   const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0);
   uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out);
@@ -210,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void proj_mfma_kernel(const ProjArgs a) {
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + j * 32 + g * 8 + fk * 4;
+        const int n = n0 + wn * WN + j * 32 + g * 8 + fk * 4;
         u32x2_t res = {0u, 0u};
         if (ok) {
           const u32x2_t ev = *reinterpret_cast<const u32x2_t*>(e0 + n);
@@ -329,7 +359,7 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int32_t S, int32_t D, int esz,
     a.nrows = n;
     a.tiles_m = int32_t((n + BM - 1) / BM);
     a.tiles_n = D / kBN;
-    hipLaunchKernelGGL(proj_mfma_kernel<BM>, dim3(unsigned(a.tiles_m * a.tiles_n)), dim3(256),
+    hipLaunchKernelGGL(proj_mfma_kernel<BM>, dim3(unsigned(a.tiles_m * a.tiles_n)), dim3(512),
                        0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -368,10 +398,14 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
   }
   if (L.dtype == NGRAM_BF16 && L.D % kBN == 0 && L.d % kBK == 0) {
     // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
-    // shorter tiles so that enough blocks exist to occupy the 256 CUs.
+    // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
+    // rows' hash indices in LDS, BM * S <= kIdxBytes / 4.
     const int64_t tiles_n = L.D / kBN;
-    if (((nrows + 255) / 256) * tiles_n >= 512) return run_mfma<256>(a, nrows, L.S, L.D, 2, st);
-    if (((nrows + 127) / 128) * tiles_n >= 256) return run_mfma<128>(a, nrows, L.S, L.D, 2, st);
+    const int64_t idx_cap = kIdxBytes / 4;
+    if (((nrows + 255) / 256) * tiles_n >= 512 && 256 * L.S <= idx_cap)
+      return run_mfma<256>(a, nrows, L.S, L.D, 2, st);
+    if (((nrows + 127) / 128) * tiles_n >= 256 && 128 * L.S <= idx_cap)
+      return run_mfma<128>(a, nrows, L.S, L.D, 2, st);
     return run_mfma<64>(a, nrows, L.S, L.D, 2, st);
   }
   const unsigned gy = unsigned((L.D + 63) / 64);
