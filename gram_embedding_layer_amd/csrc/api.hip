@@ -160,15 +160,12 @@ int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* 
   char* w = static_cast<char*>(ws);
   int32_t* tok = reinterpret_cast<int32_t*>(w + lay.tok_off);
   int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
+  // hash (and commit, when asked) in one kernel; the projection reads only tok/idx, so the
+  // cache may advance before it runs
   rc = hip_status(ngram::launch_hash_decode(L, cache->ring, cache->len, new_tokens, n_new,
-                                            cache->nseq, tmax, tok, idx, ws_flags(ws), st));
+                                            n_commit, cache->nseq, tmax, tok, idx, ws_flags(ws),
+                                            st));
   if (rc != NGRAM_OK) return rc;
-  // The projection reads only tok/idx, so the cache may advance before it runs.
-  if (n_commit != nullptr) {
-    rc = hip_status(ngram::launch_cache_commit(L, cache->ring, cache->len, new_tokens, n_commit,
-                                               n_new, cache->nseq, tmax, ws_flags(ws), st));
-    if (rc != NGRAM_OK) return rc;
-  }
   return hip_status(
       ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tok, rows, out, st));
 }

@@ -7,55 +7,55 @@
 // The projection kernel performs the same reads straight into LDS; this kernel writes them
 // to HBM and is the bandwidth probe of the gather.
 //
-// Layout on MI355X: one grid row (blockIdx.y) per sub-table, so the table base is a
-// wave-uniform scalar; each lane moves 16-byte vectors, consecutive lanes cover one table
-// row (a 512-byte row is 32 lanes), and each lane keeps kUnroll independent rows in flight
-// to cover HBM latency on random rows.
+// Layout on MI355X: idx [rows, S] and G [rows, S*d] list the (row, sub-table) pairs in the
+// same order, so G is a flat array of pair segments: 16-byte chunk `item` of G is chunk
+// item % cpr of pair item / cpr. Consecutive lanes take consecutive chunks: every table row
+// is read as one contiguous piece and every write is fully sequential. Stores are
+// non-temporal (G is not re-read here); loads stay cached, since with Zipf-distributed ids
+// many n-grams repeat within a batch. Each lane keeps kUnroll chunks in flight. These
+// choices measured best on the 30B-parameter layer with Zipf(1.1) ids.
 #include "kernels.h"
 
 namespace ngram {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct GatherArgs {
   const char* E[NGRAM_MAX_SUBTABLES];
   uint32_t Vm1[NGRAM_MAX_SUBTABLES];  // V_{n,k} - 1, the largest valid index
-  const int32_t* idx;                 // [nrows, S]
-  char* G;                            // [nrows, D]
-  int64_t nrows;
-  int32_t S;
-  uint32_t cpr;                       // 16-byte chunks per sub-table row
+  const int32_t* idx;                 // [rows, S]
+  char* G;                            // [rows, S * d]
+  uint32_t total;                     // 16-byte chunks in this launch: rows * S * cpr
+  uint32_t S;
+  uint32_t cpr;                       // 16-byte chunks per sub-table row (d * esz / 16)
   uint32_t row_bytes;                 // d * esz
-  uint32_t g_row_bytes;               // D * esz
 };
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a) {
-  const int s = blockIdx.y;
-  const char* __restrict__ table = a.E[s];
-  const uint32_t vmax = a.Vm1[s];
-  // the host splits launches so that nrows * cpr < 2^30: 32-bit index math
-  const uint32_t total = uint32_t(a.nrows) * a.cpr;
   const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-  uint4 v[kUnroll];
-  int64_t dst[kUnroll];
+  u32x4_t v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t item = base + u * kThreads;
-    dst[u] = -1;
-    if (item < total) {
-      const uint32_t r = item / a.cpr;
-      const uint32_t c = item - r * a.cpr;
-      uint32_t id = uint32_t(a.idx[int64_t(r) * a.S + s]);
-      id = id > vmax ? vmax : id;
-      v[u] = *reinterpret_cast<const uint4*>(table + int64_t(id) * a.row_bytes + c * 16u);
-      dst[u] = int64_t(r) * a.g_row_bytes + int64_t(s) * a.row_bytes + c * 16u;
+    if (item < a.total) {
+      const uint32_t p = item / a.cpr;                 // (row, sub-table) pair
+      const uint32_t c = item - p * a.cpr;             // chunk within the row
+      const uint32_t s = p % a.S;
+      uint32_t id = uint32_t(a.idx[p]);
+      id = id > a.Vm1[s] ? a.Vm1[s] : id;
+      v[u] = *reinterpret_cast<const u32x4_t*>(a.E[s] + int64_t(id) * a.row_bytes + c * 16u);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
-    if (dst[u] >= 0) *reinterpret_cast<uint4*>(a.G + dst[u]) = v[u];
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t item = base + u * kThreads;
+    if (item < a.total)
+      __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(a.G + int64_t(item) * 16));
+  }
 }
 
 }  // namespace
@@ -67,19 +67,20 @@ hipError_t launch_gather(const LayerDesc& L, const void* const* E, const int32_t
     a.E[s] = static_cast<const char*>(E[s]);
     a.Vm1[s] = L.V[s] - 1u;
   }
-  a.S = L.S;
+  a.S = uint32_t(L.S);
   a.row_bytes = uint32_t(L.d) * uint32_t(L.esz);
   a.cpr = a.row_bytes / 16u;
-  a.g_row_bytes = uint32_t(L.D) * uint32_t(L.esz);
-  const int64_t max_rows = (int64_t(1) << 30) / a.cpr;
+  // 32-bit chunk numbering: launches of at most 2^30 chunks, whole rows each
+  const int64_t chunks_per_row = int64_t(L.S) * a.cpr;
+  const int64_t max_rows = (int64_t(1) << 30) / chunks_per_row;
   const int64_t per_block = int64_t(kThreads) * kUnroll;
   for (int64_t r0 = 0; r0 < nrows; r0 += max_rows) {
     const int64_t n = nrows - r0 < max_rows ? nrows - r0 : max_rows;
     a.idx = idx + r0 * L.S;
-    a.G = static_cast<char*>(G) + r0 * int64_t(a.g_row_bytes);
-    a.nrows = n;
-    const unsigned bx = unsigned((n * a.cpr + per_block - 1) / per_block);
-    hipLaunchKernelGGL(gather_kernel, dim3(bx, unsigned(L.S)), dim3(kThreads), 0, st, a);
+    a.G = static_cast<char*>(G) + r0 * chunks_per_row * 16;
+    a.total = uint32_t(n * chunks_per_row);
+    const unsigned blocks = unsigned((int64_t(a.total) + per_block - 1) / per_block);
+    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

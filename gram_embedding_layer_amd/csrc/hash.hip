@@ -6,13 +6,26 @@
 // The raw polynomial needs up to n*31 bits (more than 64 for n >= 3 at V0 = 2^17), so it is
 // evaluated by Horner's rule from the oldest id to the newest, reducing modulo V_{n,k} after
 // every step: x <- (x*V0 + t) mod V. With x < V < 2^31 and t < 2^32 every intermediate is
-// below 2^63 and the result equals the exact residue.
+// below 2^63, and the step's residue is taken exactly by Barrett reduction (below).
 #include "kernels.h"
 
 namespace ngram {
 namespace {
 
 constexpr int kThreads = 256;
+
+// One Horner step, exactly: (x*V0 + t) mod V for x < V < 2^31, V0 < 2^31, t < 2^32, so
+// y = x*V0 + t < 2^63. With m = floor((2^64 - 1) / V), q = floor(y*m / 2^64) satisfies
+// floor(y/V) - 1 <= q <= floor(y/V) (y*m/2^64 > y/V - y/2^64 - y/(V 2^64) > y/V - 1), so
+// r = y - q*V lies in [0, 2V) and one conditional subtraction leaves y mod V.
+__device__ __forceinline__ uint64_t horner_step(uint64_t x, uint64_t V0, uint32_t t, uint64_t V,
+                                                uint64_t m) {
+  const uint64_t y = x * V0 + t;
+  const uint64_t q = __umul64hi(y, m);
+  uint64_t r = y - q * V;
+  if (r >= V) r -= V;
+  return r;
+}
 
 // Hash one position. c[j] = t_{i-j} (pad 0 before the sequence start), j < NMAX.
 template <int NMAX>
@@ -21,11 +34,11 @@ __device__ __forceinline__ void hash_position(const LayerDesc& L, const uint32_t
   const uint64_t V0 = uint64_t(L.V0);
   for (int s = 0; s < L.S; ++s) {
     const int n = 2 + s / L.K;             // order of sub-table s = (n-2)K + (k-1)
-    const uint64_t V = L.V[s];
+    const uint64_t V = L.V[s], m = L.Vinv[s];
     uint64_t x = 0;
 #pragma unroll
     for (int j = NMAX - 1; j >= 0; --j)
-      if (j < n) x = (x * V0 + c[j]) % V;
+      if (j < n) x = horner_step(x, V0, c[j], V, m);
     out[s] = int32_t(x);
   }
 }
@@ -60,47 +73,74 @@ __global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
   hash_position<NMAX>(L, c, idx + i * L.S);
 }
 
+// One decode step: every thread hashes one (sequence, slot) row from the N-gram cache and
+// the step's new ids. A block holds whole sequences (kThreads / tmax of them), so when the
+// step also commits, all reads of a sequence's ring precede the barrier and the commit's
+// writes follow it.
 template <int NMAX>
 __global__ __launch_bounds__(kThreads) void hash_decode_kernel(
-    const LayerDesc L, const int32_t* __restrict__ ring, const int64_t* __restrict__ len,
-    const int32_t* __restrict__ newtok, const int32_t* __restrict__ n_new, int32_t nseq,
-    int32_t tmax, int32_t* __restrict__ tok, int32_t* __restrict__ idx,
-    int32_t* __restrict__ flags) {
-  const int64_t r = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (r >= int64_t(nseq) * tmax) return;
-  const int b = int(r / tmax), j = int(r % tmax);
-  int nn = n_new[b];
-  if (nn < 0 || nn > tmax) {
-    if (flags != nullptr && j == 0) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
-    nn = nn < 0 ? 0 : tmax;
-  }
-  int32_t* out = idx + r * L.S;
-  if (j >= nn) {  // unused slot: E_0 token -1 makes the projection write a zero row
-    tok[r] = -1;
-    for (int s = 0; s < L.S; ++s) out[s] = 0;
-    return;
-  }
-  const int32_t* nt = newtok + int64_t(b) * tmax;
-  const int32_t t = nt[j];
-  if (flags != nullptr && uint32_t(t) >= uint32_t(L.V0)) atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
-  tok[r] = t;
+    const LayerDesc L, int32_t* __restrict__ ring, int64_t* __restrict__ len,
+    const int32_t* __restrict__ newtok, const int32_t* __restrict__ n_new,
+    const int32_t* __restrict__ n_commit, int32_t nseq, int32_t tmax, int32_t* __restrict__ tok,
+    int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
+  const int spb = kThreads / tmax;                 // sequences per block
+  const int b = blockIdx.x * spb + threadIdx.x / tmax;
+  const int j = threadIdx.x % tmax;
+  const bool active = threadIdx.x < spb * tmax && b < nseq;
   const int nm1 = L.N - 1;
-  const int64_t committed = len[b];
-  uint32_t c[NMAX];
-#pragma unroll
-  for (int i = 0; i < NMAX; ++i) {
-    uint32_t v = 0;
-    if (i < L.N) {
-      if (j - i >= 0) {
-        v = uint32_t(nt[j - i]);                 // a new id of this step
-      } else {
-        const int64_t q = committed + (j - i);   // committed position, from the cache
-        if (q >= 0) v = uint32_t(ring[int64_t(b) * nm1 + q % nm1]);
-      }
+  int nn = 0;
+  int64_t committed = 0;
+  if (active) {
+    nn = n_new[b];
+    if (nn < 0 || nn > tmax) {
+      if (flags != nullptr && j == 0) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
+      nn = nn < 0 ? 0 : tmax;
     }
-    c[i] = v;
+    committed = len[b];
+    if (committed < 0) committed = 0;
+    const int64_t r = int64_t(b) * tmax + j;
+    int32_t* out = idx + r * L.S;
+    const int32_t* nt = newtok + int64_t(b) * tmax;
+    if (j >= nn) {  // unused slot: E_0 token -1 makes the projection write a zero row
+      tok[r] = -1;
+      for (int s = 0; s < L.S; ++s) out[s] = 0;
+    } else {
+      const int32_t t = nt[j];
+      if (flags != nullptr && uint32_t(t) >= uint32_t(L.V0))
+        atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
+      tok[r] = t;
+      uint32_t c[NMAX];
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) {
+        uint32_t v = 0;
+        if (i < L.N) {
+          if (j - i >= 0) {
+            v = uint32_t(nt[j - i]);                 // a new id of this step
+          } else {
+            const int64_t q = committed + (j - i);   // committed position, from the cache
+            if (q >= 0) v = uint32_t(ring[int64_t(b) * nm1 + q % nm1]);
+          }
+        }
+        c[i] = v;
+      }
+      hash_position<NMAX>(L, c, out);
+    }
   }
-  hash_position<NMAX>(L, c, out);
+  if (n_commit == nullptr) return;
+  __syncthreads();
+  if (!active || j != 0) return;
+  // commit the first n_commit[b] (<= n_new[b]) new ids
+  int a = n_commit[b];
+  if (a < 0 || a > nn) {
+    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
+    a = a < 0 ? 0 : nn;
+  }
+  if (nm1 > 0) {
+    int32_t* rb = ring + int64_t(b) * nm1;
+    const int32_t* nt = newtok + int64_t(b) * tmax;
+    for (int q = (a > nm1 ? a - nm1 : 0); q < a; ++q) rb[(committed + q) % nm1] = nt[q];
+  }
+  len[b] = committed + a;
 }
 
 __global__ __launch_bounds__(kThreads) void cache_init_kernel(
@@ -160,14 +200,14 @@ hipError_t hash_prefill_n(const LayerDesc& L, const int32_t* tokens, const int32
 }
 
 template <int NMAX>
-hipError_t hash_decode_n(const LayerDesc& L, const int32_t* ring, const int64_t* len,
-                         const int32_t* newtok, const int32_t* n_new, int32_t nseq,
-                         int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
+hipError_t hash_decode_n(const LayerDesc& L, int32_t* ring, int64_t* len,
+                         const int32_t* newtok, const int32_t* n_new, const int32_t* n_commit,
+                         int32_t nseq, int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
                          hipStream_t st) {
-  const int64_t rows = int64_t(nseq) * tmax;
-  const unsigned blocks = unsigned((rows + kThreads - 1) / kThreads);
+  const int spb = kThreads / tmax;
+  const unsigned blocks = unsigned((nseq + spb - 1) / spb);
   hipLaunchKernelGGL(hash_decode_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, L, ring,
-                     len, newtok, n_new, nseq, tmax, tok, idx, flags);
+                     len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags);
   return hipGetLastError();
 }
 
@@ -183,18 +223,21 @@ hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const 
   return hash_prefill_n<NGRAM_MAX_ORDER>(L, tokens, cu, nseq, ntok, idx, flags, st);
 }
 
-hipError_t launch_hash_decode(const LayerDesc& L, const int32_t* ring, const int64_t* len,
-                              const int32_t* newtok, const int32_t* n_new, int32_t nseq,
-                              int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
-                              hipStream_t st) {
+hipError_t launch_hash_decode(const LayerDesc& L, int32_t* ring, int64_t* len,
+                              const int32_t* newtok, const int32_t* n_new,
+                              const int32_t* n_commit, int32_t nseq, int32_t tmax, int32_t* tok,
+                              int32_t* idx, int32_t* flags, hipStream_t st) {
   if (L.N <= 2)
-    return hash_decode_n<2>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx, flags, st);
+    return hash_decode_n<2>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags,
+                            st);
   if (L.N <= 4)
-    return hash_decode_n<4>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx, flags, st);
+    return hash_decode_n<4>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags,
+                            st);
   if (L.N <= 8)
-    return hash_decode_n<8>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx, flags, st);
-  return hash_decode_n<NGRAM_MAX_ORDER>(L, ring, len, newtok, n_new, nseq, tmax, tok, idx,
-                                        flags, st);
+    return hash_decode_n<8>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags,
+                            st);
+  return hash_decode_n<NGRAM_MAX_ORDER>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok,
+                                        idx, flags, st);
 }
 
 hipError_t launch_cache_init(const LayerDesc& L, int32_t* ring, int64_t* len,

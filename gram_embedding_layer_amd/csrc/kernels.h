@@ -12,11 +12,12 @@ hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const 
                                int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
                                hipStream_t st);
 
-// kernel 4 (front half): context from the N-gram cache + new ids -> tok, idx
-hipError_t launch_hash_decode(const LayerDesc& L, const int32_t* ring, const int64_t* len,
-                              const int32_t* newtok, const int32_t* n_new, int32_t nseq,
-                              int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
-                              hipStream_t st);
+// kernel 4 (front half): context from the N-gram cache + new ids -> tok, idx; then, if
+// n_commit is not null, the step's commit into the cache
+hipError_t launch_hash_decode(const LayerDesc& L, int32_t* ring, int64_t* len,
+                              const int32_t* newtok, const int32_t* n_new,
+                              const int32_t* n_commit, int32_t nseq, int32_t tmax, int32_t* tok,
+                              int32_t* idx, int32_t* flags, hipStream_t st);
 
 // kernel 4 (cache upkeep)
 hipError_t launch_cache_init(const LayerDesc& L, int32_t* ring, int64_t* len,

@@ -19,6 +19,7 @@ struct LayerDesc {
   int32_t esz;     // bytes per element
   int32_t V0;      // base vocabulary
   uint32_t V[NGRAM_MAX_SUBTABLES];  // V_{n,k} in sub-table order
+  uint64_t Vinv[NGRAM_MAX_SUBTABLES];  // floor((2^64 - 1) / V_{n,k}): Barrett multiplier
 };
 
 // Checks the config (section A2 shapes, the 64-bit Horner bound) and fills `out`.

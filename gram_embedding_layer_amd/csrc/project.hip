@@ -9,14 +9,20 @@
 // the only dense work on the path. Both operands are contiguous along the contraction
 // axis, which is the layout the matrix cores want.
 //
-// bf16 path (D % 256 == 0, d % 64 == 0): tiles of BM rows x 256 outputs x 64-deep slices.
-// A 64-deep slice never straddles two sub-tables, so the A-loader reads, for each of the
-// BM rows, one 128-byte piece of one sub-table row straight from HBM (no gathered copy of
-// the batch is ever written). Slices are staged through registers into a double-buffered,
-// XOR-swizzled LDS tile and fed to v_mfma_f32_32x32x16_bf16 (fp32 accumulation). The
-// epilogue adds the E_0 row, scales by 1/(S+1) in fp32 and rounds once to bf16.
-// Blocks are numbered so that the 32 blocks resident on one XCD at a time cover 8 row
-// tiles x 4 output tiles, which keeps their A rows and W panels in that XCD's L2.
+// bf16 path (D % 256 == 0, d % 64 == 0): tiles of BM rows x 256 outputs, 64-deep slices.
+// A 64-deep slice never straddles two sub-tables, so for each of the BM rows the A-loader
+// reads one 128-byte piece (a full L2 line) of one sub-table row straight from HBM into
+// LDS (global_load_lds_dwordx4; no gathered copy of the batch is ever written). W slices
+// travel the same way. Slices sit in XOR-swizzled LDS buffers (2 for 256-row tiles, 3 for
+// shorter ones); the loads of the next slice fly while 8 waves (2 per SIMD) multiply the
+// current one with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Waits and barriers are
+// explicit, so loads stay in flight across them. The epilogue adds the E_0 row, scales by
+// 1/(S+1) in fp32 and rounds once to bf16.
+// Measured on MI355X (64K rows, D = 3072): the loads, not the matrix cores, bound this
+// kernel; each CU keeps about 48 L2 lines in flight, so its load rate is set by L2 hit
+// latency, and the tile order below is chosen for L2 reuse.
+// Blocks are numbered so that the 32 blocks resident on one XCD at a time cover 4 row
+// tiles x 8 output tiles, which keeps their A rows and W panels in that XCD's L2.
 #include "kernels.h"
 
 namespace ngram {
@@ -108,13 +114,15 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   __shared__ int32_t sidx[kIdxBytes / 4];
 
   // -- XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous range
-  //    of virtual tiles and walk a range 8 row tiles at a time, outputs slowest.
+  //    of virtual tiles and walk a range GM row tiles at a time, outputs slowest, so the
+  //    32 blocks resident on an XCD share 4 tiles of gathered rows and 8 panels of W in
+  //    its L2 (the best of the 2..32 row-tile groups measured).
   const int nb = a.tiles_m * a.tiles_n;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int per = nb >> 3, rem = nb & 7;
   const int v = xcd * per + (xcd < rem ? xcd : rem) + local;
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int group = v / (GM * a.tiles_n);
   const int first_m = group * GM;
   const int gm = min(GM, a.tiles_m - first_m);
@@ -212,10 +220,10 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     // load of slice kt+NST-1 reuses.
     if (NST == 3 && kt + 1 < KT) wait_loads_and_meet<PER_SLICE>();
     else wait_loads_and_meet<0>();
+    if (kt + NST - 1 < KT) issue(kt + NST - 1);
     const char* sp = lds + (kt % NST) * STAGE;
     frags(sp, 0, 0);
     frags(sp, 1, 1);
-    if (kt + NST - 1 < KT) issue(kt + NST - 1);
     mma(0);
     frags(sp, 2, 0);
     mma(1);

@@ -31,6 +31,7 @@ int describe(const ngram_embed_config* cfg, LayerDesc* out) {
       const int64_t v = cfg->V[s];
       if (v < 1 || v >= (int64_t(1) << 31)) return NGRAM_EINVAL;
       L.V[s] = uint32_t(v);
+      L.Vinv[s] = ~uint64_t(0) / uint64_t(v);
       if (uint64_t(v) > vmax) vmax = uint64_t(v);
     }
     // Horner step x*V0 + t with x < V, t < V0 stays below V*V0 <= 2^63 - 1.

@@ -83,6 +83,23 @@ def test_hash_bit_exact_ragged(lib, N, K, V0):
     assert int(flags.item()) == 0
 
 
+def test_hash_extreme_moduli(lib):
+    """Largest accepted V0 and V_{n,k}, V = 1, and ids at V0 - 1: exact residues."""
+    V0 = 2 ** 31 - 1
+    N, K = 4, 2
+    V = [1, 2, 3, 2 ** 31 - 1, 2 ** 31 - 2, 65536]
+    rng = np.random.default_rng(77)
+    seqs = [np.full(9, V0 - 1, np.int32), rng.integers(V0 - 1000, V0, size=300).astype(np.int32),
+            rng.integers(0, V0, size=500).astype(np.int32), np.zeros(5, np.int32)]
+    tokens, cu = packed(seqs)
+    cfg = g.Config(N, K, 16 * len(V), "f32", V0, V)
+    idx = torch.full((len(tokens), len(V)), -7, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.ngram_embed_hash(cfg, dev(tokens), dev(cu), idx, flags)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.hash_indices(V0, N, K, V, tokens, cu))
+    assert int(flags.item()) == 0
+
+
 @pytest.mark.parametrize("w", [small_workload("f32", D=64), small_workload("bf16", D=256),
                                small_workload("bf16", D=192, N=4, K=1)], ids=lambda w: w.name)
 def test_gather_bytes_exact(lib, w):
