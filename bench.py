@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 WORKLOAD = "prefill_64k_30b"
 DECODE_WORKLOAD = "decode_spec5_30b"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_project_prefill_64k_30b.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_64k_30b.txt")
 
 
 def log(msg):
@@ -44,80 +44,103 @@ def source_digest(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def counter_traffic(per_launch_rows):
-    """HBM bytes per launch of the projection from the committed rocprofv3 counter summary,
+def counter_traffic(kernel, source):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy of known size),
     or None when it is missing or was taken on a different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
     for ln in open(TRAFFIC_FILE):
-        if ":" in ln and not ln.startswith("#"):
+        if ":" in ln and not ln.lstrip().startswith(("#", "|", "-")):
             k, v = ln.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("project.hip sha256[:16]") != source_digest("project.hip"):
+    if kv.get(f"{source} sha256[:16]") != source_digest(source):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[f"{kernel} hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
 
-def cpu_baseline(w, E0, E, W, tokens2d, nseq_sample):
-    """The oracle as it stands, on the first `nseq_sample` sequences of the batch. Table rows
-    the oracle asks for are copied from HBM beforehand (not timed)."""
+def cpu_baseline(w, E0, E, W, batches):
+    """The oracle as it stands, on whole benchmark batches (each 8 x 8192 tokens). Table
+    rows the oracle asks for are copied from HBM first (not timed)."""
     import numpy as np
     import torch
 
     import oracle
     from threadpoolctl import threadpool_info
 
-    seqs = tokens2d[:nseq_sample]
-    tokens = seqs.reshape(-1)
-    cu = np.arange(nseq_sample + 1, dtype=np.int64) * seqs.shape[1]
-    t0 = time.perf_counter()
-    idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
-    t_hash = time.perf_counter() - t0
-    # copy the named rows to host (excluded from the timing)
-    c0 = time.perf_counter()
-    rows = {-1: E0.index_select(0, torch.as_tensor(tokens.astype(np.int64), device="cuda"))
-            .float().cpu().numpy().astype(np.float64)}
-    for s in range(w.S):
-        r = torch.as_tensor(idx[:, s], device="cuda")
-        rows[s] = E[s].index_select(0, r).float().cpu().numpy().astype(np.float64)
     Wh = W.float().cpu().numpy().astype(np.float64)
     Wb = [Wh[:, s * w.d:(s + 1) * w.d] for s in range(w.S)]
-    t_copy = time.perf_counter() - c0
+    t_hash = t_embed = t_copy = 0.0
+    n = 0
+    for tokens2d in batches:
+        tokens = tokens2d.reshape(-1)
+        cu = np.arange(tokens2d.shape[0] + 1, dtype=np.int64) * tokens2d.shape[1]
+        t0 = time.perf_counter()
+        idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
+        t_hash += time.perf_counter() - t0
+        c0 = time.perf_counter()
+        rows = {-1: E0.index_select(0, torch.as_tensor(tokens.astype(np.int64), device="cuda"))
+                .float().cpu().numpy().astype(np.float64)}
+        for s in range(w.S):
+            r = torch.as_tensor(idx[:, s], device="cuda")
+            rows[s] = E[s].index_select(0, r).float().cpu().numpy().astype(np.float64)
+        t_copy += time.perf_counter() - c0
 
-    def fetch(s, r):
-        return rows[s]          # rows already in the oracle's order
-    t1 = time.perf_counter()
-    oracle.embed_from_indices(w.D, w.N, w.K, tokens, idx, fetch, Wb)
-    t_embed = time.perf_counter() - t1
+        def fetch(s, r, rows=rows):
+            return rows[s]          # rows already in the oracle's order
+        t1 = time.perf_counter()
+        oracle.embed_from_indices(w.D, w.N, w.K, tokens, idx, fetch, Wb)
+        t_embed += time.perf_counter() - t1
+        n += len(tokens)
+        del rows
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
                         if p.get("user_api") == "blas"] or [1])
-    n = len(tokens)
     return {
-        "value": n / (t_hash + t_embed),
+        "value": round(n / (t_hash + t_embed), 1),
         "unit": "tokens/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"{nseq_sample} of {tokens2d.shape[0]} sequences ({n} tokens) of the "
-                   f"benchmark batch; python-int hash {t_hash:.2f} s (1 thread) + float64 "
-                   f"contraction {t_embed:.2f} s ({blas_threads} BLAS threads); "
-                   f"host copy of the named rows {t_copy:.2f} s not timed"),
+        "sample": (f"{len(batches)} benchmark batches of 8 x 8192 tokens ({n} tokens); "
+                   f"python-int hash {t_hash:.2f} s on 1 thread + float64 contraction "
+                   f"{t_embed:.2f} s on {blas_threads} BLAS threads; host copy of the named "
+                   f"table rows {t_copy:.2f} s not timed"),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def profile_launches(g, cfg, tables, toks, cu, idx, out, stream):
+    """A few launches of each kernel plus a plain device copy of known size, for rocprofv3
+    counter passes (the copy calibrates FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    T, D = out.shape
+    G = torch.empty_like(out)
+    src = torch.empty_like(out).fill_(1.0)
+    for k in range(3):
+        g.ngram_embed_hash(cfg, toks[k % len(toks)], cu, idx, None, stream=stream)
+        g.ngram_embed_project(cfg, tables, idx, toks[k % len(toks)], out, stream=stream)
+        g.ngram_embed_gather(cfg, tables, idx, G, stream=stream)
+        G.copy_(src)               # plain copy: T*D*2 bytes read, the same written
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": "launched hash, project, gather and a copy of "
+                      f"{T * D * 2} bytes, 3 times each"}), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    ap.add_argument("--cpu-batches", type=int, default=4,
+                    help="benchmark batches of 64K tokens the CPU oracle is timed on")
+    ap.add_argument("--profile", action="store_true",
+                    help="only launch each kernel a few times (for rocprofv3 counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer's data-parallel path needs no second GPU "
@@ -148,6 +171,9 @@ def main():
     idx_ws = ws[idx_off:].view(torch.int32)
     idx_rot = [torch.empty((T, w.S), dtype=torch.int32, device=dev) for _ in range(nrot)]
     stream = torch.cuda.current_stream(dev)
+    if args.profile:
+        profile_launches(g, cfg, tables, toks, cu, idx_rot[0], out, stream)
+        return
 
     def step(k, ev=None):
         r = k % nrot
@@ -183,7 +209,7 @@ def main():
     flops = 2.0 * T * w.D * w.D
     alg_bytes_proj = T * (w.S * w.d * esz + w.D * esz + w.D * esz + w.S * 4 + 4) + w.D * w.D * esz
     tflops = flops / t_proj / 1e12
-    traffic = counter_traffic(T)
+    traffic = counter_traffic("project", "project.hip")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "proj_mfma_kernel<256>",
@@ -211,7 +237,8 @@ def main():
               "read_GBps": round(read_b / t_g / 1e9, 1),
               "read_write_GBps": round(2 * read_b / t_g / 1e9, 1),
               "frac_of_hbm_peak": round(2 * read_b / t_g / 1e9 / HBM_PEAK_GBS, 4),
-              "bytes_read": read_b, "bytes_written": read_b}
+              "bytes_read": read_b, "bytes_written": read_b,
+              "traffic": counter_traffic("gather", "gather.hip")}
     log(f"gather {t_g*1e6:.1f} us: {2*read_b/t_g/1e9:.0f} GB/s read+write")
     del G
 
@@ -221,8 +248,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_seqs} sequences")
-        cpu = cpu_baseline(w, E0, E, W, tok_host[0], args.cpu_sample_seqs)
+        log(f"cpu baseline: oracle on {args.cpu_batches} batches")
+        cpu = cpu_baseline(w, E0, E, W, tok_host[:max(1, min(args.cpu_batches, nrot))])
         log(f"cpu baseline {cpu['value']:.0f} tokens/s")
 
     step_bytes = alg_bytes_proj + T * 4 * (1 + w.S)   # + hash: ids in, indices out
