@@ -158,7 +158,10 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   const int kps = a.d / kBK;     // slices per sub-table
   int s_cur = -1;
 
-  auto issue = [&](int kt) __attribute__((always_inline)) {
+  // The slice being fetched: its LDS stage, its offset within the current sub-table.
+  uint32_t f_sb = 0;
+  int f_koff = 0, f_kt = 0;
+  auto prep = [&](int kt) __attribute__((always_inline)) {
     if (kt == (s_cur + 1) * kps) {          // first slice of the next sub-table
       ++s_cur;
 #pragma unroll
@@ -168,13 +171,22 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
         ap[q] = E[s_cur] + int64_t(id) * a.d + pchunk * 8;
       }
     }
-    const uint32_t sb = lds0 + uint32_t(kt % NST) * STAGE;
-    const int koff = (kt - s_cur * kps) * kBK;
+    f_sb = lds0 + uint32_t(kt % NST) * STAGE;
+    f_koff = (kt - s_cur * kps) * kBK;
+    f_kt = kt;
+  };
+  // load q of this wave's PER_SLICE loads of the slice (A rows first, then W rows)
+  auto dma = [&](int q) __attribute__((always_inline)) {
+    if (q < QA)
+      dma16(ap[q] + f_koff, f_sb + w * (BM * 16) + q * 1024);
+    else
+      dma16(bp + int64_t((q - QA) * 8) * a.D + f_kt * kBK,
+            f_sb + A_BYTES + w * 4096 + (q - QA) * 1024);
+  };
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    prep(kt);
 #pragma unroll
-    for (int q = 0; q < QA; ++q) dma16(ap[q] + koff, sb + w * (BM * 16) + q * 1024);
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-      dma16(bp + int64_t(q * 8) * a.D + kt * kBK, sb + A_BYTES + w * 4096 + q * 1024);
+    for (int q = 0; q < PER_SLICE; ++q) dma(q);
   };
 
   f32x16_t acc[TJ][TI];
@@ -202,15 +214,27 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     for (int i = 0; i < TI; ++i)
       xf[buf][i] = *reinterpret_cast<const bf16x8_t*>(sp + arow0 + i * 32 * 128 + pcs[kk]);
   };
-  // W block as the first operand: each lane's results are 4 consecutive outputs of one
-  // row, which makes the epilogue's E_0 reads and stores 8 bytes wide.
-  auto mma = [&](int buf) __attribute__((always_inline)) {
+  // One 16-deep k-step: TI x TJ matrix-core ops. W block as the first operand: each lane's
+  // results are 4 consecutive outputs of one row, which makes the epilogue's E_0 reads and
+  // stores 8 bytes wide. The next slice's loads are spread between the ops (DPP per k-step):
+  // issued all at once after the barrier, the 8 waves' loads overflow the address unit's
+  // queue and hold every wave at issue, away from its matrix-core work.
+  constexpr int NM = TI * TJ;
+  constexpr int DPP = (PER_SLICE + 3) / 4;
+  constexpr int EVERY = NM / DPP > 0 ? NM / DPP : 1;
+  auto mma = [&](int buf, bool loads, int part) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], xf[buf][i], acc[j][i],
-                                                            0, 0, 0);
+    for (int x = 0; x < NM; ++x) {
+      const int j = x / TI, i = x % TI;
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], xf[buf][i], acc[j][i],
+                                                          0, 0, 0);
+      const int q = part * DPP + (x + 1) / EVERY - 1;
+      if (loads && (x + 1) % EVERY == 0 && (x + 1) / EVERY <= DPP && q < PER_SLICE) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma(q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   for (int p = 0; p < NST - 1 && p < KT; ++p) issue(p);
@@ -220,16 +244,17 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     // load of slice kt+NST-1 reuses.
     if (NST == 3 && kt + 1 < KT) wait_loads_and_meet<PER_SLICE>();
     else wait_loads_and_meet<0>();
-    if (kt + NST - 1 < KT) issue(kt + NST - 1);
+    const bool loads = kt + NST - 1 < KT;
+    if (loads) prep(kt + NST - 1);
     const char* sp = lds + (kt % NST) * STAGE;
     frags(sp, 0, 0);
     frags(sp, 1, 1);
-    mma(0);
+    mma(0, loads, 0);
     frags(sp, 2, 0);
-    mma(1);
+    mma(1, loads, 1);
     frags(sp, 3, 1);
-    mma(0);
-    mma(1);
+    mma(0, loads, 2);
+    mma(1, loads, 3);
   }
 
   // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*WN + 32j + 8g + 4fk + q of
