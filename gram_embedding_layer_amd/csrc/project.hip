@@ -32,6 +32,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte vector
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -110,8 +111,13 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   constexpr int QA = BM / 64;            // A loads per wave per slice (8 rows each)
   constexpr int QB = kBN / 64;           // W loads per wave per slice
   constexpr int PER_SLICE = QA + QB;
-  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
-  __shared__ int32_t sidx[kIdxBytes / 4];
+  // One LDS pool: NST slice stages + the tile's hash indices during the main loop; the
+  // epilogue then reuses it to turn each wave's results into row-major order.
+  constexpr int EP_PITCH = WN * 4 + 32;  // bytes per staged fp32 row (conflict-free pitch)
+  constexpr int POOL = NST * STAGE + kIdxBytes;
+  static_assert(8 * 32 * EP_PITCH <= POOL, "epilogue staging must fit the LDS pool");
+  __shared__ __attribute__((aligned(1024))) char lds[POOL];
+  int32_t* sidx = reinterpret_cast<int32_t*>(lds + NST * STAGE);
 
   // -- XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous range
   //    of virtual tiles and walk a range GM row tiles at a time, outputs slowest, so the
@@ -257,35 +263,67 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     mma(1, loads, 3);
   }
 
-  // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*WN + 32j + 8g + 4fk + q of
-  //    row m = m0 + wm*WM + 32i + fr.
+  // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*WN + 32j + 8g + 4fk + q of row
+  //    m = m0 + wm*WM + 32i + fr. Each wave stages 32 rows at a time (fp32) in its own
+  //    part of the LDS pool, then reads them back row-major: WN/4 lanes per row, 4
+  //    consecutive outputs per lane, so E_0 is read and the output written in whole
+  //    lines. E_0 add and the 1/(S+1) scale in fp32, one rounding to bf16.
+  __syncthreads();                      // every wave is done with the slice buffers
   const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0);
   uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out);
+  char* ep = lds + w * (32 * EP_PITCH);
+  constexpr int LPR = WN / 4;           // lanes per output row
+  constexpr int RPI = 64 / LPR;         // rows per wave instruction
+  const int er = lane / LPR, ec = lane % LPR;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    const int64_t m = m0 + wm * WM + i * 32 + fr;
-    if (m >= a.nrows) continue;
-    const int32_t tk = a.tok[m];
-    const bool ok = uint32_t(tk) < uint32_t(a.V0);
-    const uint16_t* e0 = E0 + int64_t(ok ? tk : 0) * a.D;
-    uint16_t* o = out + m * a.D;
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + j * 32 + g * 8 + fk * 4;
+        f32x4_t v = {acc[j][i][4 * g + 0], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
+                     acc[j][i][4 * g + 3]};
+        *reinterpret_cast<f32x4_t*>(ep + fr * EP_PITCH + (j * 32 + g * 8 + fk * 4) * 4) = v;
+      }
+    // the wave reads back what its own lanes wrote: wait for the writes, keep the order
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // all loads of the 32 rows first (tok, then E_0), then the stores: a load placed after
+    // a store would wait for it, since the compiler cannot rule out aliasing
+    constexpr int NIT = 32 / RPI;
+    const int64_t mrow = m0 + wm * WM + i * 32 + er;
+    const int n = n0 + wn * WN + ec * 4;
+    int32_t tk[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int64_t m = mrow + it * RPI;
+      tk[it] = m < a.nrows ? a.tok[m] : -1;
+    }
+    u32x2_t ev[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      ev[it] = u32x2_t{0u, 0u};
+      if (uint32_t(tk[it]) < uint32_t(a.V0))
+        ev[it] = *reinterpret_cast<const u32x2_t*>(E0 + int64_t(tk[it]) * a.D + n);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int64_t m = mrow + it * RPI;
+      const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
+                                                           ec * 16);
+      if (m < a.nrows) {
         u32x2_t res = {0u, 0u};
-        if (ok) {
-          const u32x2_t ev = *reinterpret_cast<const u32x2_t*>(e0 + n);
-          const float y0 = (acc[j][i][4 * g + 0] + bf16_to_f32(ev.x & 0xffffu)) * a.inv;
-          const float y1 = (acc[j][i][4 * g + 1] + bf16_to_f32(ev.x >> 16)) * a.inv;
-          const float y2 = (acc[j][i][4 * g + 2] + bf16_to_f32(ev.y & 0xffffu)) * a.inv;
-          const float y3 = (acc[j][i][4 * g + 3] + bf16_to_f32(ev.y >> 16)) * a.inv;
+        if (uint32_t(tk[it]) < uint32_t(a.V0)) {
+          const float y0 = (y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv;
+          const float y1 = (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv;
+          const float y2 = (y[2] + bf16_to_f32(ev[it].y & 0xffffu)) * a.inv;
+          const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
           res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
           res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
         }
-        *reinterpret_cast<u32x2_t*>(o + n) = res;
+        __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + m * a.D + n));
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next writes
   }
 }
 
