@@ -24,6 +24,10 @@ Readings where the pages are silent:
   * N = 1 has no sub-tables: e_i = E_0(t_i);
   * token ids must lie in [0, V0) (the hash reads them as base-V0 digits).
 
+Embedding amplification (section 3.2.4 of the same page, outside the final form itself):
+amplify() applies the output scale or the layer normalisation the pages describe; the
+reading of the latter is stated there.
+
 Arithmetic: hashes are exact Python integers (the n-gram value is formed as a sum of powers,
 not by Horner's rule, and reduced once); embeddings are computed in float64.
 Parity pins: tests/test_oracle_pins.py. Nothing here is "parity unpinned".
@@ -179,6 +183,41 @@ class DecodeOracle:
             if a < 0 or a > len(toks):
                 raise ValueError("n_accept outside [0, n_new]")
             self.hist[b].extend(int(t) for t in toks[:a])
+
+
+AMP_MODES = ("none", "scale", "layernorm")
+
+
+def amplify(e: np.ndarray, mode: str = "none", scale: float = 1.0, eps: float = 1e-5,
+            weight=None, bias=None) -> np.ndarray:
+    """Embedding amplification of section 3.2.4 of the deep-notes page ("effective training
+    through embedding amplification"), applied to the layer output e [T, D] before it joins
+    the residual stream. Two strategies are described there:
+      * "scale": multiply the output by a factor (sqrt(D) in the pages);
+      * "layernorm": layer normalisation over the hidden dimension D. The pages give no
+        formula; the reading here is the usual one: per row, mean m and biased variance v of
+        the D values, (e - m) / sqrt(v + eps), then the optional elementwise affine
+        weight * x + bias (weight 1 and bias 0 when absent).
+    float64 throughout."""
+    e = np.asarray(e, dtype=np.float64)
+    if mode == "none":
+        return e.copy()
+    if mode == "scale":
+        return e * float(scale)
+    if mode == "layernorm":
+        if not eps > 0:
+            raise ValueError("layernorm needs eps > 0")
+        D = e.shape[-1]
+        m = e.sum(axis=-1, keepdims=True) / D
+        c = e - m
+        v = (c * c).sum(axis=-1, keepdims=True) / D
+        y = c / np.sqrt(v + float(eps))
+        if weight is not None:
+            y = y * np.asarray(weight, dtype=np.float64)
+        if bias is not None:
+            y = y + np.asarray(bias, dtype=np.float64)
+        return y
+    raise ValueError(f"amplification mode must be one of {AMP_MODES}")
 
 
 def param_count(V0: int, D: int, N: int, K: int, V: Sequence[int]) -> dict:

@@ -354,3 +354,77 @@ def test_pins_catch_planted_mistakes(monkeypatch, mistake):
         assert _fails(check_hash_golden) or _fails(check_hash_decimal)
     else:
         assert _fails(check_embed_golden)
+
+
+# ------------------------------------------------------------------ embedding amplification
+# Section 3.2.4 of the deep-notes page: the output scaled (by sqrt(D)) or layer-normalised
+# before it joins the residual stream. The layer normalisation is pinned to closed forms
+# worked by hand, to its defining invariants and to torch's own layer_norm.
+
+def check_layernorm_closed_form():
+    e = np.array([[1.0, 2.0, 3.0, 4.0]])
+    r5 = np.sqrt(5.0)
+    # mean 5/2 and biased variance 5/4, so (e - 5/2) / sqrt(5/4) = (2e - 5) / sqrt(5)
+    np.testing.assert_allclose(O.amplify(e, "layernorm", eps=1e-300),
+                               [[-3 / r5, -1 / r5, 1 / r5, 3 / r5]], rtol=1e-12)
+    # eps = 3/4 makes the denominator sqrt(5/4 + 3/4) = sqrt(2)
+    np.testing.assert_allclose(O.amplify(e, "layernorm", eps=0.75),
+                               [[-1.5 / np.sqrt(2), -0.5 / np.sqrt(2), 0.5 / np.sqrt(2),
+                                 1.5 / np.sqrt(2)]], rtol=1e-12)
+    # elementwise affine: weight * x + bias
+    w, b = np.array([2.0, 0.0, -1.0, 1.0]), np.array([0.0, 1.0, 0.0, -3.0])
+    np.testing.assert_allclose(O.amplify(e, "layernorm", eps=0.75, weight=w, bias=b),
+                               [[-3 / np.sqrt(2), 1.0, -0.5 / np.sqrt(2), 1.5 / np.sqrt(2) - 3]],
+                               rtol=1e-12)
+    # a constant row has zero variance: the output is the bias alone
+    np.testing.assert_allclose(O.amplify(np.full((1, 4), 7.0), "layernorm", eps=1e-5, bias=b),
+                               [b], rtol=0, atol=1e-12)
+
+
+def test_layernorm_closed_form():
+    check_layernorm_closed_form()
+
+
+def test_layernorm_invariants_and_library():
+    import torch
+    rng = np.random.default_rng(11)
+    e = rng.normal(0.3, 0.02, size=(9, 96))
+    y = O.amplify(e, "layernorm", eps=1e-300)
+    np.testing.assert_allclose(y.mean(axis=1), 0, atol=1e-12)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1, rtol=1e-10)
+    # shift and positive scale invariance of the normalised rows
+    np.testing.assert_allclose(O.amplify(5 * e - 2, "layernorm", eps=1e-300), y, atol=1e-10)
+    w, b = rng.normal(size=96), rng.normal(size=96)
+    want = torch.nn.functional.layer_norm(torch.tensor(e), (96,), torch.tensor(w),
+                                          torch.tensor(b), eps=1e-5).numpy()
+    np.testing.assert_allclose(O.amplify(e, "layernorm", eps=1e-5, weight=w, bias=b), want,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_scale_amplification():
+    rng = np.random.default_rng(12)
+    e = rng.normal(size=(5, 16))
+    np.testing.assert_array_equal(O.amplify(e, "scale", 4.0), 4.0 * e)
+    np.testing.assert_array_equal(O.amplify(e, "scale", 1.0), e)
+    np.testing.assert_array_equal(O.amplify(e, "none"), e)
+    with pytest.raises(ValueError):
+        O.amplify(e, "rms")
+
+
+@pytest.mark.parametrize("mistake", ["unbiased_var", "eps_outside_sqrt", "no_center",
+                                     "affine_swapped"])
+def test_layernorm_pins_catch_planted_mistakes(monkeypatch, mistake):
+    def planted(e, mode="none", scale=1.0, eps=1e-5, weight=None, bias=None):
+        e = np.asarray(e, dtype=np.float64)
+        D = e.shape[-1]
+        m = e.mean(axis=-1, keepdims=True)
+        c = e - m
+        if mistake == "no_center":
+            c = e
+        v = (c * c).sum(axis=-1, keepdims=True) / (D - 1 if mistake == "unbiased_var" else D)
+        y = c / (np.sqrt(v) + eps) if mistake == "eps_outside_sqrt" else c / np.sqrt(v + eps)
+        w = np.ones(D) if weight is None else np.asarray(weight, dtype=np.float64)
+        b = np.zeros(D) if bias is None else np.asarray(bias, dtype=np.float64)
+        return y * b + w if mistake == "affine_swapped" else y * w + b
+    monkeypatch.setattr(O, "amplify", planted)
+    assert _fails(check_layernorm_closed_form)
