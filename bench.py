@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-amp", action="store_true",
+                    help="skip the amplified (scale / layer-norm) prefill timings")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-batches", type=int, default=4,
                     help="benchmark batches of 64K tokens the CPU oracle is timed on")
@@ -212,7 +214,7 @@ def main():
     traffic = counter_traffic("project", "project.hip")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "proj_mfma_kernel<256>",
+                "traffic": traffic, "kernel": "proj_mfma_kernel<256, false>",
                 "kernel_us": round(t_proj * 1e6, 1),
                 "algorithmic_hbm_GBps": round(alg_bytes_proj / t_proj / 1e9, 1)}
     log(f"step {ms_per_step:.3f} ms: hash {t_hash*1e6:.1f} us, project {t_proj*1e6:.1f} us "
@@ -242,6 +244,10 @@ def main():
     log(f"gather {t_g*1e6:.1f} us: {2*read_b/t_g/1e9:.0f} GB/s read+write")
     del G
 
+    amp = None
+    if not args.no_amp:
+        amp = bench_amplification(g, w, tables, toks, cu, dev, stream, args.steps)
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(g, WL, cfg, tables, dev, stream, args.decode_steps)
@@ -266,10 +272,61 @@ def main():
         "kernels_us": {"hash": round(t_hash * 1e6, 1), "project": round(t_proj * 1e6, 1)},
         "roofline": roofline,
         "gather": gather,
+        "amplification": amp,
         "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_amplification(g, w, tables, toks, cu, dev, stream, steps):
+    """The prefill entry point on the same batches, plain and with each embedding
+    amplification (output factor sqrt(D); layer normalisation with seeded bf16 weight and
+    bias), HIP events around each call. The layer normalisation adds an fp32 row write in the
+    projection's epilogue and a second, HBM-bound pass (the trace shows its own duration)."""
+    import numpy as np
+    import torch
+
+    T = int(toks[0].shape[0])
+    out = torch.empty((T, w.D), dtype=torch.bfloat16, device=dev)
+    rng = np.random.default_rng(7)
+    lw = torch.as_tensor(rng.normal(1.0, 0.1, size=w.D)).to(torch.bfloat16).to(dev)
+    lb = torch.as_tensor(rng.normal(0.0, 0.1, size=w.D)).to(torch.bfloat16).to(dev)
+    res = {"workload": WORKLOAD, "entry": "ngram_embed_prefill"}
+    modes = ("none", "scale", "layernorm")
+    runs = {}
+    for mode in modes:
+        cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V), amp=mode)
+        runs[mode] = (cfg, g.Tables(tables.E0, tables.E, tables.W, lw, lb),
+                      g.alloc_workspace(cfg, T, device=dev))
+    for k in range(3):
+        for mode in modes:
+            cfg, tab, ws = runs[mode]
+            g.ngram_embed_prefill(cfg, tab, toks[k % len(toks)], cu, out, ws, stream=stream)
+    # modes interleaved call by call, so clock ramps and cache state treat them alike
+    ev = {m: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] for m in modes}
+    for k in range(steps):
+        for mode in modes:
+            cfg, tab, ws = runs[mode]
+            ev[mode][k][0].record(stream)
+            g.ngram_embed_prefill(cfg, tab, toks[k % len(toks)], cu, out, ws, stream=stream)
+            ev[mode][k][1].record(stream)
+    torch.cuda.synchronize(dev)
+    for mode in modes:
+        if g.ngram_embed_read_error_flag(runs[mode][2], stream=stream) != 0:
+            raise RuntimeError(f"device error flags set in the {mode} prefill")
+        t = float(np.mean([a.elapsed_time(b) for a, b in ev[mode]])) * 1e-3
+        res[mode] = {"us_per_step": round(t * 1e6, 1), "tokens_per_s": round(T / t, 1)}
+    del runs
+    for mode in ("scale", "layernorm"):
+        res[mode]["extra_us_vs_plain"] = round(res[mode]["us_per_step"] -
+                                               res["none"]["us_per_step"], 1)
+    # the normalisation pass alone moves 4D bytes in (fp32 rows) and 2D out per token
+    res["layernorm"]["norm_pass_bytes"] = T * w.D * (4 + 2)
+    log(f"prefill: plain {res['none']['us_per_step']:.0f} us, x sqrt(D) "
+        f"{res['scale']['us_per_step']:.0f} us, layer norm {res['layernorm']['us_per_step']:.0f} us")
+    return res
 
 
 def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):

@@ -6,7 +6,8 @@ fallback: if the library is missing, load() raises.
 
 The layer (section A2 of the deep-notes page on "Scaling Embeddings Outperforms Scaling
 Experts in Language Models"): e_i = (E_0(t_i) + sum_{n,k} W_{n,k} E_{n,k}(H_{n,k})) / ((N-1)K+1)
-with H_{n,k} the polynomial rolling hash modulo V_{n,k}.
+with H_{n,k} the polynomial rolling hash modulo V_{n,k}; optionally amplified (section 3.2.4:
+an output factor such as sqrt(D), or a layer normalisation over D).
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ from typing import Optional, Sequence
 
 __all__ = [
     "LIB_PATH", "NgramError", "Config", "Tables", "Cache", "load",
-    "NGRAM_OK", "NGRAM_F32", "NGRAM_BF16",
+    "NGRAM_OK", "NGRAM_F32", "NGRAM_BF16", "AMP_MODES",
     "NGRAM_FLAG_BAD_TOKEN", "NGRAM_FLAG_BAD_SEQLENS", "NGRAM_FLAG_BAD_COUNT",
     "ngram_embed_workspace_size", "ngram_embed_workspace_layout", "ngram_embed_hash",
     "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
@@ -31,6 +32,8 @@ NGRAM_OK = 0
 NGRAM_F32, NGRAM_BF16 = 0, 1
 NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS, NGRAM_FLAG_BAD_COUNT = 1, 2, 4
 NGRAM_MAX_DECODE_TOKENS = 8
+# embedding amplification modes (NGRAM_AMP_NONE / SCALE / LAYERNORM)
+AMP_MODES = {"none": 0, "scale": 1, "layernorm": 2}
 
 
 class NgramError(RuntimeError):
@@ -42,12 +45,14 @@ class NgramError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("V0", ctypes.c_int64),
-                ("V", ctypes.POINTER(ctypes.c_int64))]
+                ("V", ctypes.POINTER(ctypes.c_int64)), ("amp", ctypes.c_int32),
+                ("amp_scale", ctypes.c_float), ("ln_eps", ctypes.c_float)]
 
 
 class _CTables(ctypes.Structure):
     _fields_ = [("E0", ctypes.c_void_p), ("E", ctypes.POINTER(ctypes.c_void_p)),
-                ("W", ctypes.c_void_p)]
+                ("W", ctypes.c_void_p), ("ln_weight", ctypes.c_void_p),
+                ("ln_bias", ctypes.c_void_p)]
 
 
 class _CCache(ctypes.Structure):
@@ -100,13 +105,17 @@ def load():
 
 @dataclass
 class Config:
-    """Mirror of ngram_embed_config: N, K, D, dtype ("f32"/"bf16" or 0/1), V0, V_{n,k}."""
+    """Mirror of ngram_embed_config: N, K, D, dtype ("f32"/"bf16" or 0/1), V0, V_{n,k}, and
+    the amplification: amp in AMP_MODES, amp_scale (None: sqrt(D)), ln_eps."""
     N: int
     K: int
     D: int
     dtype: object
     V0: int
     V: Sequence[int]
+    amp: object = "none"
+    amp_scale: Optional[float] = None
+    ln_eps: float = 1e-5
 
     @property
     def S(self) -> int:
@@ -124,24 +133,33 @@ class Config:
             return NGRAM_BF16
         return int(self.dtype) if isinstance(self.dtype, int) else -1
 
+    @property
+    def amp_code(self) -> int:
+        return AMP_MODES[self.amp] if isinstance(self.amp, str) else int(self.amp)
+
     def _c(self):
         arr = (ctypes.c_int64 * max(1, len(self.V)))(*[int(v) for v in self.V])
+        scale = float(self.D) ** 0.5 if self.amp_scale is None else float(self.amp_scale)
         c = _CConfig(int(self.N), int(self.K), int(self.D), self.dtype_code, int(self.V0),
-                     ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+                     ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), self.amp_code, scale,
+                     float(self.ln_eps))
         return c, arr
 
 
 @dataclass
 class Tables:
-    """E0 [V0, D], E = S sub-tables [V_s, d], W [D, D] stacked (device tensors)."""
+    """E0 [V0, D], E = S sub-tables [V_s, d], W [D, D] stacked; optional layer-norm weight
+    and bias [D] (device tensors)."""
     E0: object
     E: Sequence[object]
     W: object
+    ln_weight: object = None
+    ln_bias: object = None
 
     def _c(self):
         arr = (ctypes.c_void_p * max(1, len(self.E)))(*[_ptr(e) for e in self.E])
         return _CTables(_ptr(self.E0), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
-                        _ptr(self.W)), arr
+                        _ptr(self.W), _ptr(self.ln_weight), _ptr(self.ln_bias)), arr
 
 
 @dataclass

@@ -18,7 +18,28 @@ int check_tables(const LayerDesc& L, const ngram_embed_tables* T, bool need_e0_w
     for (int s = 0; s < L.S; ++s)
       if (!ngram::aligned(T->E[s], 16)) return NGRAM_EALIGN;
   }
+  // optional layer-normalisation parameters: null, or 16-byte aligned
+  if (L.amp == NGRAM_AMP_LAYERNORM &&
+      ((T->ln_weight != nullptr && !ngram::aligned(T->ln_weight, 16)) ||
+       (T->ln_bias != nullptr && !ngram::aligned(T->ln_bias, 16))))
+    return NGRAM_EALIGN;
   return NGRAM_OK;
+}
+
+// Projection of `rows` rows into `out`, then the amplification: the scale is part of the
+// projection's epilogue; the layer normalisation reads the unrounded rows from the
+// workspace.
+int project_amplified(const LayerDesc& L, const ngram_embed_tables* T, const int32_t* idx,
+                      const int32_t* tok, int64_t rows, void* out, void* ws,
+                      const ngram::WsLayout& lay, hipStream_t st) {
+  if (L.amp != NGRAM_AMP_LAYERNORM)
+    return hip_status(ngram::launch_project(L, T->E0, T->E, T->W, idx, tok, rows, out, false,
+                                            st));
+  float* pre = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.pre_off);
+  int rc = hip_status(ngram::launch_project(L, T->E0, T->E, T->W, idx, tok, rows, pre, true, st));
+  if (rc != NGRAM_OK) return rc;
+  return hip_status(ngram::launch_layernorm(L, pre, tok, T->ln_weight, T->ln_bias, rows, out,
+                                            st));
 }
 
 int check_ws(const LayerDesc& L, const void* ws, size_t ws_bytes, int64_t rows,
@@ -89,13 +110,14 @@ int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables*
   int rc = ngram::describe(cfg, &L);
   if (rc != NGRAM_OK) return rc;
   if (nrows < 0) return NGRAM_EINVAL;
+  if (L.amp == NGRAM_AMP_LAYERNORM) return NGRAM_EINVAL;   // needs a workspace
   if (nrows == 0) return NGRAM_OK;
   if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
   if ((L.S > 0 && !ngram::aligned(idx, 4)) || !ngram::aligned(tok, 4) ||
       !ngram::aligned(out, 16))
     return NGRAM_EALIGN;
   return hip_status(ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tok, nrows,
-                                          out, static_cast<hipStream_t>(stream)));
+                                          out, false, static_cast<hipStream_t>(stream)));
 }
 
 int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
@@ -118,8 +140,7 @@ int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables*
                                                ws_flags(ws), st));
     if (rc != NGRAM_OK) return rc;
   }
-  return hip_status(
-      ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tokens, ntok, out, st));
+  return project_amplified(L, tables, idx, tokens, ntok, out, ws, lay, st);
 }
 
 int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const int32_t* tokens,
@@ -166,8 +187,7 @@ int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* 
                                             n_commit, cache->nseq, tmax, tok, idx, ws_flags(ws),
                                             st));
   if (rc != NGRAM_OK) return rc;
-  return hip_status(
-      ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tok, rows, out, st));
+  return project_amplified(L, tables, idx, tok, rows, out, ws, lay, st);
 }
 
 int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,

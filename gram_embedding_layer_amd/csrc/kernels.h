@@ -33,9 +33,16 @@ hipError_t launch_clear_flags(int32_t* flags, hipStream_t st);
 hipError_t launch_gather(const LayerDesc& L, const void* const* E, const int32_t* idx,
                          int64_t nrows, void* G, hipStream_t st);
 
-// kernels 2+3: fused gather + projection + E_0 epilogue
+// kernels 2+3: fused gather + projection + E_0 epilogue (times the output factor); with
+// f32out, `out` is fp32 [nrows, D] and holds the unrounded rows
 hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
                           const void* W, const int32_t* idx, const int32_t* tok,
-                          int64_t nrows, void* out, hipStream_t st);
+                          int64_t nrows, void* out, bool f32out, hipStream_t st);
+
+// amplification by layer normalisation: pre fp32 [nrows, D] -> out [nrows, D] (config dtype);
+// weight / bias: [D] in the config dtype or null
+hipError_t launch_layernorm(const LayerDesc& L, const float* pre, const int32_t* tok,
+                            const void* weight, const void* bias, int64_t nrows, void* out,
+                            hipStream_t st);
 
 }  // namespace ngram

@@ -20,7 +20,13 @@ struct LayerDesc {
   int32_t V0;      // base vocabulary
   uint32_t V[NGRAM_MAX_SUBTABLES];  // V_{n,k} in sub-table order
   uint64_t Vinv[NGRAM_MAX_SUBTABLES];  // floor((2^64 - 1) / V_{n,k}): Barrett multiplier
+  int32_t amp;     // NGRAM_AMP_NONE / SCALE / LAYERNORM
+  float scale;     // output factor: amp_scale with NGRAM_AMP_SCALE, else 1
+  float ln_eps;    // layer-normalisation epsilon (NGRAM_AMP_LAYERNORM)
 };
+
+// Largest D the layer normalisation accepts (a row in the registers of one block).
+constexpr int32_t kMaxNormD = 8192;
 
 // Checks the config (section A2 shapes, the 64-bit Horner bound) and fills `out`.
 // Returns NGRAM_OK or a negative status.
@@ -28,7 +34,7 @@ int describe(const ngram_embed_config* cfg, LayerDesc* out);
 
 // Workspace layout for `rows` output rows; false when rows < 0.
 struct WsLayout {
-  size_t tok_off, idx_off, total;
+  size_t tok_off, idx_off, pre_off, total;  // pre_off: fp32 [rows, D] (layer norm only)
 };
 bool ws_layout(const LayerDesc& L, int64_t rows, WsLayout* out);
 

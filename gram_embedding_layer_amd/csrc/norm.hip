@@ -1,0 +1,164 @@
+// Embedding amplification by layer normalisation (section 3.2.4 of the deep-notes page on
+// "Scaling Embeddings Outperforms Scaling Experts in Language Models": a LayerNorm on the
+// layer output before it joins the residual stream; the pages give no formula, the usual
+// one is taken):
+//   out[r, :] = (e_r - mean_r) / sqrt(var_r + eps) * weight + bias
+// over the D values of row r, var the biased variance, from the unrounded fp32 rows e that
+// the projection left in the workspace. Rows whose token is outside [0, V0) (bad ids,
+// unused decode slots) are written as zeros, like the plain layer's.
+//
+// One wave per row (4 rows per 256-thread block): each lane loads its NV 16-byte vectors of
+// the row at once (consecutive lanes on consecutive vectors), the two reductions (the mean,
+// then the centred squares, so no cancellation) stay inside the wave in a fixed order, and
+// the row is written once, rounded once. NV is picked per D from a few sizes so the row sits
+// in registers. Both streams are touched once, so loads and stores are non-temporal (about
+// 2% faster on the 64K-token batch). HBM-bound: 4D bytes read and D * esz written per row.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace ngram {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Sum over the wave in a fixed order (butterfly): every lane ends with the same total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// 4 consecutive parameters (weight or bias) as fp32; `fill` when the pointer is null.
+template <typename T>
+__device__ __forceinline__ f32x4_t load4(const T* p, int c4, float fill);
+template <>
+__device__ __forceinline__ f32x4_t load4<float>(const float* p, int c4, float fill) {
+  return p ? reinterpret_cast<const f32x4_t*>(p)[c4] : f32x4_t{fill, fill, fill, fill};
+}
+template <>
+__device__ __forceinline__ f32x4_t load4<uint16_t>(const uint16_t* p, int c4, float fill) {
+  if (!p) return f32x4_t{fill, fill, fill, fill};
+  const u32x2_t h = reinterpret_cast<const u32x2_t*>(p)[c4];
+  return f32x4_t{bf16_to_f32(h.x & 0xffffu), bf16_to_f32(h.x >> 16),
+                 bf16_to_f32(h.y & 0xffffu), bf16_to_f32(h.y >> 16)};
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, int c4, f32x4_t y);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, int c4, f32x4_t y) {
+  __builtin_nontemporal_store(y, reinterpret_cast<f32x4_t*>(p) + c4);
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, int c4, f32x4_t y) {
+  u32x2_t h;
+  h.x = f32_to_bf16_rne(y.x) | (f32_to_bf16_rne(y.y) << 16);
+  h.y = f32_to_bf16_rne(y.z) | (f32_to_bf16_rne(y.w) << 16);
+  __builtin_nontemporal_store(h, reinterpret_cast<u32x2_t*>(p) + c4);
+}
+
+template <typename T, int NV>
+__global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
+    const float* __restrict__ pre, const int32_t* __restrict__ tok, int32_t V0,
+    const T* __restrict__ weight, const T* __restrict__ bias, float eps, int32_t D,
+    int64_t nrows, T* __restrict__ out) {
+  const int64_t r = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= nrows) return;                        // whole waves leave; no barrier follows
+  const int D4 = D / 4;
+  T* o = out + r * D;
+  if (uint32_t(tok[r]) >= uint32_t(V0)) {        // the whole wave takes this branch
+    for (int c4 = lane; c4 < D4; c4 += 64) store4<T>(o, c4, f32x4_t{0.f, 0.f, 0.f, 0.f});
+    return;
+  }
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pre + r * D);
+  f32x4_t v[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int c4 = lane + k * 64;
+    v[k] = c4 < D4 ? __builtin_nontemporal_load(src + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+  const float mean = wave_sum(s) / float(D);
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if (lane + k * 64 < D4) {
+      const f32x4_t c = v[k] - mean;
+      q += (c.x * c.x + c.y * c.y) + (c.z * c.z + c.w * c.w);
+    }
+  }
+  const float var = wave_sum(q) / float(D);
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int c4 = lane + k * 64;
+    if (c4 < D4) {
+      const f32x4_t y = (v[k] - mean) * rstd * load4<T>(weight, c4, 1.f) + load4<T>(bias, c4, 0.f);
+      store4<T>(o, c4, y);
+    }
+  }
+}
+
+template <typename T, int NV>
+hipError_t launch_rows(const LayerDesc& L, const float* pre, const int32_t* tok,
+                       const void* weight, const void* bias, int64_t nrows, void* out,
+                       hipStream_t st) {
+  const int64_t chunk = int64_t(1) << 30;        // rows per launch keeps the grid in range
+  for (int64_t r0 = 0; r0 < nrows; r0 += chunk) {
+    const int64_t n = std::min(chunk, nrows - r0);
+    hipLaunchKernelGGL((layernorm_rows_kernel<T, NV>),
+                       dim3(unsigned((n + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(kThreads),
+                       0, st, pre + r0 * L.D, tok + r0, L.V0, static_cast<const T*>(weight),
+                       static_cast<const T*>(bias), L.ln_eps, L.D, n,
+                       static_cast<T*>(out) + r0 * L.D);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t launch_typed(const LayerDesc& L, const float* pre, const int32_t* tok,
+                        const void* weight, const void* bias, int64_t nrows, void* out,
+                        hipStream_t st) {
+  // 16-byte vectors per lane: the smallest listed size that holds D / 256 of them
+  const int need = (L.D / 4 + 63) / 64;
+  if (need <= 2) return launch_rows<T, 2>(L, pre, tok, weight, bias, nrows, out, st);
+  if (need <= 4) return launch_rows<T, 4>(L, pre, tok, weight, bias, nrows, out, st);
+  if (need <= 8) return launch_rows<T, 8>(L, pre, tok, weight, bias, nrows, out, st);
+  if (need <= 12) return launch_rows<T, 12>(L, pre, tok, weight, bias, nrows, out, st);
+  if (need <= 16) return launch_rows<T, 16>(L, pre, tok, weight, bias, nrows, out, st);
+  if (need <= 24) return launch_rows<T, 24>(L, pre, tok, weight, bias, nrows, out, st);
+  return launch_rows<T, kMaxNormD / 256>(L, pre, tok, weight, bias, nrows, out, st);
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(const LayerDesc& L, const float* pre, const int32_t* tok,
+                            const void* weight, const void* bias, int64_t nrows, void* out,
+                            hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  if (L.dtype == NGRAM_F32)
+    return launch_typed<float>(L, pre, tok, weight, bias, nrows, out, st);
+  return launch_typed<uint16_t>(L, pre, tok, weight, bias, nrows, out, st);
+}
+
+}  // namespace ngram

@@ -17,12 +17,16 @@
 // shorter ones); the loads of the next slice fly while 8 waves (2 per SIMD) multiply the
 // current one with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Waits and barriers are
 // explicit, so loads stay in flight across them. The epilogue adds the E_0 row, scales by
-// 1/(S+1) in fp32 and rounds once to bf16.
+// 1/(S+1) (times the output factor of the scale amplification, section 3.2.4) in fp32 and
+// rounds once to bf16, or, for the layer-normalisation amplification, stores the unrounded
+// fp32 rows that the normalisation pass reads.
 // Measured on MI355X (64K rows, D = 3072): the loads, not the matrix cores, bound this
 // kernel; each CU keeps about 48 L2 lines in flight, so its load rate is set by L2 hit
 // latency, and the tile order below is chosen for L2 reuse.
 // Blocks are numbered so that the 32 blocks resident on one XCD at a time cover 4 row
 // tiles x 8 output tiles, which keeps their A rows and W panels in that XCD's L2.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace ngram {
@@ -51,10 +55,10 @@ struct ProjArgs {
   const int32_t* tok;                 // [nrows]; outside [0, V0) -> zero row
   const void* E0;                     // [V0, D]
   const void* W;                      // [D, D]
-  void* out;                          // [nrows, D]
+  void* out;                          // [nrows, D], the config dtype or fp32 (F32OUT)
   int64_t nrows;
   int32_t D, S, d, V0;
-  float inv;                          // 1 / (S + 1)
+  float inv;                          // output factor / (S + 1)
   int32_t tiles_m, tiles_n;
 };
 
@@ -96,7 +100,8 @@ __device__ __forceinline__ void wait_loads_and_meet() {
 // 32x32 matrix-core tiles.
 template <int BM> struct WaveGrid { static constexpr int WGM = BM >= 128 ? 4 : 2; };
 
-template <int BM>
+// F32OUT: write the unrounded fp32 rows (input of the layer normalisation) instead of bf16.
+template <int BM, bool F32OUT>
 __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   constexpr int NST = Stages<BM>::value;
   constexpr int WGM = WaveGrid<BM>::WGM;
@@ -317,16 +322,22 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
       const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
                                                            ec * 16);
       if (m < a.nrows) {
-        u32x2_t res = {0u, 0u};
-        if (uint32_t(tk[it]) < uint32_t(a.V0)) {
-          const float y0 = (y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv;
-          const float y1 = (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv;
-          const float y2 = (y[2] + bf16_to_f32(ev[it].y & 0xffffu)) * a.inv;
-          const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
-          res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
-          res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
+        const bool ok = uint32_t(tk[it]) < uint32_t(a.V0);
+        const float y0 = (y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv;
+        const float y1 = (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv;
+        const float y2 = (y[2] + bf16_to_f32(ev[it].y & 0xffffu)) * a.inv;
+        const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
+        if constexpr (F32OUT) {
+          const f32x4_t res = ok ? f32x4_t{y0, y1, y2, y3} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + m * a.D + n) = res;
+        } else {
+          u32x2_t res = {0u, 0u};
+          if (ok) {
+            res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+            res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
+          }
+          __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + m * a.D + n));
         }
-        __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + m * a.D + n));
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next writes
@@ -348,7 +359,7 @@ template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float v) {
   *p = uint16_t(f32_to_bf16_rne(v));
 }
 
-template <typename T>
+template <typename T, typename TO>
 __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
@@ -390,7 +401,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
     __syncthreads();
   }
   const T* __restrict__ E0 = static_cast<const T*>(a.E0);
-  T* __restrict__ out = static_cast<T*>(a.out);
+  TO* __restrict__ out = static_cast<TO*>(a.out);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + ty + 16 * i;
@@ -402,12 +413,13 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
       const int n = n0 + tx + 16 * j;
       if (n >= a.D) continue;
       const float y = ok ? (acc[i][j] + ld<T>(E0 + int64_t(tk) * a.D + n)) * a.inv : 0.f;
-      st<T>(out + m * a.D + n, y);
+      st<TO>(out + m * a.D + n, y);
     }
   }
 }
 
-// N = 1: no sub-tables, e = E_0(t). 16-byte vectors, one per thread.
+// N = 1: no sub-tables, e = E_0(t) (then any output factor or normalisation).
+// Plain rows: 16-byte vectors copied, one per thread.
 __global__ __launch_bounds__(256) void e0_lookup_kernel(const ProjArgs a, int32_t row_bytes) {
   const int64_t cpr = row_bytes / 16;
   const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -420,7 +432,20 @@ __global__ __launch_bounds__(256) void e0_lookup_kernel(const ProjArgs a, int32_
   reinterpret_cast<uint4*>(static_cast<char*>(a.out) + r * row_bytes)[c] = v;
 }
 
-template <int BM>
+// Scaled (or fp32-output) rows: one element per thread, fp32 product, one rounding.
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void e0_scaled_kernel(const ProjArgs a) {
+  const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= a.nrows * a.D) return;
+  const int64_t r = item / a.D;
+  const int32_t tk = a.tok[r];
+  float v = 0.f;
+  if (uint32_t(tk) < uint32_t(a.V0))
+    v = ld<T>(static_cast<const T*>(a.E0) + int64_t(tk) * a.D + (item - r * a.D)) * a.inv;
+  st<TO>(static_cast<TO*>(a.out) + item, v);
+}
+
+template <int BM, bool F32OUT>
 hipError_t run_mfma(ProjArgs a, int64_t nrows, int32_t S, int32_t D, int esz,
                     hipStream_t st) {
   // at most 2^20 row tiles per launch keeps the tile numbering in 32-bit ints
@@ -436,8 +461,8 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int32_t S, int32_t D, int esz,
     a.nrows = n;
     a.tiles_m = int32_t((n + BM - 1) / BM);
     a.tiles_n = D / kBN;
-    hipLaunchKernelGGL(proj_mfma_kernel<BM>, dim3(unsigned(a.tiles_m * a.tiles_n)), dim3(512),
-                       0, st, a);
+    hipLaunchKernelGGL((proj_mfma_kernel<BM, F32OUT>), dim3(unsigned(a.tiles_m * a.tiles_n)),
+                       dim3(512), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -448,7 +473,7 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int32_t S, int32_t D, int esz,
 
 hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
                           const void* W, const int32_t* idx, const int32_t* tok,
-                          int64_t nrows, void* out, hipStream_t st) {
+                          int64_t nrows, void* out, bool f32out, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   ProjArgs a{};
   for (int s = 0; s < L.S; ++s) {
@@ -465,13 +490,34 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
   a.S = L.S;
   a.d = L.d;
   a.V0 = L.V0;
-  a.inv = 1.0f / float(L.S + 1);
+  a.inv = L.scale / float(L.S + 1);
+  const int osz = f32out ? 4 : L.esz;   // bytes per output element
   if (L.S == 0) {
-    const int32_t row_bytes = L.D * L.esz;
-    const int64_t items = nrows * (row_bytes / 16);
-    hipLaunchKernelGGL(e0_lookup_kernel, dim3(unsigned((items + 255) / 256)), dim3(256), 0, st,
-                       a, row_bytes);
-    return hipGetLastError();
+    if (!f32out && L.scale == 1.0f) {
+      const int32_t row_bytes = L.D * L.esz;
+      const int64_t items = nrows * (row_bytes / 16);
+      hipLaunchKernelGGL(e0_lookup_kernel, dim3(unsigned((items + 255) / 256)), dim3(256), 0,
+                         st, a, row_bytes);
+      return hipGetLastError();
+    }
+    // at most 2^30 rows x D elements per launch keeps the grid in range
+    const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 38) / L.D);
+    for (int64_t r0 = 0; r0 < nrows; r0 += rows_per) {
+      ProjArgs b = a;
+      b.nrows = std::min(rows_per, nrows - r0);
+      b.tok = tok + r0;
+      b.out = static_cast<char*>(out) + r0 * L.D * osz;
+      const dim3 grid(unsigned((b.nrows * L.D + 255) / 256));
+      if (L.dtype == NGRAM_F32)
+        hipLaunchKernelGGL((e0_scaled_kernel<float, float>), grid, dim3(256), 0, st, b);
+      else if (f32out)
+        hipLaunchKernelGGL((e0_scaled_kernel<uint16_t, float>), grid, dim3(256), 0, st, b);
+      else
+        hipLaunchKernelGGL((e0_scaled_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, b);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (L.dtype == NGRAM_BF16 && L.D % kBN == 0 && L.d % kBK == 0) {
     // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
@@ -479,11 +525,16 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
     // rows' hash indices in LDS, BM * S <= kIdxBytes / 4.
     const int64_t tiles_n = L.D / kBN;
     const int64_t idx_cap = kIdxBytes / 4;
-    if (((nrows + 255) / 256) * tiles_n >= 512 && 256 * L.S <= idx_cap)
-      return run_mfma<256>(a, nrows, L.S, L.D, 2, st);
-    if (((nrows + 127) / 128) * tiles_n >= 256 && 128 * L.S <= idx_cap)
-      return run_mfma<128>(a, nrows, L.S, L.D, 2, st);
-    return run_mfma<64>(a, nrows, L.S, L.D, 2, st);
+    const bool big = ((nrows + 255) / 256) * tiles_n >= 512 && 256 * L.S <= idx_cap;
+    const bool mid = ((nrows + 127) / 128) * tiles_n >= 256 && 128 * L.S <= idx_cap;
+    if (f32out) {
+      if (big) return run_mfma<256, true>(a, nrows, L.S, L.D, osz, st);
+      if (mid) return run_mfma<128, true>(a, nrows, L.S, L.D, osz, st);
+      return run_mfma<64, true>(a, nrows, L.S, L.D, osz, st);
+    }
+    if (big) return run_mfma<256, false>(a, nrows, L.S, L.D, osz, st);
+    if (mid) return run_mfma<128, false>(a, nrows, L.S, L.D, osz, st);
+    return run_mfma<64, false>(a, nrows, L.S, L.D, osz, st);
   }
   const unsigned gy = unsigned((L.D + 63) / 64);
   for (int64_t r0 = 0; r0 < nrows; r0 += (int64_t(1) << 30)) {
@@ -491,13 +542,15 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
     const int64_t n = nrows - r0 < (int64_t(1) << 30) ? nrows - r0 : (int64_t(1) << 30);
     b.idx = idx + r0 * L.S;
     b.tok = tok + r0;
-    b.out = static_cast<char*>(out) + r0 * L.D * L.esz;
+    b.out = static_cast<char*>(out) + r0 * L.D * osz;
     b.nrows = n;
     const dim3 grid(unsigned((n + 63) / 64), gy);
     if (L.dtype == NGRAM_F32)
-      hipLaunchKernelGGL(proj_generic_kernel<float>, grid, dim3(256), 0, st, b);
+      hipLaunchKernelGGL((proj_generic_kernel<float, float>), grid, dim3(256), 0, st, b);
+    else if (f32out)
+      hipLaunchKernelGGL((proj_generic_kernel<uint16_t, float>), grid, dim3(256), 0, st, b);
     else
-      hipLaunchKernelGGL(proj_generic_kernel<uint16_t>, grid, dim3(256), 0, st, b);
+      hipLaunchKernelGGL((proj_generic_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,4 +1,6 @@
 // Host-side validation of the layer config and workspace layout (no HIP calls).
+#include <cmath>
+
 #include "layer_desc.h"
 
 namespace ngram {
@@ -37,6 +39,21 @@ int describe(const ngram_embed_config* cfg, LayerDesc* out) {
     // Horner step x*V0 + t with x < V, t < V0 stays below V*V0 <= 2^63 - 1.
     if (vmax > ((uint64_t(1) << 63) - 1) / uint64_t(cfg->V0)) return NGRAM_EOVERFLOW;
   }
+  // Embedding amplification (section 3.2.4): a finite output factor, or a layer
+  // normalisation with a positive epsilon over rows that fit one block's LDS.
+  L.amp = cfg->amp;
+  L.scale = 1.0f;
+  L.ln_eps = 0.0f;
+  if (cfg->amp == NGRAM_AMP_SCALE) {
+    if (!std::isfinite(cfg->amp_scale)) return NGRAM_EINVAL;
+    L.scale = cfg->amp_scale;
+  } else if (cfg->amp == NGRAM_AMP_LAYERNORM) {
+    if (!std::isfinite(cfg->ln_eps) || !(cfg->ln_eps > 0.0f)) return NGRAM_EINVAL;
+    if (cfg->D > kMaxNormD) return NGRAM_EINVAL;
+    L.ln_eps = cfg->ln_eps;
+  } else if (cfg->amp != NGRAM_AMP_NONE) {
+    return NGRAM_EINVAL;
+  }
   *out = L;
   return NGRAM_OK;
 }
@@ -48,7 +65,9 @@ bool ws_layout(const LayerDesc& L, int64_t rows, WsLayout* out) {
   WsLayout w;
   w.tok_off = 256;
   w.idx_off = w.tok_off + align256(size_t(rows) * 4);
-  w.total = w.idx_off + align256(size_t(rows) * size_t(L.S) * 4);
+  w.pre_off = w.idx_off + align256(size_t(rows) * size_t(L.S) * 4);
+  w.total = w.pre_off +
+            (L.amp == NGRAM_AMP_LAYERNORM ? align256(size_t(rows) * size_t(L.D) * 4) : 0);
   *out = w;
   return true;
 }

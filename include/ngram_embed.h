@@ -14,7 +14,9 @@
  *
  * sub-tables E_{n,k} of shape [V_{n,k}, d], d = D/((N-1)K), and projections W_{n,k} of
  * shape [D, d]. Section 4.2 of that page (N-gram cache, KV-cache-like management of n-gram
- * ids on the device) motivates the decode entry points.
+ * ids on the device) motivates the decode entry points. Section 3.2.4 of the same page
+ * (embedding amplification) gives the optional output scale or layer normalisation that
+ * the config's `amp` field selects.
  *
  * Conventions used throughout:
  *  - S = (N-1)K sub-tables, ordered s = (n-2)*K + (k-1) (n-major, k-minor).
@@ -64,6 +66,18 @@ enum {
   NGRAM_FLAG_BAD_COUNT = 4    /* n_new or n_accept outside [0, tmax] */
 };
 
+/* Embedding amplification (section 3.2.4): what is applied to e_i before it is written.
+ * The pages describe both strategies without a formula for the second; the layer
+ * normalisation here is the usual one over the D values of a row:
+ *   y = (e - mean) / sqrt(var + ln_eps) * ln_weight + ln_bias,  var the biased variance,
+ * computed in fp32 from the unrounded e and rounded once. */
+enum {
+  NGRAM_AMP_NONE = 0,      /* out = e_i: the final form as is */
+  NGRAM_AMP_SCALE = 1,     /* out = amp_scale * e_i (the pages use sqrt(D)), one rounding */
+  NGRAM_AMP_LAYERNORM = 2  /* out = LayerNorm(e_i) as above; needs the workspace (prefill,
+                              decode), so ngram_embed_project rejects it */
+};
+
 #define NGRAM_MAX_ORDER 16         /* largest accepted N */
 #define NGRAM_MAX_SUBTABLES 64     /* largest accepted (N-1)K */
 #define NGRAM_MAX_DECODE_TOKENS 8  /* largest accepted tmax (1 + speculative drafts) */
@@ -78,6 +92,10 @@ typedef struct ngram_embed_config {
   int64_t V0;        /* base vocabulary, 1 <= V0 < 2^31 */
   const int64_t* V;  /* host, S entries: V_{n,k} in sub-table order, 1 <= V < 2^31,
                         and V0 * max V < 2^63 (else NGRAM_EOVERFLOW) */
+  int32_t amp;       /* NGRAM_AMP_*; 0 (a zero-filled config) is the final form as is */
+  float amp_scale;   /* NGRAM_AMP_SCALE: the factor, finite (ignored otherwise) */
+  float ln_eps;      /* NGRAM_AMP_LAYERNORM: variance epsilon, finite and > 0; the layer
+                        normalisation also needs D <= 8192 (ignored otherwise) */
 } ngram_embed_config;
 
 /* Parameters of the layer, all in device memory, in the config's dtype. Every device
@@ -86,6 +104,9 @@ typedef struct ngram_embed_tables {
   const void* E0;        /* [V0, D] base embedding E_0 */
   const void* const* E;  /* host array of S device pointers; E[s] is E_{n,k} [V_{n,k}, d] */
   const void* W;         /* [D, D] stacked projection: W[o, s*d + c] = W_{n,k}[o, c] */
+  const void* ln_weight; /* [D] layer-normalisation weight, or NULL for all ones (read only
+                            with NGRAM_AMP_LAYERNORM) */
+  const void* ln_bias;   /* [D] layer-normalisation bias, or NULL for zeros (same) */
 } ngram_embed_tables;
 
 /* N-gram cache of a batch of sequences in decode (section 4.2): the last N-1 committed ids
@@ -99,9 +120,11 @@ typedef struct ngram_cache {
 
 /* ---------------------------------------------------------------- workspace
  * Scratch for up to `max_rows` output rows: the error flags (int32 at offset 0), the E_0
- * token of every row (int32 [max_rows] at *tok_off) and the hash indices (int32
- * [max_rows, S] at *idx_off). Must be 256-byte aligned and zero-filled once before first
- * use (the flags are sticky until cleared). Returns the size in bytes, 0 on a bad config. */
+ * token of every row (int32 [max_rows] at *tok_off), the hash indices (int32
+ * [max_rows, S] at *idx_off) and, with NGRAM_AMP_LAYERNORM, the unrounded rows e_i (fp32
+ * [max_rows, D], after the indices) that the normalisation reads. Must be 256-byte
+ * aligned and zero-filled once before first use (the flags are sticky until cleared).
+ * Returns the size in bytes, 0 on a bad config. */
 size_t ngram_embed_workspace_size(const ngram_embed_config* cfg, int64_t max_rows);
 int ngram_embed_workspace_layout(const ngram_embed_config* cfg, int64_t max_rows,
                                  size_t* tok_off, size_t* idx_off);
@@ -128,6 +151,7 @@ int ngram_embed_gather(const ngram_embed_config* cfg, const ngram_embed_tables* 
 
 /* ---------------------------------------------------------------- kernels 2+3: projection
  * out[r, :] = ( E_0[tok[r], :] + sum_s W_{n,k} E_{n,k}[idx[r*S + s], :] ) / (S + 1)
+ * (times amp_scale with NGRAM_AMP_SCALE; NGRAM_AMP_LAYERNORM returns NGRAM_EINVAL here)
  * for nrows rows: the sub-table rows are gathered straight into on-chip memory and
  * multiplied by the stacked W on the matrix cores, with the E_0 add and the scale in the
  * epilogue. tok: device int32 [nrows]; rows whose tok is outside [0, V0) are written as
@@ -139,7 +163,9 @@ int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables*
 
 /* ---------------------------------------------------------------- prefill
  * The whole forward pass over packed sequences: ngram_embed_hash into the workspace, then
- * ngram_embed_project with tok = tokens. out: device [ntok, D]. ws: workspace of at least
+ * ngram_embed_project with tok = tokens, then the amplification the config selects (the
+ * layer normalisation as a second pass over the unrounded rows kept in the workspace; rows
+ * of ids outside [0, V0) stay zero). out: device [ntok, D]. ws: workspace of at least
  * ngram_embed_workspace_size(cfg, ntok) bytes; bad ids set NGRAM_FLAG_BAD_TOKEN there. */
 int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                         const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
@@ -156,7 +182,8 @@ int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const in
  * proposes its first n_new[b] entries (device int32 [nseq], 0 <= n_new <= tmax <= 8) as the
  * positions len[b], len[b]+1, ... . out[b, j, :] (device [nseq, tmax, D]) is the embedding
  * that a prefill of (committed history, new_tokens[b, 0..j]) gives its last position; rows
- * j >= n_new[b] are zeros. The context comes from the cache (the last N-1 committed ids),
+ * j >= n_new[b] are zeros (also with amplification, which applies as in prefill). The
+ * context comes from the cache (the last N-1 committed ids),
  * never from the host. If n_commit (device int32 [nseq], 0 <= n_commit <= n_new) is not
  * NULL, the first n_commit[b] new ids are then appended to the cache, as by
  * ngram_cache_commit. ws: at least ngram_embed_workspace_size(cfg, nseq * tmax) bytes; the

@@ -36,6 +36,8 @@ def device_fetch(E0, E):
 
 
 def w_blocks(W, S):
+    if S == 0:                     # N = 1: no sub-tables, no projections
+        return []
     Wh = to_f64(W)
     d = Wh.shape[1] // S
     return [Wh[:, s * d:(s + 1) * d] for s in range(S)]

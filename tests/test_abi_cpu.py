@@ -168,6 +168,34 @@ def test_hash_gather_project_argument_checks(lib):
     assert lib.ngram_embed_clear_error_flag(FAKE + 16, 0) == -3
 
 
+def test_amplification_checks(lib):
+    """Embedding amplification: the layer normalisation keeps the fp32 rows in the
+    workspace, needs that workspace (so the bare projection refuses it), a positive epsilon
+    and 16-byte aligned parameters; the scale needs a finite factor."""
+    P = ctypes.byref
+    plain, ln = tiny_cfg(), tiny_cfg(amp="layernorm")
+    assert g.ngram_embed_workspace_size(ln, 1000) == \
+        g.ngram_embed_workspace_size(plain, 1000) + ((1000 * 64 * 4 + 255) // 256) * 256
+    assert g.ngram_embed_workspace_size(tiny_cfg(amp="scale"), 1000) == \
+        g.ngram_embed_workspace_size(plain, 1000)
+    for kw in (dict(amp="layernorm", ln_eps=0.0), dict(amp="layernorm", ln_eps=-1e-5),
+               dict(amp="layernorm", ln_eps=float("nan")), dict(amp="scale", amp_scale=float("inf")),
+               dict(amp="scale", amp_scale=float("nan")), dict(amp=3), dict(amp=-1),
+               dict(amp="layernorm", N=2, K=1, D=8192 + 64, V=[5003])):
+        c, keep = tiny_cfg(**kw)._c()
+        assert lib.ngram_embed_workspace_size(P(c), 16) == 0, kw
+        assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, 1 << 20, 0) == -1
+    c, keep = ln._c()
+    T, keep2 = _tables_c(4)
+    assert lib.ngram_embed_project(P(c), P(T), FAKE, FAKE, 5, FAKE, 0) == -1
+    ws_need = g.ngram_embed_workspace_size(ln, 16)
+    arr = (ctypes.c_void_p * 4)(*([FAKE] * 4))
+    for wt, bs in ((FAKE + 2, None), (None, FAKE + 8)):
+        Tb = g._CTables(FAKE, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), FAKE, wt, bs)
+        assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need,
+                                       0) == -3
+
+
 def test_zero_sized_calls_enqueue_nothing(lib):
     # ntok = 0 / nrows = 0 / nseq = 0 succeed without touching the device.
     cfg = tiny_cfg()

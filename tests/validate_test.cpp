@@ -56,6 +56,42 @@ int main() {
   EXPECT(ngram::ws_layout(L, 1000, &w) && w.tok_off == 256 && w.idx_off == 256 + 4096 &&
          w.total == w.idx_off + 16128);
   EXPECT(!ngram::ws_layout(L, -1, &w));
+
+  // embedding amplification: a zero-filled config is the plain layer (factor 1)
+  EXPECT(ngram::describe(&c, &L) == NGRAM_OK && L.amp == NGRAM_AMP_NONE && L.scale == 1.0f);
+  ngram_embed_config amp = c;
+  amp.amp = NGRAM_AMP_SCALE;
+  amp.amp_scale = 8.0f;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_OK && L.scale == 8.0f);
+  amp.amp_scale = __builtin_nanf("");
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp.amp_scale = __builtin_inff();
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp = c;
+  amp.amp = NGRAM_AMP_LAYERNORM;
+  amp.amp_scale = 3.0f;            // ignored by the layer normalisation
+  amp.ln_eps = 1e-5f;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_OK && L.scale == 1.0f && L.ln_eps == 1e-5f);
+  // the layer normalisation keeps the unrounded fp32 rows in the workspace
+  EXPECT(ngram::ws_layout(L, 1000, &w) && w.pre_off == w.idx_off + 16128 &&
+         w.total == w.pre_off + 1000 * 64 * 4);
+  amp.ln_eps = 0.0f;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp.ln_eps = -1.0f;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp.ln_eps = __builtin_nanf("");
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp.ln_eps = 1e-5f;
+  amp.D = 8192 + 64;               // rows longer than one block normalises
+  amp.K = 1;                       // S = 2 divides D; d = 4128 bf16 is whole 16-byte vectors
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp.D = 8192;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_OK);
+  amp = c;
+  amp.amp = 3;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  amp.amp = -1;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
   EXPECT(ngram::aligned(reinterpret_cast<void*>(0x1000), 256));
   EXPECT(!ngram::aligned(reinterpret_cast<void*>(0x1004), 16));
   EXPECT(!ngram::aligned(nullptr, 4));
