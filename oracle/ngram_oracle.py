@@ -24,6 +24,9 @@ Readings where the pages are silent:
   * N = 1 has no sub-tables: e_i = E_0(t_i);
   * token ids must lie in [0, V0) (the hash reads them as base-V0 digits).
 
+Backward (training, which the pages do but do not spell out): backward() gives the plain
+gradients of the final form, duplicates accumulated.
+
 Embedding amplification (section 3.2.4 of the same page, outside the final form itself):
 amplify() applies the output scale or the layer normalisation the pages describe; the
 reading of the latter is stated there.
@@ -218,6 +221,39 @@ def amplify(e: np.ndarray, mode: str = "none", scale: float = 1.0, eps: float = 
             y = y + np.asarray(bias, dtype=np.float64)
         return y
     raise ValueError(f"amplification mode must be one of {AMP_MODES}")
+
+
+def backward(D: int, N: int, K: int, tokens: Sequence[int], idx: np.ndarray, dout: np.ndarray,
+             fetch: RowFetch, W_blocks: Sequence[np.ndarray], V0: int, V: Sequence[int],
+             scale: float = 1.0):
+    """Gradients of the final form (section A2) for one batch, float64.
+
+    The pages train the model but give no backward; this is the plain reading: the layer is
+    e_i = c (E_0(t_i) + sum_s W_s E_s(h_{i,s})) with c = scale / ((N-1)K + 1) (scale 1, or the
+    amplification factor of section 3.2.4), so for the upstream gradient dout = dL/de [T, D]:
+      dE_0[t]    = c * sum over positions i with t_i = t of dout_i,
+      dW_s       = c * sum_i dout_i E_s(h_{i,s})^T                     ([D, d] each),
+      dE_s[r]    = c * sum over positions i with h_{i,s} = r of W_s^T dout_i.
+    Repeated ids and indices accumulate. Returns (dE0 [V0, D], [dE_s [V_s, d]], [dW_s])."""
+    S = num_subtables(N, K)
+    d = D // S if S else 0
+    tok = np.asarray(tokens, dtype=np.int64)
+    g = np.asarray(dout, dtype=np.float64)
+    if g.shape != (len(tok), D):
+        raise ValueError("dout must be [T, D]")
+    c = float(scale) / float(S + 1)
+    dE0 = np.zeros((V0, D))
+    np.add.at(dE0, tok, c * g)                                      # E_0(t_i) appears once
+    dE, dW = [], []
+    for s in range(S):
+        rows = np.asarray(fetch(s, idx[:, s]), dtype=np.float64)    # E_s(h_{i,s}) [T, d]
+        Ws = np.asarray(W_blocks[s], dtype=np.float64)              # [D, d]
+        dW.append(c * (g.T @ rows))                                 # sum_i dout_i rows_i^T
+        grad_rows = c * (g @ Ws)                                    # W_s^T dout_i, [T, d]
+        dEs = np.zeros((int(V[s]), d))
+        np.add.at(dEs, np.asarray(idx[:, s], dtype=np.int64), grad_rows)
+        dE.append(dEs)
+    return dE0, dE, dW
 
 
 def param_count(V0: int, D: int, N: int, K: int, V: Sequence[int]) -> dict:

@@ -428,3 +428,107 @@ def test_layernorm_pins_catch_planted_mistakes(monkeypatch, mistake):
         return y * b + w if mistake == "affine_swapped" else y * w + b
     monkeypatch.setattr(O, "amplify", planted)
     assert _fails(check_layernorm_closed_form)
+
+
+# ------------------------------------------------------------------ backward (training)
+# The gradients of the final form, pinned to the oracle's own forward by finite differences:
+# L = sum(dout * e) is linear in E_0, in each E_s and in each W_s, so a central difference in
+# float64 is exact up to rounding, whatever the step.
+
+def _bw_case(seed=3, V0=9, D=12, N=3, K=2, lengths=(7, 1, 6)):
+    rng = np.random.default_rng(seed)
+    S = (N - 1) * K
+    d = D // S
+    V = [5, 7, 6, 11][:S]
+    seqs = [rng.integers(0, V0, size=L) for L in lengths]
+    tokens = np.concatenate(seqs)
+    cu = cu_seqlens_from_lengths(lengths)
+    E0 = rng.normal(size=(V0, D))
+    E = [rng.normal(size=(V[s], d)) for s in range(S)]
+    Wb = [rng.normal(size=(D, d)) for _ in range(S)]
+    dout = rng.normal(size=(len(tokens), D))
+    return dict(V0=V0, D=D, N=N, K=K, V=V, tokens=tokens, cu=cu, E0=E0, E=E, W=Wb, dout=dout)
+
+
+def _loss(c, E0, E, Wb, scale):
+    idx = O.hash_indices(c["V0"], c["N"], c["K"], c["V"], c["tokens"], c["cu"])
+    e = O.embed_from_indices(c["D"], c["N"], c["K"], c["tokens"], idx, O.table_fetch(E0, E), Wb)
+    return float(np.sum(c["dout"] * e * scale))
+
+
+def check_backward_fd(scale=1.0):
+    c = _bw_case()
+    idx = O.hash_indices(c["V0"], c["N"], c["K"], c["V"], c["tokens"], c["cu"])
+    dE0, dE, dW = O.backward(c["D"], c["N"], c["K"], c["tokens"], idx, c["dout"],
+                             O.table_fetch(c["E0"], c["E"]), c["W"], c["V0"], c["V"], scale)
+    rng = np.random.default_rng(4)
+    h = 0.5
+
+    def fd(kind, s, pos):
+        def shifted(delta):
+            E0, E, Wb = c["E0"].copy(), [e.copy() for e in c["E"]], [w.copy() for w in c["W"]]
+            tgt = E0 if kind == "E0" else (E[s] if kind == "E" else Wb[s])
+            tgt[pos] += delta
+            return _loss(c, E0, E, Wb, scale)
+        return (shifted(h) - shifted(-h)) / (2 * h)
+
+    for _ in range(12):
+        pos = (int(rng.integers(c["V0"])), int(rng.integers(c["D"])))
+        np.testing.assert_allclose(dE0[pos], fd("E0", None, pos), rtol=1e-9, atol=1e-9)
+    for s in range(len(c["E"])):
+        for _ in range(6):
+            pos = (int(rng.integers(c["V"][s])), int(rng.integers(c["D"] // len(c["E"]))))
+            np.testing.assert_allclose(dE[s][pos], fd("E", s, pos), rtol=1e-9, atol=1e-9)
+            pos = (int(rng.integers(c["D"])), int(rng.integers(c["D"] // len(c["E"]))))
+            np.testing.assert_allclose(dW[s][pos], fd("W", s, pos), rtol=1e-9, atol=1e-9)
+
+
+def test_backward_matches_finite_differences():
+    check_backward_fd()
+    check_backward_fd(scale=np.sqrt(12.0))
+
+
+def test_backward_identity_projection_closed_form():
+    """N = 2, K = 1 (S = 1, d = D) with W = I: dE_1[h] and dE_0[t] are the scattered sums of
+    dout / 2, and dW = (1/2) sum_i dout_i E_1(h_i)^T."""
+    rng = np.random.default_rng(8)
+    V0, D, V = 5, 4, [3]
+    tokens = np.array([1, 1, 4, 1, 0, 2])
+    cu = np.array([0, 6])
+    idx = O.hash_indices(V0, 2, 1, V, tokens, cu)
+    E1 = rng.normal(size=(3, D))
+    dout = rng.normal(size=(6, D))
+    dE0, dE, dW = O.backward(D, 2, 1, tokens, idx, dout, O.table_fetch(np.zeros((V0, D)), [E1]),
+                             [np.eye(D)], V0, V)
+    want0 = np.zeros((V0, D))
+    want1 = np.zeros((3, D))
+    wantW = np.zeros((D, D))
+    for i in range(6):
+        want0[tokens[i]] += dout[i] / 2
+        want1[idx[i, 0]] += dout[i] / 2
+        wantW += np.outer(dout[i], E1[idx[i, 0]]) / 2
+    np.testing.assert_allclose(dE0, want0, atol=1e-15)
+    np.testing.assert_allclose(dE[0], want1, atol=1e-15)
+    np.testing.assert_allclose(dW[0], wantW, atol=1e-14)
+    # token 1 appears three times: its gradient row is the sum of three upstream rows
+    np.testing.assert_allclose(dE0[1], (dout[0] + dout[1] + dout[3]) / 2, atol=1e-15)
+
+
+@pytest.mark.parametrize("mistake", ["no_scale", "W_rows_flipped", "overwrite_duplicates"])
+def test_backward_pins_catch_planted_mistakes(monkeypatch, mistake):
+    real = O.backward
+
+    def planted(D, N, K, tokens, idx, dout, fetch, W_blocks, V0, V, scale=1.0):
+        S = (N - 1) * K
+        if mistake == "no_scale":
+            return real(D, N, K, tokens, idx, dout, fetch, W_blocks, V0, V, scale * (S + 1))
+        if mistake == "W_rows_flipped":
+            return real(D, N, K, tokens, idx, dout, fetch,
+                        [np.asarray(w)[::-1] for w in W_blocks], V0, V, scale)
+        dE0, dE, dW = real(D, N, K, tokens, idx, dout, fetch, W_blocks, V0, V, scale)
+        c = scale / (S + 1)
+        dE0 = np.zeros_like(dE0)
+        dE0[np.asarray(tokens)] = c * np.asarray(dout)       # last write wins: no accumulation
+        return dE0, dE, dW
+    monkeypatch.setattr(O, "backward", planted)
+    assert _fails(check_backward_fd)
