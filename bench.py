@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward (training gradients) timing")
     ap.add_argument("--no-amp", action="store_true",
                     help="skip the amplified (scale / layer-norm) prefill timings")
     ap.add_argument("--decode-steps", type=int, default=1000)
@@ -214,7 +216,7 @@ def main():
     traffic = counter_traffic("project", "project.hip")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "proj_mfma_kernel<256, false>",
+                "traffic": traffic, "kernel": "proj_mfma_kernel<256, 0>",
                 "kernel_us": round(t_proj * 1e6, 1),
                 "algorithmic_hbm_GBps": round(alg_bytes_proj / t_proj / 1e9, 1)}
     log(f"step {ms_per_step:.3f} ms: hash {t_hash*1e6:.1f} us, project {t_proj*1e6:.1f} us "
@@ -248,6 +250,10 @@ def main():
     if not args.no_amp:
         amp = bench_amplification(g, w, tables, toks, cu, dev, stream, args.steps)
 
+    backward = None
+    if not args.no_backward:
+        backward = bench_backward(g, w, cfg, tables, toks, cu, dev, stream, min(args.steps, 10))
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(g, WL, cfg, tables, dev, stream, args.decode_steps)
@@ -273,6 +279,7 @@ def main():
         "roofline": roofline,
         "gather": gather,
         "amplification": amp,
+        "backward": backward,
         "decode": decode,
         "cpu_baseline": cpu,
     }
@@ -326,6 +333,49 @@ def bench_amplification(g, w, tables, toks, cu, dev, stream, steps):
     res["layernorm"]["norm_pass_bytes"] = T * w.D * (4 + 2)
     log(f"prefill: plain {res['none']['us_per_step']:.0f} us, x sqrt(D) "
         f"{res['scale']['us_per_step']:.0f} us, layer norm {res['layernorm']['us_per_step']:.0f} us")
+    return res
+
+
+def bench_backward(g, w, cfg, tables, toks, cu, dev, stream, steps):
+    """Gradients of the 64K-token batch for every parameter (fp32 buffers: 120 GB for the
+    sub-tables, 3.2 GB for E_0, 38 MB for W), accumulated, HIP events around each call. Its two
+    products (dout W and dout^T G) are 2 x 2*T*D^2 flops on the matrix cores; the rest is
+    the hash, transposes, sorts and segmented sums."""
+    import numpy as np
+    import torch
+
+    T = int(toks[0].shape[0])
+    rng = np.random.default_rng(11)
+    dout = torch.as_tensor(rng.normal(0.0, 1.0, size=(T, w.D)).astype(np.float32)).to(
+        torch.bfloat16).to(dev)
+    dE0 = torch.zeros((w.V0, w.D), dtype=torch.float32, device=dev)
+    dE = [torch.zeros((v, w.d), dtype=torch.float32, device=dev) for v in w.V]
+    dW = torch.zeros((w.D, w.D), dtype=torch.float32, device=dev)
+    ws = g.alloc_backward_workspace(cfg, T, device=dev)
+    log(f"backward: {steps} steps, workspace {ws.numel() / 1e9:.2f} GB")
+    for k in range(2):
+        g.ngram_embed_backward(cfg, tables, toks[k % len(toks)], cu, dout, dE0, dE, dW, ws,
+                               stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(stream)
+        g.ngram_embed_backward(cfg, tables, toks[k % len(toks)], cu, dout, dE0, dE, dW, ws,
+                               stream=stream)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize(dev)
+    if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+        raise RuntimeError("device error flags set during the backward")
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    flops = 2 * 2.0 * T * w.D * w.D
+    res = {"workload": WORKLOAD, "steps": steps, "us_per_step": round(t * 1e6, 1),
+           "tokens_per_s": round(T / t, 1), "product_flops": flops,
+           "tflops_over_step": round(flops / t / 1e12, 1),
+           "workspace_bytes": int(ws.numel())}
+    log(f"backward {t * 1e6:.0f} us per 64K-token step ({flops / t / 1e12:.0f} TFLOP/s of "
+        "products over the whole step)")
+    del dE0, dE, dW, ws, dout
+    torch.cuda.empty_cache()
     return res
 
 

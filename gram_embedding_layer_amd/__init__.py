@@ -24,6 +24,7 @@ __all__ = [
     "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
     "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
     "ngram_embed_clear_error_flag", "ngram_embed_status_string", "alloc_workspace",
+    "ngram_embed_backward_workspace_size", "ngram_embed_backward", "alloc_backward_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libngram_embed.so")
@@ -90,6 +91,9 @@ def load():
         "ngram_cache_init": (ctypes.c_int, [cfgp, cachep, P, P, I64, P]),
         "ngram_embed_decode": (ctypes.c_int, [cfgp, tabp, cachep, P, P, I32, P, P, P, SZ, P]),
         "ngram_cache_commit": (ctypes.c_int, [cfgp, cachep, P, P, I32, P, P]),
+        "ngram_embed_backward_workspace_size": (SZ, [cfgp, I64]),
+        "ngram_embed_backward": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, P,
+                                                ctypes.POINTER(P), P, P, SZ, P]),
         "ngram_embed_read_error_flag": (ctypes.c_int, [P, ctypes.POINTER(I32), P]),
         "ngram_embed_clear_error_flag": (ctypes.c_int, [P, P]),
         "ngram_embed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -227,6 +231,35 @@ def alloc_workspace(cfg: Config, max_rows: int, device="cuda"):
     if n == 0:
         raise NgramError("ngram_embed_workspace_size", -1)
     return torch.zeros((n,), dtype=torch.uint8, device=device)
+
+
+def ngram_embed_backward_workspace_size(cfg: Config, ntok: int) -> int:
+    c, keep = cfg._c()
+    return int(load().ngram_embed_backward_workspace_size(ctypes.byref(c), int(ntok)))
+
+
+def alloc_backward_workspace(cfg: Config, ntok: int, device="cuda"):
+    """Zero-filled uint8 device workspace for the backward of ntok tokens."""
+    import torch
+    n = ngram_embed_backward_workspace_size(cfg, ntok)
+    if n == 0:
+        raise NgramError("ngram_embed_backward_workspace_size", -1)
+    return torch.zeros((n,), dtype=torch.uint8, device=device)
+
+
+def ngram_embed_backward(cfg: Config, tables: Tables, tokens, cu_seqlens, dout, dE0, dE, dW,
+                         ws, stream=None):
+    """Accumulate the gradients of one batch into fp32 buffers dE0 [V0, D], dE (S tensors
+    [V_s, d]) and dW [D, D]; any may be None."""
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    dE_arr = None
+    if dE is not None:
+        dE_arr = (ctypes.c_void_p * max(1, len(dE)))(*[_ptr(e) for e in dE])
+    _check("ngram_embed_backward", load().ngram_embed_backward(
+        ctypes.byref(c), ctypes.byref(t), _ptr(tokens), _ptr(cu_seqlens),
+        int(cu_seqlens.numel()) - 1, int(tokens.numel()), _ptr(dout), _ptr(dE0),
+        dE_arr, _ptr(dW), _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
 
 
 def ngram_embed_hash(cfg: Config, tokens, cu_seqlens, idx, err_flags=None, stream=None):

@@ -209,6 +209,72 @@ int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
                                                static_cast<hipStream_t>(stream)));
 }
 
+size_t ngram_embed_backward_workspace_size(const ngram_embed_config* cfg, int64_t ntok) {
+  LayerDesc L;
+  ngram::BwLayout lay;
+  if (ngram::describe(cfg, &L) != NGRAM_OK || L.amp == NGRAM_AMP_LAYERNORM ||
+      !ngram::bw_layout(L, ntok, &lay))
+    return 0;
+  return lay.total;
+}
+
+int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                         const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
+                         int64_t ntok, const void* dout, float* dE0, float* const* dE,
+                         float* dW, void* ws, size_t ws_bytes, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (L.amp == NGRAM_AMP_LAYERNORM) return NGRAM_EINVAL;   // not differentiated here
+  if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
+  // positions are sort values (uint32) and the tile numbering stays in range
+  if (ntok > (int64_t(1) << 31) / (L.S > 0 ? L.S : 1)) return NGRAM_EINVAL;
+  ngram::BwLayout lay;
+  if (!ngram::bw_layout(L, ntok, &lay)) return NGRAM_EINVAL;
+  if (!ngram::aligned(ws, 256) || ws_bytes < lay.total) return NGRAM_EWORKSPACE;
+  if (ntok == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4) || !ngram::aligned(dout, 16))
+    return NGRAM_EALIGN;
+  if ((dE0 != nullptr && !ngram::aligned(dE0, 16)) || (dW != nullptr && !ngram::aligned(dW, 16)))
+    return NGRAM_EALIGN;
+  if (dE != nullptr)
+    for (int s = 0; s < L.S; ++s)
+      if (!ngram::aligned(dE[s], 16)) return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
+  if (L.S > 0) {
+    rc = hip_status(ngram::launch_hash_prefill(L, tokens, cu_seqlens, nseq, ntok, idx,
+                                               ws_flags(ws), st));
+    if (rc != NGRAM_OK) return rc;
+  }
+  ngram::BackwardArgs b{};
+  b.E = tables->E;
+  b.W = tables->W;
+  b.tokens = tokens;
+  b.idx = idx;
+  b.dout = dout;
+  b.dE0 = dE0;
+  b.dE = dE;
+  b.dW = dW;
+  b.rows = ntok;
+  b.ident = reinterpret_cast<int32_t*>(w + lay.ident_off);
+  b.WT = w + lay.wt_off;
+  b.doutT = w + lay.doutt_off;
+  b.GT = w + lay.gt_off;
+  b.dG = reinterpret_cast<float*>(w + lay.dg_off);
+  b.part = reinterpret_cast<float*>(w + lay.part_off);
+  b.keys0 = reinterpret_cast<uint64_t*>(w + lay.keys0_off);
+  b.keys1 = reinterpret_cast<uint64_t*>(w + lay.keys1_off);
+  b.vals0 = reinterpret_cast<uint32_t*>(w + lay.vals0_off);
+  b.vals1 = reinterpret_cast<uint32_t*>(w + lay.vals1_off);
+  b.hist = reinterpret_cast<uint32_t*>(w + lay.hist_off);
+  b.head = reinterpret_cast<float*>(w + lay.head_off);
+  b.tail = reinterpret_cast<float*>(w + lay.tail_off);
+  return hip_status(ngram::launch_backward(L, b, st));
+}
+
 int ngram_embed_read_error_flag(const void* ws, int32_t* flags, void* stream) {
   if (!ngram::aligned(ws, 256) || flags == nullptr) return NGRAM_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -39,6 +39,43 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
                           const void* W, const int32_t* idx, const int32_t* tok,
                           int64_t nrows, void* out, bool f32out, hipStream_t st);
 
+// dense product for the backward: out = inv * A B^T (fp32, overwritten) or, with
+// accumulate, out += inv * A B^T through `splits` fp32 partial sums in `part`
+// ([splits, M, ldo]) added in split order. A [M, K] and B [N, K] row-major in the config
+// dtype; ident: int32 [M] = 0..M-1.
+hipError_t launch_dense_product(const LayerDesc& L, const void* A, int64_t M, const void* B,
+                                int32_t N, int32_t K, const int32_t* ident, float* out,
+                                int64_t ldo, float inv, bool accumulate, float* part,
+                                int32_t splits, hipStream_t st);
+
+// backward (training): gradients accumulated into fp32 buffers; the workspace pieces
+// follow BwLayout
+struct BackwardArgs {
+  const void* const* E;   // sub-tables (host array of S device pointers)
+  const void* W;          // [D, D] stacked
+  const int32_t* tokens;  // [rows]
+  const int32_t* idx;     // [rows, S] (hash indices, computed first)
+  const void* dout;       // [rows, D] upstream gradient, config dtype
+  float* dE0;             // [V0, D] or null
+  float* const* dE;       // host array of S device pointers [V_s, d], or null
+  float* dW;              // [D, D] or null
+  int64_t rows;
+  int32_t* ident;         // workspace pieces
+  void* WT;
+  void* doutT;
+  void* GT;
+  float* dG;
+  float* part;
+  uint64_t* keys0;
+  uint64_t* keys1;
+  uint32_t* vals0;
+  uint32_t* vals1;
+  uint32_t* hist;
+  float* head;
+  float* tail;
+};
+hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_t st);
+
 // amplification by layer normalisation: pre fp32 [nrows, D] -> out [nrows, D] (config dtype);
 // weight / bias: [D] in the config dtype or null
 hipError_t launch_layernorm(const LayerDesc& L, const float* pre, const int32_t* tok,

@@ -38,6 +38,19 @@ struct WsLayout {
 };
 bool ws_layout(const LayerDesc& L, int64_t rows, WsLayout* out);
 
+// Backward (training) workspace: the hash indices, identity indices, W^T, dout^T and G^T
+// (tokens padded to a multiple of 64), dG = c dout W (fp32), the split partial sums of dW,
+// the radix-sort buffers and the partial sums of the segmented reduction.
+constexpr int kSortTile = 4096;   // keys per radix-sort block
+constexpr int kChunk = 32;        // sorted entries per segmented-reduction chunk
+struct BwLayout {
+  size_t idx_off, ident_off, wt_off, doutt_off, gt_off, dg_off, part_off;
+  size_t keys0_off, keys1_off, vals0_off, vals1_off, hist_off, head_off, tail_off, total;
+};
+// contraction ranges of dW (c dout^T G, contracted over the rows)
+int32_t backward_splits(const LayerDesc& L, int64_t rows);
+bool bw_layout(const LayerDesc& L, int64_t rows, BwLayout* out);
+
 inline bool aligned(const void* p, size_t a) {
   return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }

@@ -48,18 +48,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// One product out[m, n] = inv * (E0[tok[m], n] + sum_k A[m, k] B[n, k]) over nrows rows m and
+// N outputs n, with A's row m the concatenation of the S gathered rows E[s][idx[m, s]] (K
+// values in all, d per sub-table) and B [N, K] row-major with row stride ldb. The layer's
+// forward has N = K = ldb = ldo = D; its backward runs dense products through the same
+// kernels: a dense A is one "sub-table" read with identity indices, and E0 is null.
 struct ProjArgs {
   const void* E[NGRAM_MAX_SUBTABLES];
   uint32_t Vm1[NGRAM_MAX_SUBTABLES];  // V_{n,k} - 1: indices are clamped to their table
   const int32_t* idx;                 // [nrows, S]
-  const int32_t* tok;                 // [nrows]; outside [0, V0) -> zero row
-  const void* E0;                     // [V0, D]
-  const void* W;                      // [D, D]
-  void* out;                          // [nrows, D], the config dtype or fp32 (F32OUT)
+  const int32_t* tok;                 // [nrows]; outside [0, V0) -> zero row (E0 only)
+  const void* E0;                     // [V0, N], or null: no E_0 term, every row valid
+  const void* W;                      // B operand [N, ldb] (the stacked W in the layer)
+  void* out;                          // [nrows, ldo]: config dtype, fp32, or fp32 partials
+                                      // [splits, nrows, ldo]
   int64_t nrows;
-  int32_t D, S, d, V0;
-  float inv;                          // output factor / (S + 1)
+  int64_t ldb, ldo;                   // row strides of B and of the output, in elements
+  int32_t K, N, S, d, V0;
+  float inv;                          // output factor / (S + 1), or the product's factor
   int32_t tiles_m, tiles_n;
+  int32_t splits;                     // contraction ranges (partial-sum output only)
+};
+
+// Output modes of the matrix-core kernel.
+enum OutMode {
+  kOutBf16 = 0,     // inv * (acc + E_0 row), rounded once to bf16 (the layer's output)
+  kOutF32 = 1,      // the same value unrounded, fp32 (layer-norm input; dense products)
+  kOutPartial = 2   // acc of this block's contraction range, fp32, no E_0 and no factor
 };
 
 // ------------------------------------------------------------------ bf16 matrix-core path
@@ -100,8 +115,7 @@ __device__ __forceinline__ void wait_loads_and_meet() {
 // 32x32 matrix-core tiles.
 template <int BM> struct WaveGrid { static constexpr int WGM = BM >= 128 ? 4 : 2; };
 
-// F32OUT: write the unrounded fp32 rows (input of the layer normalisation) instead of bf16.
-template <int BM, bool F32OUT>
+template <int BM, int OM>
 __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   constexpr int NST = Stages<BM>::value;
   constexpr int WGM = WaveGrid<BM>::WGM;
@@ -128,11 +142,14 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   //    of virtual tiles and walk a range GM row tiles at a time, outputs slowest, so the
   //    32 blocks resident on an XCD share 4 tiles of gathered rows and 8 panels of W in
   //    its L2 (the best of the 2..32 row-tile groups measured).
-  const int nb = a.tiles_m * a.tiles_n;
+  //    The contraction ranges of one tile (partial-sum output) take consecutive numbers.
+  const int nb = a.tiles_m * a.tiles_n * (OM == kOutPartial ? a.splits : 1);
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int per = nb >> 3, rem = nb & 7;
-  const int v = xcd * per + (xcd < rem ? xcd : rem) + local;
+  const int vb = xcd * per + (xcd < rem ? xcd : rem) + local;
+  const int split = OM == kOutPartial ? vb % a.splits : 0;
+  const int v = OM == kOutPartial ? vb / a.splits : vb;
   constexpr int GM = 4;
   const int group = v / (GM * a.tiles_n);
   const int first_m = group * GM;
@@ -163,9 +180,12 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)lds));
   const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E);
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
-  const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.D + pchunk * 8;
+  const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.ldb + pchunk * 8;
   const uint16_t* ap[QA];
-  const int KT = a.D / kBK;      // slices
+  const int KT_ALL = a.K / kBK;  // slices of the whole contraction
+  // this block's slice range (all of it unless the contraction is split)
+  const int kt_lo = OM == kOutPartial ? int(int64_t(split) * KT_ALL / a.splits) : 0;
+  const int kt_hi = OM == kOutPartial ? int(int64_t(split + 1) * KT_ALL / a.splits) : KT_ALL;
   const int kps = a.d / kBK;     // slices per sub-table
   int s_cur = -1;
 
@@ -173,8 +193,8 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   uint32_t f_sb = 0;
   int f_koff = 0, f_kt = 0;
   auto prep = [&](int kt) __attribute__((always_inline)) {
-    if (kt == (s_cur + 1) * kps) {          // first slice of the next sub-table
-      ++s_cur;
+    if (kt == kt_lo || kt == (s_cur + 1) * kps) {   // first slice of the range or of a table
+      s_cur = kt / kps;
 #pragma unroll
       for (int q = 0; q < QA; ++q) {
         const int r = w * (BM / 8) + q * 8 + prow;
@@ -182,7 +202,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
         ap[q] = E[s_cur] + int64_t(id) * a.d + pchunk * 8;
       }
     }
-    f_sb = lds0 + uint32_t(kt % NST) * STAGE;
+    f_sb = lds0 + uint32_t((kt - kt_lo) % NST) * STAGE;
     f_koff = (kt - s_cur * kps) * kBK;
     f_kt = kt;
   };
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     if (q < QA)
       dma16(ap[q] + f_koff, f_sb + w * (BM * 16) + q * 1024);
     else
-      dma16(bp + int64_t((q - QA) * 8) * a.D + f_kt * kBK,
+      dma16(bp + int64_t((q - QA) * 8) * a.ldb + f_kt * kBK,
             f_sb + A_BYTES + w * 4096 + (q - QA) * 1024);
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -254,16 +274,17 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     }
   };
 
-  for (int p = 0; p < NST - 1 && p < KT; ++p) issue(p);
-  for (int kt = 0; kt < KT; ++kt) {
-    // own loads of slice kt done (later slices may stay in flight), then all waves meet:
-    // slice kt is complete in LDS and every wave is past slice kt-1, whose buffer the
-    // load of slice kt+NST-1 reuses.
-    if (NST == 3 && kt + 1 < KT) wait_loads_and_meet<PER_SLICE>();
+  const int NK = kt_hi - kt_lo;  // slices of this block
+  for (int p = 0; p < NST - 1 && p < NK; ++p) issue(kt_lo + p);
+  for (int k = 0; k < NK; ++k) {
+    // own loads of slice k done (later slices may stay in flight), then all waves meet:
+    // slice k is complete in LDS and every wave is past slice k-1, whose buffer the
+    // load of slice k+NST-1 reuses.
+    if (NST == 3 && k + 1 < NK) wait_loads_and_meet<PER_SLICE>();
     else wait_loads_and_meet<0>();
-    const bool loads = kt + NST - 1 < KT;
-    if (loads) prep(kt + NST - 1);
-    const char* sp = lds + (kt % NST) * STAGE;
+    const bool loads = k + NST - 1 < NK;
+    if (loads) prep(kt_lo + k + NST - 1);
+    const char* sp = lds + (k % NST) * STAGE;
     frags(sp, 0, 0);
     frags(sp, 1, 1);
     mma(0, loads, 0);
@@ -303,18 +324,32 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     constexpr int NIT = 32 / RPI;
     const int64_t mrow = m0 + wm * WM + i * 32 + er;
     const int n = n0 + wn * WN + ec * 4;
+    if constexpr (OM == kOutPartial) {
+      float* pp = static_cast<float*>(a.out) + int64_t(split) * a.nrows * a.ldo;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int64_t m = mrow + it * RPI;
+        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
+                                                             ec * 16);
+        if (m < a.nrows) *reinterpret_cast<f32x4_t*>(pp + m * a.ldo + n) = y;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      continue;
+    }
+    // without E_0 (dense products) every row is valid and nothing is added
+    const bool has_e0 = a.E0 != nullptr;
     int32_t tk[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int64_t m = mrow + it * RPI;
-      tk[it] = m < a.nrows ? a.tok[m] : -1;
+      tk[it] = m < a.nrows ? (has_e0 ? a.tok[m] : 0) : -1;
     }
     u32x2_t ev[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       ev[it] = u32x2_t{0u, 0u};
-      if (uint32_t(tk[it]) < uint32_t(a.V0))
-        ev[it] = *reinterpret_cast<const u32x2_t*>(E0 + int64_t(tk[it]) * a.D + n);
+      if (has_e0 && uint32_t(tk[it]) < uint32_t(a.V0))
+        ev[it] = *reinterpret_cast<const u32x2_t*>(E0 + int64_t(tk[it]) * a.N + n);
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -322,21 +357,21 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
       const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
                                                            ec * 16);
       if (m < a.nrows) {
-        const bool ok = uint32_t(tk[it]) < uint32_t(a.V0);
+        const bool ok = !has_e0 || uint32_t(tk[it]) < uint32_t(a.V0);
         const float y0 = (y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv;
         const float y1 = (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv;
         const float y2 = (y[2] + bf16_to_f32(ev[it].y & 0xffffu)) * a.inv;
         const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
-        if constexpr (F32OUT) {
+        if constexpr (OM == kOutF32) {
           const f32x4_t res = ok ? f32x4_t{y0, y1, y2, y3} : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + m * a.D + n) = res;
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + m * a.ldo + n) = res;
         } else {
           u32x2_t res = {0u, 0u};
           if (ok) {
             res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
             res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
           }
-          __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + m * a.D + n));
+          __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + m * a.ldo + n));
         }
       }
     }
@@ -375,21 +410,21 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
   const T* __restrict__ W = static_cast<const T*>(a.W);
   float acc[4][4] = {};
   __syncthreads();
-  for (int k0 = 0; k0 < a.D; k0 += 16) {
+  for (int k0 = 0; k0 < a.K; k0 += 16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int lin = t + 256 * e, r = lin >> 4, kk = lin & 15;
       const int k = k0 + kk;
       const int64_t m = m0 + r;
       float v = 0.f;
-      if (m < a.nrows && k < a.D) {
+      if (m < a.nrows && k < a.K) {
         const int s = k / a.d, c = k - s * a.d;
         const uint32_t id = min(uint32_t(a.idx[m * a.S + s]), Vtab[s]);
         v = ld<T>(Etab[s] + int64_t(id) * a.d + c);
       }
       As[kk][r] = v;
       const int n = n0 + r;
-      Bs[kk][r] = (n < a.D && k < a.D) ? ld<T>(W + int64_t(n) * a.D + k) : 0.f;
+      Bs[kk][r] = (n < a.N && k < a.K) ? ld<T>(W + int64_t(n) * a.ldb + k) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -406,14 +441,16 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + ty + 16 * i;
     if (m >= a.nrows) continue;
-    const int32_t tk = a.tok[m];
-    const bool ok = uint32_t(tk) < uint32_t(a.V0);
+    const bool has_e0 = a.E0 != nullptr;        // without E_0 every row is valid
+    const int32_t tk = has_e0 ? a.tok[m] : 0;
+    const bool ok = !has_e0 || uint32_t(tk) < uint32_t(a.V0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx + 16 * j;
-      if (n >= a.D) continue;
-      const float y = ok ? (acc[i][j] + ld<T>(E0 + int64_t(tk) * a.D + n)) * a.inv : 0.f;
-      st<TO>(out + m * a.D + n, y);
+      if (n >= a.N) continue;
+      const float e0 = has_e0 && ok ? ld<T>(E0 + int64_t(tk) * a.N + n) : 0.f;
+      const float y = ok ? (acc[i][j] + e0) * a.inv : 0.f;
+      st<TO>(out + m * a.ldo + n, y);
     }
   }
 }
@@ -436,37 +473,133 @@ __global__ __launch_bounds__(256) void e0_lookup_kernel(const ProjArgs a, int32_
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void e0_scaled_kernel(const ProjArgs a) {
   const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (item >= a.nrows * a.D) return;
-  const int64_t r = item / a.D;
+  if (item >= a.nrows * a.N) return;
+  const int64_t r = item / a.N;
   const int32_t tk = a.tok[r];
   float v = 0.f;
   if (uint32_t(tk) < uint32_t(a.V0))
-    v = ld<T>(static_cast<const T*>(a.E0) + int64_t(tk) * a.D + (item - r * a.D)) * a.inv;
+    v = ld<T>(static_cast<const T*>(a.E0) + int64_t(tk) * a.N + (item - r * a.N)) * a.inv;
   st<TO>(static_cast<TO*>(a.out) + item, v);
 }
 
-template <int BM, bool F32OUT>
-hipError_t run_mfma(ProjArgs a, int64_t nrows, int32_t S, int32_t D, int esz,
-                    hipStream_t st) {
-  // at most 2^20 row tiles per launch keeps the tile numbering in 32-bit ints
+// out[m, n] += f * sum_s part[s, m, n]: the split partial sums added in split order (the
+// same order every run), 4 outputs per thread.
+__global__ __launch_bounds__(256) void accum_partials_kernel(const float* __restrict__ part,
+                                                             int32_t splits, int64_t M,
+                                                             int64_t ldo, int32_t N, float f,
+                                                             float* __restrict__ out) {
+  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;   // group of 4 outputs
+  const int64_t per_row = N / 4;
+  if (q >= M * per_row) return;
+  const int64_t m = q / per_row;
+  const int64_t off = m * ldo + (q - m * per_row) * 4;
+  f32x4_t y = *reinterpret_cast<const f32x4_t*>(part + off);
+  for (int s = 1; s < splits; ++s)
+    y += *reinterpret_cast<const f32x4_t*>(part + int64_t(s) * M * ldo + off);
+  f32x4_t* o = reinterpret_cast<f32x4_t*>(out + off);
+  *o = *o + y * f;
+}
+
+template <int BM, int OM>
+hipError_t run_mfma(ProjArgs a, int64_t nrows, int osz, hipStream_t st) {
+  // at most 2^20 row tiles per launch keeps the tile numbering in 32-bit ints (partial sums
+  // are laid out per launch, so they take one launch)
   const int64_t chunk = int64_t(BM) << 20;
+  if (OM == kOutPartial && nrows > chunk) return hipErrorInvalidValue;
   const int32_t* idx = a.idx;
   const int32_t* tok = a.tok;
   char* out = static_cast<char*>(a.out);
   for (int64_t r0 = 0; r0 < nrows; r0 += chunk) {
     const int64_t n = nrows - r0 < chunk ? nrows - r0 : chunk;
-    a.idx = idx + r0 * S;
-    a.tok = tok + r0;
-    a.out = out + r0 * D * esz;
+    a.idx = idx + r0 * a.S;
+    a.tok = tok ? tok + r0 : nullptr;
+    a.out = out + r0 * a.ldo * osz;
     a.nrows = n;
     a.tiles_m = int32_t((n + BM - 1) / BM);
-    a.tiles_n = D / kBN;
-    hipLaunchKernelGGL((proj_mfma_kernel<BM, F32OUT>), dim3(unsigned(a.tiles_m * a.tiles_n)),
-                       dim3(512), 0, st, a);
+    a.tiles_n = a.N / kBN;
+    const int64_t blocks = int64_t(a.tiles_m) * a.tiles_n * (OM == kOutPartial ? a.splits : 1);
+    hipLaunchKernelGGL((proj_mfma_kernel<BM, OM>), dim3(unsigned(blocks)), dim3(512), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Runs the product `a` describes (E/idx/S/d, K, N, ldb, ldo, E0/tok, inv) over nrows rows.
+// om: kOutBf16 (config dtype), kOutF32, or kOutPartial (a.splits ranges, matrix cores only).
+hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStream_t st) {
+  const int osz = om == kOutBf16 ? (dtype == NGRAM_F32 ? 4 : 2) : 4;
+  if (dtype == NGRAM_BF16 && a.N % kBN == 0 && a.d % kBK == 0 && a.K % kBK == 0) {
+    // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
+    // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
+    // rows' hash indices in LDS, BM * S <= kIdxBytes / 4.
+    const int64_t tiles_n = a.N / kBN;
+    const int64_t idx_cap = kIdxBytes / 4;
+    const int64_t sp = om == kOutPartial ? a.splits : 1;
+    const bool big = ((nrows + 255) / 256) * tiles_n * sp >= 512 && 256 * a.S <= idx_cap;
+    const bool mid = ((nrows + 127) / 128) * tiles_n * sp >= 256 && 128 * a.S <= idx_cap;
+    if (om == kOutPartial) {
+      if (big || 128 * a.S > idx_cap) return run_mfma<256, kOutPartial>(a, nrows, osz, st);
+      if (mid) return run_mfma<128, kOutPartial>(a, nrows, osz, st);
+      return run_mfma<64, kOutPartial>(a, nrows, osz, st);
+    }
+    if (om == kOutF32) {
+      if (big) return run_mfma<256, kOutF32>(a, nrows, osz, st);
+      if (mid) return run_mfma<128, kOutF32>(a, nrows, osz, st);
+      return run_mfma<64, kOutF32>(a, nrows, osz, st);
+    }
+    if (big) return run_mfma<256, kOutBf16>(a, nrows, osz, st);
+    if (mid) return run_mfma<128, kOutBf16>(a, nrows, osz, st);
+    return run_mfma<64, kOutBf16>(a, nrows, osz, st);
+  }
+  if (om == kOutPartial) return hipErrorInvalidValue;   // callers use kOutF32 here
+  const unsigned gy = unsigned((a.N + 63) / 64);
+  const int32_t* idx = a.idx;
+  const int32_t* tok = a.tok;
+  char* out = static_cast<char*>(a.out);
+  for (int64_t r0 = 0; r0 < nrows; r0 += (int64_t(1) << 30)) {
+    ProjArgs b = a;
+    const int64_t n = nrows - r0 < (int64_t(1) << 30) ? nrows - r0 : (int64_t(1) << 30);
+    b.idx = idx + r0 * a.S;
+    b.tok = tok ? tok + r0 : nullptr;
+    b.out = out + r0 * a.ldo * osz;
+    b.nrows = n;
+    const dim3 grid(unsigned((n + 63) / 64), gy);
+    if (dtype == NGRAM_F32)
+      hipLaunchKernelGGL((proj_generic_kernel<float, float>), grid, dim3(256), 0, st, b);
+    else if (om == kOutF32)
+      hipLaunchKernelGGL((proj_generic_kernel<uint16_t, float>), grid, dim3(256), 0, st, b);
+    else
+      hipLaunchKernelGGL((proj_generic_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// A dense product A [M, K] x B [N, K]^T as ProjArgs: A is one "sub-table" of M rows of K
+// values read through identity indices, no E_0.
+ProjArgs dense_args(const void* A, int64_t M, const void* B, int32_t N, int32_t K,
+                    const int32_t* ident, void* out, int64_t ldo, float inv) {
+  ProjArgs a{};
+  a.E[0] = A;
+  a.Vm1[0] = uint32_t(M - 1);
+  a.idx = ident;
+  a.tok = nullptr;
+  a.E0 = nullptr;
+  a.W = B;
+  a.out = out;
+  a.nrows = M;
+  a.ldb = K;
+  a.ldo = ldo;
+  a.K = K;
+  a.N = N;
+  a.S = 1;
+  a.d = K;
+  a.V0 = 0;
+  a.inv = inv;
+  a.splits = 1;
+  return a;
 }
 
 }  // namespace
@@ -486,11 +619,15 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
   a.W = W;
   a.out = out;
   a.nrows = nrows;
-  a.D = L.D;
+  a.K = L.D;
+  a.N = L.D;
+  a.ldb = L.D;
+  a.ldo = L.D;
   a.S = L.S;
   a.d = L.d;
   a.V0 = L.V0;
   a.inv = L.scale / float(L.S + 1);
+  a.splits = 1;
   const int osz = f32out ? 4 : L.esz;   // bytes per output element
   if (L.S == 0) {
     if (!f32out && L.scale == 1.0f) {
@@ -519,42 +656,34 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
     }
     return hipSuccess;
   }
-  if (L.dtype == NGRAM_BF16 && L.D % kBN == 0 && L.d % kBK == 0) {
-    // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
-    // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
-    // rows' hash indices in LDS, BM * S <= kIdxBytes / 4.
-    const int64_t tiles_n = L.D / kBN;
-    const int64_t idx_cap = kIdxBytes / 4;
-    const bool big = ((nrows + 255) / 256) * tiles_n >= 512 && 256 * L.S <= idx_cap;
-    const bool mid = ((nrows + 127) / 128) * tiles_n >= 256 && 128 * L.S <= idx_cap;
-    if (f32out) {
-      if (big) return run_mfma<256, true>(a, nrows, L.S, L.D, osz, st);
-      if (mid) return run_mfma<128, true>(a, nrows, L.S, L.D, osz, st);
-      return run_mfma<64, true>(a, nrows, L.S, L.D, osz, st);
-    }
-    if (big) return run_mfma<256, false>(a, nrows, L.S, L.D, osz, st);
-    if (mid) return run_mfma<128, false>(a, nrows, L.S, L.D, osz, st);
-    return run_mfma<64, false>(a, nrows, L.S, L.D, osz, st);
+  return run_product(a, L.dtype, f32out ? kOutF32 : kOutBf16, nrows, st);
+}
+
+hipError_t launch_dense_product(const LayerDesc& L, const void* A, int64_t M, const void* B,
+                                int32_t N, int32_t K, const int32_t* ident, float* out,
+                                int64_t ldo, float inv, bool accumulate, float* part,
+                                int32_t splits, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!accumulate)
+    return run_product(dense_args(A, M, B, N, K, ident, out, ldo, inv), L.dtype, kOutF32, M, st);
+  // accumulate: partial sums into `part`, then out += inv * (their sum in split order)
+  const bool mfma = L.dtype == NGRAM_BF16 && N % kBN == 0 && K % kBK == 0;
+  hipError_t e;
+  float f = inv;
+  if (mfma) {
+    ProjArgs a = dense_args(A, M, B, N, K, ident, part, ldo, 1.0f);
+    a.splits = splits < 1 ? 1 : splits;
+    e = run_product(a, L.dtype, kOutPartial, M, st);
+  } else {
+    splits = 1;
+    e = run_product(dense_args(A, M, B, N, K, ident, part, ldo, inv), L.dtype, kOutF32, M, st);
+    f = 1.0f;
   }
-  const unsigned gy = unsigned((L.D + 63) / 64);
-  for (int64_t r0 = 0; r0 < nrows; r0 += (int64_t(1) << 30)) {
-    ProjArgs b = a;
-    const int64_t n = nrows - r0 < (int64_t(1) << 30) ? nrows - r0 : (int64_t(1) << 30);
-    b.idx = idx + r0 * L.S;
-    b.tok = tok + r0;
-    b.out = static_cast<char*>(out) + r0 * L.D * osz;
-    b.nrows = n;
-    const dim3 grid(unsigned((n + 63) / 64), gy);
-    if (L.dtype == NGRAM_F32)
-      hipLaunchKernelGGL((proj_generic_kernel<float, float>), grid, dim3(256), 0, st, b);
-    else if (f32out)
-      hipLaunchKernelGGL((proj_generic_kernel<uint16_t, float>), grid, dim3(256), 0, st, b);
-    else
-      hipLaunchKernelGGL((proj_generic_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, b);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (e != hipSuccess) return e;
+  const int64_t groups = M * (N / 4);
+  hipLaunchKernelGGL(accum_partials_kernel, dim3(unsigned((groups + 255) / 256)), dim3(256), 0,
+                     st, part, mfma ? splits : 1, M, ldo, N, f, out);
+  return hipGetLastError();
 }
 
 }  // namespace ngram

@@ -72,4 +72,48 @@ bool ws_layout(const LayerDesc& L, int64_t rows, WsLayout* out) {
   return true;
 }
 
+int32_t backward_splits(const LayerDesc& L, int64_t rows) {
+  // the matrix-core path only (bf16, whole 256-wide output tiles): about four waves of
+  // blocks over the 256 CUs, at most 8 ranges and at least 4 slices per range
+  if (L.dtype != NGRAM_BF16 || L.D % 256 != 0 || rows <= 0) return 1;
+  const int64_t tiles = int64_t(L.D / 256) * (L.D / 256);
+  const int64_t slices = (rows + 63) / 64;
+  int64_t sp = (1024 + tiles / 2) / tiles;
+  const int64_t cap = slices / 4 < 8 ? slices / 4 : 8;
+  if (sp > cap) sp = cap;
+  return sp < 1 ? 1 : int32_t(sp);
+}
+
+bool bw_layout(const LayerDesc& L, int64_t rows, BwLayout* out) {
+  if (rows < 0) return false;
+  const size_t T = size_t(rows), D = size_t(L.D), S = size_t(L.S), esz = size_t(L.esz);
+  const size_t Tp = (T + 63) / 64 * 64;
+  const size_t nsort = T * (S > 1 ? S : 1);
+  const size_t nblocks = (nsort + kSortTile - 1) / kSortTile;
+  const size_t seg_s = (T * S + kChunk - 1) / kChunk * size_t(L.d);
+  const size_t seg_0 = (T + kChunk - 1) / kChunk * D;
+  const size_t seg = seg_s > seg_0 ? seg_s : seg_0;
+  const bool tables = S > 0;
+  BwLayout w;
+  size_t o = 256;                                    // error flags
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  w.idx_off = take(T * S * 4);
+  w.ident_off = take((T > D ? T : D) * 4);
+  w.wt_off = take(tables ? D * D * esz : 0);
+  w.doutt_off = take(tables ? D * Tp * esz : 0);
+  w.gt_off = take(tables ? D * Tp * esz : 0);
+  w.dg_off = take(tables ? T * D * 4 : 0);
+  w.part_off = take(tables ? size_t(backward_splits(L, rows)) * D * D * 4 : 0);
+  w.keys0_off = take(nsort * 8);
+  w.keys1_off = take(nsort * 8);
+  w.vals0_off = take(nsort * 4);
+  w.vals1_off = take(nsort * 4);
+  w.hist_off = take(256 * (nblocks > 0 ? nblocks : 1) * 4);
+  w.head_off = take(seg * 4);
+  w.tail_off = take(seg * 4);
+  w.total = o;
+  *out = w;
+  return true;
+}
+
 }  // namespace ngram

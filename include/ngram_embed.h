@@ -200,6 +200,30 @@ int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
                        const int32_t* new_tokens, const int32_t* n_accept, int32_t tmax,
                        int32_t* err_flags, void* stream);
 
+/* ---------------------------------------------------------------- backward (training)
+ * Gradients of the layer for one batch, given the upstream gradient dout = dL/dout
+ * (device [ntok, D], config dtype, 16-byte aligned) of out = ngram_embed_prefill(tokens).
+ * The pages train the layer from scratch but state no backward; these are the plain
+ * derivatives of the final form (section A2), with c = amp_scale / ((N-1)K + 1) for
+ * NGRAM_AMP_SCALE and 1 / ((N-1)K + 1) otherwise:
+ *   dE0[t, :]  += c * sum of dout[i, :] over positions i with token t
+ *   dW         += c * dout^T G,  G[i, s*d + j] = E_{n,k}[h_{i,s}, j]  (W's stacked layout)
+ *   dE[s][r, :] += c * sum over positions i with h_{i,s} = r of (dout W)[i, s*d : (s+1)*d]
+ * All gradient buffers are caller-owned fp32 device memory, accumulated into (zero them to
+ * start a step): dE0 [V0, D], dE = host array of S device pointers to [V_{n,k}, d], dW
+ * [D, D]; any of them may be NULL to skip it. Positions whose token is outside [0, V0)
+ * contribute nothing (their forward rows are zero). The result does not depend on thread
+ * timing: repeated ids are summed in position order (sort + segmented sums, no atomics).
+ * NGRAM_AMP_LAYERNORM is not differentiated here (NGRAM_EINVAL). tokens/cu_seqlens/nseq as
+ * in ngram_embed_prefill; ntok * max(S, 1) < 2^31. ws: at least
+ * ngram_embed_backward_workspace_size(cfg, ntok) bytes, 256-byte aligned, flags at offset 0
+ * as for the forward workspace (bad ids set NGRAM_FLAG_BAD_TOKEN). */
+size_t ngram_embed_backward_workspace_size(const ngram_embed_config* cfg, int64_t ntok);
+int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                         const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
+                         int64_t ntok, const void* dout, float* dE0, float* const* dE,
+                         float* dW, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- errors
  * Wait for `stream`, then copy the workspace's error flags to *flags (host). */
 int ngram_embed_read_error_flag(const void* ws, int32_t* flags, void* stream);

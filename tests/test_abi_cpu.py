@@ -35,9 +35,10 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ngram_embed_prefill", "ngram_embed_decode", "ngram_embed_hash",
               "ngram_embed_gather", "ngram_embed_project", "ngram_cache_init",
-              "ngram_cache_commit"):
+              "ngram_cache_commit", "ngram_embed_backward",
+              "ngram_embed_backward_workspace_size"):
         assert n in names
-    assert len(names) == 12
+    assert len(names) == 14
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -194,6 +195,36 @@ def test_amplification_checks(lib):
         Tb = g._CTables(FAKE, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), FAKE, wt, bs)
         assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need,
                                        0) == -3
+
+
+def test_backward_argument_checks(lib):
+    """Backward: its workspace grows with the batch, layer normalisation is refused, and
+    bad workspaces, sizes and pointers are rejected before any launch."""
+    P = ctypes.byref
+    cfg = tiny_cfg()
+    n1, n2 = g.ngram_embed_backward_workspace_size(cfg, 100), \
+        g.ngram_embed_backward_workspace_size(cfg, 1000)
+    assert 0 < n1 < n2 and n1 % 256 == 0 and n2 % 256 == 0
+    assert g.ngram_embed_backward_workspace_size(tiny_cfg(amp="layernorm"), 100) == 0
+    assert g.ngram_embed_backward_workspace_size(cfg, -1) == 0
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    ws = g.ngram_embed_backward_workspace_size(cfg, 16)
+    bw = lib.ngram_embed_backward
+    assert bw(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE, None, FAKE, FAKE, ws - 1, 0) == -4
+    assert bw(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE, None, FAKE, FAKE + 64, ws, 0) == -4
+    assert bw(P(c), P(T), FAKE, FAKE, 1, -1, FAKE, FAKE, None, FAKE, FAKE, ws, 0) == -1
+    assert bw(P(c), P(T), FAKE, FAKE, 0, 16, FAKE, FAKE, None, FAKE, FAKE, ws, 0) == -1
+    assert bw(P(c), P(T), FAKE, FAKE, 1, 16, FAKE + 8, FAKE, None, FAKE, FAKE, ws, 0) == -3
+    assert bw(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE + 4, None, FAKE, FAKE, ws, 0) == -3
+    assert bw(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, None, None, FAKE + 4, FAKE, ws, 0) == -3
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE + 4, FAKE)
+    assert bw(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, None, arr, None, FAKE, ws, 0) == -3
+    assert bw(P(c), None, FAKE, FAKE, 1, 16, FAKE, None, None, None, FAKE, ws, 0) == -3
+    cl, keep3 = tiny_cfg(amp="layernorm")._c()
+    assert bw(P(cl), P(T), FAKE, FAKE, 1, 16, FAKE, None, None, None, FAKE, ws, 0) == -1
+    # an empty batch succeeds without touching the device
+    assert bw(P(c), P(T), FAKE, FAKE, 0, 0, FAKE, FAKE, None, FAKE, FAKE, ws, 0) == 0
 
 
 def test_zero_sized_calls_enqueue_nothing(lib):

@@ -1,0 +1,171 @@
+"""GPU parity of the backward (training gradients), through the C ABI, against
+oracle.backward on the same seeded inputs.
+
+The inputs (tables, W, upstream gradient) are exact in the config dtype, so the only error is
+fp32 accumulation: about u * sqrt(n) relative for n summed terms (u = 2^-24). Bounds: relative
+L2 <= 1e-5 for the small cases (n up to a few thousand), <= 1e-4 at the 64K-token batch.
+Small cases compare every gradient entry; repeated ids and hash indices are forced with small
+vocabularies and tables. Also: bitwise-repeatable results (no atomics), accumulation into the
+buffers, N = 1, the sqrt(D) factor, and the 30B-parameter layer at its 64K-token shape
+(sampled rows of every gradient)."""
+import numpy as np
+import pytest
+
+import gram_embedding_layer_amd as g
+import oracle
+import workloads as WL
+from tests.gpu_helpers import device_fetch, packed, rel_l2, to_f64, w_blocks
+from tests.test_gpu_prefill import dev, host_to_dev_tables, small_workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def grad_buffers(w, dtype=torch.float32):
+    dE0 = torch.zeros((w.V0, w.D), dtype=dtype, device="cuda")
+    dE = [torch.zeros((v, w.d), dtype=dtype, device="cuda") for v in w.V]
+    dW = torch.zeros((w.D, w.D), dtype=dtype, device="cuda")
+    return dE0, dE, dW
+
+
+def upstream(w, T, seed):
+    rng = np.random.default_rng(seed)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    return torch.as_tensor(rng.normal(0.0, 1.0, size=(T, w.D))).to(dt).cuda()
+
+
+def run_backward(cfg, tables, tokens, cu, dout, bufs):
+    ws = g.alloc_backward_workspace(cfg, len(tokens))
+    dE0, dE, dW = bufs
+    g.ngram_embed_backward(cfg, tables, dev(tokens), dev(cu), dout, dE0, dE, dW, ws)
+    torch.cuda.synchronize()
+    return ws
+
+
+def check(name, got, want, tol):
+    r = rel_l2(to_f64(got), want)
+    print(f"  {name}: rel_l2={r:.3e}", flush=True)
+    assert np.all(np.isfinite(to_f64(got)))
+    assert r <= tol, (name, r)
+
+
+CASES = [
+    ("f32_generic", WL.workload("tiny_f32"), None, None),
+    ("bf16_dup_d256", small_workload("bf16", D=256, N=3, K=2, V0=50), (300, 1, 0, 77, 1000), None),
+    ("bf16_d1024", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (3000, 2100, 5), None),
+    ("bf16_n5k4_d2048", small_workload("bf16", D=2048, N=5, K=4, V0=131072), (700, 60), None),
+    ("bf16_scaled", small_workload("bf16", D=768, N=4, K=2, V0=300), (500, 400), "scale"),
+    ("f32_n1", small_workload("f32", D=64, N=1, K=1), (40, 9), None),
+    ("bf16_n1", small_workload("bf16", D=256, N=1, K=1, V0=20), (400, 9), None),
+]
+
+
+@pytest.mark.parametrize("name,w,lengths,amp", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(lib, name, w, lengths, amp):
+    E0, E, W = host_to_dev_tables(w)
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V), amp=amp or "none")
+    if lengths is None:
+        seqs = list(WL.token_batch(w))
+    else:
+        rng = np.random.default_rng(len(name))
+        seqs = [rng.integers(0, w.V0, size=L).astype(np.int32) for L in lengths]
+    tokens, cu = packed(seqs)
+    T = len(tokens)
+    dout = upstream(w, T, 17)
+    bufs = grad_buffers(w)
+    ws = run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, bufs)
+    assert g.ngram_embed_read_error_flag(ws) == 0
+    idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
+    scale = np.sqrt(w.D) if amp == "scale" else 1.0
+    dE0_r, dE_r, dW_r = oracle.backward(w.D, w.N, w.K, tokens, idx, to_f64(dout),
+                                         device_fetch(E0, E), w_blocks(W, w.S), w.V0, w.V,
+                                         scale)
+    dE0, dE, dW = bufs
+    check(f"{name} dE0", dE0, dE0_r, 1e-5)
+    for s in range(w.S):
+        check(f"{name} dE[{s}]", dE[s], dE_r[s], 1e-5)
+    if w.S:
+        dW_ref = np.concatenate(dW_r, axis=1)          # the stacked layout [D, S*d]
+        check(f"{name} dW", dW, dW_ref, 1e-5)
+
+
+def test_backward_is_repeatable_and_accumulates(lib):
+    w = small_workload("bf16", D=256, N=3, K=2, V0=50)
+    E0, E, W = host_to_dev_tables(w)
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    rng = np.random.default_rng(4)
+    tokens, cu = packed([rng.integers(0, w.V0, size=L).astype(np.int32) for L in (900, 130)])
+    dout = upstream(w, len(tokens), 5)
+    a, b = grad_buffers(w), grad_buffers(w)
+    run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, a)
+    run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, b)
+    for x, y in zip([a[0], a[2]] + a[1], [b[0], b[2]] + b[1]):
+        assert torch.equal(x, y)                        # no atomics: same bits every run
+    run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, b)
+    for x, y in zip([a[0], a[2]] + a[1], [b[0], b[2]] + b[1]):
+        assert torch.equal(2 * x, y)                    # accumulated: x + x, exactly
+
+
+def test_backward_skips_only_requested_buffers(lib):
+    w = small_workload("bf16", D=256, N=3, K=2, V0=50)
+    E0, E, W = host_to_dev_tables(w)
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    rng = np.random.default_rng(6)
+    tokens, cu = packed([rng.integers(0, w.V0, size=600).astype(np.int32)])
+    dout = upstream(w, len(tokens), 7)
+    full = grad_buffers(w)
+    run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, full)
+    dE0, dE, dW = grad_buffers(w)
+    ws = g.alloc_backward_workspace(cfg, len(tokens))
+    g.ngram_embed_backward(cfg, g.Tables(E0, E, W), dev(tokens), dev(cu), dout, None, dE, None, ws)
+    g.ngram_embed_backward(cfg, g.Tables(E0, E, W), dev(tokens), dev(cu), dout, dE0, None, dW, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dE0, full[0]) and torch.equal(dW, full[2])
+    for x, y in zip(dE, full[1]):
+        assert torch.equal(x, y)
+
+
+def test_backward_30b_sampled(lib, tables_30b):
+    """The 30B-parameter layer at its 64K-token shape: 16 rows of dW, the 20 most frequent
+    and 20 random present tokens of dE0, and 8 rows of each sub-table's gradient (among the
+    most and least hit), against the oracle's sums written out for those rows."""
+    w = WL.workload("prefill_64k_30b")
+    E0, E, W = tables_30b
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    tokens, cu = packed(list(WL.token_batch(w)))
+    T = len(tokens)
+    dout = upstream(w, T, 23)
+    bufs = grad_buffers(w)
+    print(f"  backward of {T} tokens: gradient buffers {sum(b.numel() for b in bufs[1]) * 4 / 1e9:.0f} GB",
+          flush=True)
+    ws = run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, bufs)
+    assert g.ngram_embed_read_error_flag(ws) == 0
+    dE0, dE, dW = bufs
+    c = 1.0 / (w.S + 1)
+    D64 = to_f64(dout)
+    rng = np.random.default_rng(3)
+    # dW rows: c * sum_i dout[i, o] * G[i, :]
+    fetch = device_fetch(E0, E)
+    idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
+    G = np.concatenate([fetch(s, idx[:, s]) for s in range(w.S)], axis=1)   # [T, D] float64
+    rows = rng.choice(w.D, 16, replace=False)
+    check("30b dW rows", dW[torch.as_tensor(rows, device="cuda")], c * (D64[:, rows].T @ G), 1e-4)
+    del G
+    # dE0 rows: c * sum of dout over the token's positions
+    uniq, counts = np.unique(tokens, return_counts=True)
+    pick = np.concatenate([uniq[np.argsort(-counts)[:20]], rng.choice(uniq, 20, replace=False)])
+    want0 = np.stack([c * D64[tokens == t].sum(axis=0) for t in pick])
+    check("30b dE0 rows", dE0[torch.as_tensor(pick.astype(np.int64), device="cuda")], want0, 1e-4)
+    # dE_s rows: c * sum over positions hashing to r of (dout W)[:, s*d:(s+1)*d]
+    W64 = to_f64(W)
+    for s in range(w.S):
+        r_uniq, r_counts = np.unique(idx[:, s], return_counts=True)
+        order = np.argsort(-r_counts)
+        pick_r = np.concatenate([r_uniq[order[:4]], r_uniq[order[-4:]]])
+        Ws = W64[:, s * w.d:(s + 1) * w.d]
+        want = np.stack([c * (D64[idx[:, s] == r] @ Ws).sum(axis=0) for r in pick_r])
+        check(f"30b dE[{s}] rows", dE[s][torch.as_tensor(pick_r.astype(np.int64), device="cuda")],
+              want, 1e-4)
+    del bufs, dE0, dE, dW, ws
+    torch.cuda.empty_cache()
