@@ -272,6 +272,7 @@ int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables
   b.hist = reinterpret_cast<uint32_t*>(w + lay.hist_off);
   b.head = reinterpret_cast<float*>(w + lay.head_off);
   b.tail = reinterpret_cast<float*>(w + lay.tail_off);
+  b.owners = reinterpret_cast<uint32_t*>(w + lay.owners_off);
   return hip_status(ngram::launch_backward(L, b, st));
 }
 

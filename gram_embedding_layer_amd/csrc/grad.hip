@@ -35,11 +35,9 @@ template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) {
 }
 
 constexpr int kTile = 64;           // transpose tile edge
+constexpr int kChunkWide = 64;      // E_0's chunk of sorted entries (kChunk: sub-tables)
 constexpr int kSortThreads = 256;
 constexpr int kSortRounds = kSortTile / kSortThreads;   // keys per thread per sort tile
-constexpr int kScanThreads = 1024;
-constexpr int kColsPerThread = 4;   // columns per thread in the reductions
-constexpr int kColGroup = 256 * kColsPerThread;
 
 __global__ __launch_bounds__(256) void iota_kernel(int32_t* p, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -72,6 +70,58 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict_
     const int64_t r = r0 + tx;
     if (c < cols && r < ldt) XT[int64_t(c) * ldt + r] = tile[tx][j];
   }
+}
+
+// 16-bit elements, 16-byte vectors: the same transposes with each thread moving 8 elements
+// per access (64 x 64 tiles; the LDS pitch of 72 elements keeps the column reads spread
+// over the banks). `src_row(r)` points at the tile's first column in source row r (null =
+// a zero row).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kPitch = kTile + 8;
+
+template <typename RowFn>
+__device__ __forceinline__ void transpose_tile16(uint16_t (*tile)[kPitch], RowFn src_row,
+                                                 int c0, uint16_t* XT, int64_t ldt, int cols,
+                                                 int64_t r0) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {                  // 512 vectors of 8 elements per tile
+    const int r = t / 8 + 32 * k, q = t % 8;
+    const uint16_t* row = src_row(r);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row != nullptr) v = *reinterpret_cast<const u32x4_t*>(row + q * 8);
+    *reinterpret_cast<u32x4_t*>(&tile[r][q * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = t / 8 + 32 * k, q = t % 8;    // output row c0 + c, tokens r0 + 8q ..
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = uint32_t(tile[q * 8 + 2 * j][c]) | (uint32_t(tile[q * 8 + 2 * j + 1][c]) << 16);
+    if (c0 + c < cols && r0 + q * 8 < ldt)
+      *reinterpret_cast<u32x4_t*>(XT + int64_t(c0 + c) * ldt + r0 + q * 8) =
+          u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// dout^T for bf16 (cols % 64 == 0, ldt % 64 == 0)
+__global__ __launch_bounds__(256) void transpose_pad16_kernel(const uint16_t* __restrict__ X,
+                                                              int64_t rows, int32_t cols,
+                                                              const int32_t* __restrict__ tok,
+                                                              int32_t V0,
+                                                              uint16_t* __restrict__ XT,
+                                                              int64_t ldt) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][kPitch];
+  const int64_t r0 = int64_t(blockIdx.x) * kTile;
+  const int c0 = blockIdx.y * kTile;
+  auto src_row = [&](int r) -> const uint16_t* {
+    const int64_t rr = r0 + r;
+    if (rr >= rows || (tok != nullptr && uint32_t(tok[rr]) >= uint32_t(V0))) return nullptr;
+    return X + rr * cols + c0;
+  };
+  transpose_tile16(tile, src_row, c0, XT, ldt, cols, r0);
 }
 
 struct GatherTArgs {
@@ -110,6 +160,22 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(const GatherTArgs
     const int64_t r = r0 + tx;
     if (c < a.D && r < a.ldt) GT[int64_t(c) * a.ldt + r] = tile[tx][j];
   }
+}
+
+// G^T for bf16 when every 64-column tile lies in one sub-table (d % 64 == 0)
+__global__ __launch_bounds__(256) void gather_transpose16_kernel(const GatherTArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][kPitch];
+  const int64_t r0 = int64_t(blockIdx.x) * kTile;
+  const int c0 = blockIdx.y * kTile;
+  const int s = c0 / a.d;
+  const uint16_t* E = static_cast<const uint16_t*>(a.E[s]);
+  auto src_row = [&](int r) -> const uint16_t* {
+    const int64_t rr = r0 + r;
+    if (rr >= a.rows || uint32_t(a.tok[rr]) >= uint32_t(a.V0)) return nullptr;
+    const uint32_t id = min(uint32_t(a.idx[rr * a.S + s]), a.Vm1[s]);
+    return E + int64_t(id) * a.d + (c0 - s * a.d);
+  };
+  transpose_tile16(tile, src_row, c0, static_cast<uint16_t*>(a.GT), a.ldt, a.D, r0);
 }
 
 // Sort inputs. E_0: key = token, value = position. Sub-tables: pair p = i*S + s has key
@@ -157,27 +223,68 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const uint64_t
   hist[int64_t(t) * gridDim.x + blockIdx.x] = h[t];
 }
 
-// In-place exclusive prefix sum of n counts, one block.
-__global__ __launch_bounds__(kScanThreads) void exclusive_scan_kernel(uint32_t* v, int64_t n) {
-  __shared__ uint32_t part[kScanThreads];
+// In-place exclusive prefix sum of the m digit-major counts hist[digit * nblocks + b], in
+// two launches over tiles of kScanTile counts: the tile totals, then each tile scanned with
+// the sum of the tiles before it (read by every block: there are few tiles).
+constexpr int kScanTile = 1024;
+
+__global__ __launch_bounds__(256) void scan_totals_kernel(const uint32_t* v, int64_t m,
+                                                          uint32_t* totals) {
+  __shared__ uint32_t part[256];
   const int t = threadIdx.x;
-  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = std::min<int64_t>(n, t * per), hi = std::min<int64_t>(n, lo + per);
-  uint32_t sum = 0;
-  for (int64_t i = lo; i < hi; ++i) sum += v[i];
-  part[t] = sum;
+  const int64_t base = int64_t(blockIdx.x) * kScanTile;
+  uint32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kScanTile / 256; ++k) {
+    const int64_t i = base + k * 256 + t;
+    if (i < m) s += v[i];
+  }
+  part[t] = s;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {     // Hillis-Steele over the sums
-    const uint32_t x = t >= off ? part[t - off] : 0u;
-    __syncthreads();
-    part[t] += x;
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) part[t] += part[t + off];
     __syncthreads();
   }
-  uint32_t run = part[t] - sum;                            // exclusive prefix of this thread
-  for (int64_t i = lo; i < hi; ++i) {
-    const uint32_t x = v[i];
-    v[i] = run;
-    run += x;
+  if (t == 0) totals[blockIdx.x] = part[0];
+}
+
+__global__ __launch_bounds__(256) void scan_apply_kernel(uint32_t* v, int64_t m,
+                                                         const uint32_t* totals) {
+  __shared__ uint32_t part[256];
+  const int t = threadIdx.x;
+  // sum of the earlier tiles
+  uint32_t before = 0;
+  for (int64_t b = t; b < blockIdx.x; b += 256) before += totals[b];
+  part[t] = before;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) part[t] += part[t + off];
+    __syncthreads();
+  }
+  const uint32_t carry = part[0];
+  __syncthreads();
+  // this tile: thread t holds 4 consecutive counts
+  constexpr int PER = kScanTile / 256;
+  const int64_t base = int64_t(blockIdx.x) * kScanTile + int64_t(t) * PER;
+  uint32_t x[PER], s = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    x[k] = base + k < m ? v[base + k] : 0u;
+    s += x[k];
+  }
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {                // inclusive scan of thread sums
+    const uint32_t y = t >= off ? part[t - off] : 0u;
+    __syncthreads();
+    part[t] += y;
+    __syncthreads();
+  }
+  uint32_t run = carry + part[t] - s;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (base + k < m) v[base + k] = run;
+    run += x[k];
   }
 }
 
@@ -231,99 +338,167 @@ struct SegArgs {
   const void* src;                   // rows summed: [rows, ld_src] (fp32 or config dtype)
   float* head;                       // [nchunks, width]: sum of the run a chunk starts in
   float* tail;                       // [nchunks, width]: sum of the run a chunk ends in
+  uint32_t* owners;                  // [1 + nchunks]: count, then chunks that own a run
+                                     // continuing past their end (any order)
   int64_t n, nchunks, ld_src;
   uint64_t sentinel;
   int32_t width;                     // gradient row width (D for E_0, d for sub-tables)
+  int32_t chunk;                     // sorted entries per chunk
   int32_t by_table;                  // 1: key = (s << 31) | r, source columns s*width...
   float factor;                      // applied to source rows (c for dout, 1 for dG)
 };
-
-template <typename T>
-__device__ __forceinline__ void run_add(const SegArgs& a, int64_t j, int col0, f32x4_t& acc) {
-  const uint64_t key = a.keys[j];
-  const int s = a.by_table ? int(key >> 31) : 0;
-  const T* row = static_cast<const T*>(a.src) + int64_t(a.vals[j]) * a.ld_src + s * a.width;
-#pragma unroll
-  for (int k = 0; k < kColsPerThread; ++k) {
-    const int c = col0 + k * 256;
-    if (c < a.width) acc[k] += ldf<T>(row + c) * a.factor;
-  }
-}
 
 __device__ __forceinline__ float* dst_row(const SegArgs& a, uint64_t key) {
   if (a.by_table) return a.dst[key >> 31] + int64_t(key & 0x7fffffffu) * a.width;
   return a.dst[0] + int64_t(key) * a.width;
 }
 
-__device__ __forceinline__ void add_row(float* row, int col0, int width, const f32x4_t& v) {
-#pragma unroll
-  for (int k = 0; k < kColsPerThread; ++k) {
-    const int c = col0 + k * 256;
-    if (c < width) row[c] += v[k];
-  }
+// 4 consecutive source values as fp32 (16 bytes of fp32, 8 bytes of bf16).
+template <typename T> __device__ __forceinline__ f32x4_t ld4(const T* p);
+template <> __device__ __forceinline__ f32x4_t ld4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <> __device__ __forceinline__ f32x4_t ld4<uint16_t>(const uint16_t* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
+  return f32x4_t{bf16_to_f32(h.x & 0xffffu), bf16_to_f32(h.x >> 16), bf16_to_f32(h.y & 0xffffu),
+                 bf16_to_f32(h.y >> 16)};
 }
 
-__device__ __forceinline__ void put_row(float* row, int col0, int width, const f32x4_t& v) {
-#pragma unroll
-  for (int k = 0; k < kColsPerThread; ++k) {
-    const int c = col0 + k * 256;
-    if (c < width) row[c] = v[k];
+// The runs are summed in vectors of 4 columns: lane v of a block of THREADS handles vectors
+// v, v + THREADS, ... (NV of them) of a gradient row, so a sub-table row (256 values) is
+// one wave and an E_0 row (3072) one 256-thread block. Blocks cover column groups of
+// THREADS * NV * 4 values (grid.y) when rows are wider.
+template <int THREADS, int NV>
+struct Cols {
+  static constexpr int kGroup = THREADS * NV * 4;
+  static __device__ __forceinline__ int col(int v) {
+    return int(blockIdx.y) * kGroup + (int(threadIdx.x) + v * THREADS) * 4;
   }
-}
+};
 
-// Level 1: block (chunk, column group) walks its kChunk entries in order. A run lying
+// Level 1: block (chunk, column group) walks its CH entries in order. A run lying
 // wholly inside the chunk is added to its gradient row here (its only owner); the run the
 // chunk starts in, if it began earlier, goes to head[chunk]; a run that begins here and
-// continues past the chunk goes to tail[chunk] for level 2.
-template <typename T>
-__global__ __launch_bounds__(256) void segsum_level1_kernel(const SegArgs a) {
+// continues past the chunk goes to tail[chunk] and the chunk joins the level-2 list. The
+// chunk's keys and positions are staged in LDS; the source rows of B entries, and the
+// gradient rows of the runs they end, are loaded before any is used.
+template <typename T, int THREADS, int NV, int CH>
+__global__ __launch_bounds__(THREADS) void segsum_level1_kernel(const SegArgs a) {
+  constexpr int B = NV >= 4 ? 2 : (NV >= 2 ? 4 : 8);
+  using C = Cols<THREADS, NV>;
+  __shared__ uint64_t skey[CH + 2];         // keys[lo - 1 .. hi] (ends valid if present)
+  __shared__ uint32_t sval[CH];
   const int64_t chunk = blockIdx.x;
-  const int col0 = blockIdx.y * kColGroup + threadIdx.x;
-  const int64_t lo = chunk * kChunk, hi = std::min<int64_t>(a.n, lo + kChunk);
-  const bool cont_in = lo > 0 && a.keys[lo - 1] == a.keys[lo];
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int t = threadIdx.x;
+  const int64_t lo = chunk * CH, hi = std::min<int64_t>(a.n, lo + CH);
+  const int cnt = int(hi - lo);
+  const bool has_prev = lo > 0, has_next = hi < a.n;
+  for (int i = t; i < cnt; i += THREADS) {
+    skey[i + 1] = a.keys[lo + i];
+    sval[i] = a.vals[lo + i];
+  }
+  if (t == 0) skey[0] = has_prev ? a.keys[lo - 1] : 0;
+  if (t == 0) skey[cnt + 1] = has_next ? a.keys[hi] : 0;
+  __syncthreads();
+  const bool cont_in = has_prev && skey[0] == skey[1];
+  f32x4_t acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool first = true;
-  for (int64_t j = lo; j < hi; ++j) {
-    const uint64_t key = a.keys[j];
-    if (key == a.sentinel) break;                  // invalid positions sort last
-    run_add<T>(a, j, col0, acc);
-    const bool run_ends_here = j + 1 >= hi || a.keys[j + 1] != key;
-    if (!run_ends_here) continue;
-    const bool cont_out = j + 1 == hi && hi < a.n && a.keys[hi] == key;
-    if (first && cont_in) {
-      put_row(a.head + chunk * a.width, col0, a.width, acc);
-    } else if (cont_out) {
-      put_row(a.tail + chunk * a.width, col0, a.width, acc);
-    } else {
-      add_row(dst_row(a, key), col0, a.width, acc);
+  for (int b0 = 0; b0 < cnt; b0 += B) {
+    f32x4_t rows[B][NV], dsts[B][NV];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int j = b0 + u;
+      const bool live = j < cnt && skey[j + 1] != a.sentinel;
+      const uint64_t key = live ? skey[j + 1] : 0;
+      const int s = a.by_table ? int(key >> 31) : 0;
+      const T* row = static_cast<const T*>(a.src) + int64_t(live ? sval[j] : 0) * a.ld_src +
+                     s * a.width;
+      const bool last = j + 1 == cnt;
+      const bool ends = live && (last ? !(has_next && skey[cnt + 1] == key) : skey[j + 2] != key);
+      const bool owned = ends && !(cont_in && key == skey[1]);   // added here, directly
+      const float* d = owned ? dst_row(a, key) : nullptr;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int c = C::col(v);
+        rows[u][v] = live && c < a.width ? ld4<T>(row + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dsts[u][v] = owned && c < a.width ? *reinterpret_cast<const f32x4_t*>(d + c)
+                                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    first = false;
-    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int j = b0 + u;
+      if (j >= cnt) break;
+      const uint64_t key = skey[j + 1];
+      if (key == a.sentinel) return;               // invalid positions sort last
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] += rows[u][v] * a.factor;
+      const bool last = j + 1 == cnt;
+      if (!last && skey[j + 2] == key) continue;   // the run goes on in this chunk
+      const bool cont_out = last && has_next && skey[cnt + 1] == key;
+      float* dst = first && cont_in ? a.head + chunk * a.width
+                   : cont_out       ? a.tail + chunk * a.width
+                                    : dst_row(a, key);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int c = C::col(v);
+        if (c < a.width)
+          *reinterpret_cast<f32x4_t*>(dst + c) =
+              (first && cont_in) || cont_out ? acc[v] : dsts[u][v] + acc[v];
+        acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if (cont_out && !(first && cont_in) && blockIdx.y == 0 && t == 0)
+        a.owners[1 + atomicAdd(a.owners, 1u)] = uint32_t(chunk);
+      first = false;
+    }
   }
 }
 
-// Level 2: a chunk whose last run starts in it and continues adds its tail and the head
-// sums of the following chunks that the run covers, in order.
-__global__ __launch_bounds__(256) void segsum_level2_kernel(const SegArgs a) {
-  const int64_t chunk = blockIdx.x;
-  const int col0 = blockIdx.y * kColGroup + threadIdx.x;
-  const int64_t lo = chunk * kChunk, hi = std::min<int64_t>(a.n, lo + kChunk);
-  if (hi >= a.n) return;
-  const uint64_t key = a.keys[hi - 1];
-  if (key == a.sentinel || a.keys[hi] != key) return;      // the last run ends here
-  if (lo > 0 && a.keys[lo - 1] == key) return;             // ... or began in an earlier chunk
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const float* tl = a.tail + chunk * a.width;
+// Level 2: each chunk listed by level 1 (its last run starts in it and continues) adds its
+// tail and the head sums of the following chunks that the run covers, in order. The run's
+// end is found by binary search first, so the sum's loads do not wait on each other. Blocks
+// stride over the list; its order does not matter (each run has one owner).
+template <int THREADS, int NV>
+__global__ __launch_bounds__(THREADS) void segsum_level2_kernel(const SegArgs a) {
+  using C = Cols<THREADS, NV>;
+  const uint32_t n_owners = a.owners[0];
+  for (uint32_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
+    const int64_t chunk = a.owners[1 + o];
+    const int64_t hi = std::min<int64_t>(a.n, chunk * a.chunk + a.chunk);
+    const uint64_t key = a.keys[hi - 1];
+    int64_t l = hi, r = a.n;                       // first index past the run in [hi, n)
+    while (l < r) {
+      const int64_t m = (l + r) / 2;
+      if (a.keys[m] == key) l = m + 1; else r = m;
+    }
+    const int64_t last_chunk = (l - 1) / a.chunk;  // chunks chunk+1 .. last_chunk hold a head
+    f32x4_t acc[NV];
+    const float* tl = a.tail + chunk * a.width;
 #pragma unroll
-  for (int k = 0; k < kColsPerThread; ++k)
-    if (col0 + k * 256 < a.width) acc[k] = tl[col0 + k * 256];
-  for (int64_t c = chunk + 1; c < a.nchunks && a.keys[c * kChunk] == key; ++c) {
-    const float* hd = a.head + c * a.width;
+    for (int v = 0; v < NV; ++v) {
+      const int c = C::col(v);
+      acc[v] = c < a.width ? *reinterpret_cast<const f32x4_t*>(tl + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll 8
+    for (int64_t ch = chunk + 1; ch <= last_chunk; ++ch) {
+      const float* hd = a.head + ch * a.width;
 #pragma unroll
-    for (int k = 0; k < kColsPerThread; ++k)
-      if (col0 + k * 256 < a.width) acc[k] += hd[col0 + k * 256];
+      for (int v = 0; v < NV; ++v) {
+        const int c = C::col(v);
+        if (c < a.width) acc[v] += *reinterpret_cast<const f32x4_t*>(hd + c);
+      }
+    }
+    float* dst = dst_row(a, key);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = C::col(v);
+      if (c < a.width)
+        *reinterpret_cast<f32x4_t*>(dst + c) = *reinterpret_cast<const f32x4_t*>(dst + c) + acc[v];
+    }
   }
-  add_row(dst_row(a, key), col0, a.width, acc);
 }
 
 int key_bits(uint64_t max_key) {
@@ -339,8 +514,11 @@ hipError_t radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1, ui
   for (int shift = 0; shift < bits; shift += 8) {
     hipLaunchKernelGGL(radix_hist_kernel, dim3(unsigned(nblocks)), dim3(kSortThreads), 0, st, k0,
                        n, shift, hist);
-    hipLaunchKernelGGL(exclusive_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, hist,
-                       256 * nblocks);
+    const int64_t m = 256 * nblocks, ntiles = (m + kScanTile - 1) / kScanTile;
+    hipLaunchKernelGGL(scan_totals_kernel, dim3(unsigned(ntiles)), dim3(256), 0, st, hist, m,
+                       hist + m);
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(unsigned(ntiles)), dim3(256), 0, st, hist, m,
+                       hist + m);
     hipLaunchKernelGGL(radix_scatter_kernel, dim3(unsigned(nblocks)), dim3(kSortThreads), 0, st,
                        k0, v0, n, shift, hist, k1, v1);
     const hipError_t e = hipGetLastError();
@@ -358,17 +536,41 @@ hipError_t radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1, ui
   return hipSuccess;
 }
 
-hipError_t segsum(SegArgs a, bool src_f32, hipStream_t st) {
-  a.nchunks = (a.n + kChunk - 1) / kChunk;
-  const dim3 grid(unsigned(a.nchunks), unsigned((a.width + kColGroup - 1) / kColGroup));
-  if (src_f32)
-    hipLaunchKernelGGL(segsum_level1_kernel<float>, grid, dim3(256), 0, st, a);
+__global__ void clear_count_kernel(uint32_t* c) { *c = 0u; }
+
+template <typename T, int THREADS, int NV>
+hipError_t segsum_launch(const SegArgs& a, hipStream_t st) {
+  const unsigned gy = unsigned((a.width + Cols<THREADS, NV>::kGroup - 1) / Cols<THREADS, NV>::kGroup);
+  if (a.chunk == kChunkWide)
+    hipLaunchKernelGGL((segsum_level1_kernel<T, THREADS, NV, kChunkWide>),
+                       dim3(unsigned(a.nchunks), gy), dim3(THREADS), 0, st, a);
   else
-    hipLaunchKernelGGL(segsum_level1_kernel<uint16_t>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((segsum_level1_kernel<T, THREADS, NV, kChunk>),
+                       dim3(unsigned(a.nchunks), gy), dim3(THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(segsum_level2_kernel, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((segsum_level2_kernel<THREADS, NV>),
+                     dim3(unsigned(std::min<int64_t>(a.nchunks, 1024)), gy), dim3(THREADS), 0, st,
+                     a);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t segsum_typed(const SegArgs& a, hipStream_t st) {
+  // one 4-value vector per lane: a wave per row of up to 256 values, else 256-thread blocks
+  // over column groups of 1024 values (more blocks, longer load batches)
+  if (a.width <= 256) return segsum_launch<T, 64, 1>(a, st);
+  return segsum_launch<T, 256, 1>(a, st);
+}
+
+// Chunks of kChunk entries for the sub-tables (many short runs), kChunkWide for E_0, whose
+// hottest tokens form runs of thousands: fewer partial sums for their owner to add, while
+// enough chunks remain to fill the GPU in level 1 (measured best of 32, 64 and 256).
+hipError_t segsum(SegArgs a, bool src_f32, hipStream_t st) {
+  a.chunk = a.by_table ? kChunk : kChunkWide;
+  a.nchunks = (a.n + a.chunk - 1) / a.chunk;
+  hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(1), 0, st, a.owners);
+  return src_f32 ? segsum_typed<float>(a, st) : segsum_typed<uint16_t>(a, st);
 }
 
 int32_t ceil_log2(int64_t x) {
@@ -431,10 +633,18 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
                          static_cast<float*>(b.doutT), Tp);
       hipLaunchKernelGGL(gather_transpose_kernel<float>, g, dim3(256), 0, st, ga);
     } else {
-      hipLaunchKernelGGL(transpose_pad_kernel<uint16_t>, g, dim3(256), 0, st,
-                         static_cast<const uint16_t*>(b.dout), T, int32_t(D), b.tokens, L.V0,
-                         static_cast<uint16_t*>(b.doutT), Tp);
-      hipLaunchKernelGGL(gather_transpose_kernel<uint16_t>, g, dim3(256), 0, st, ga);
+      if (D % kTile == 0)
+        hipLaunchKernelGGL(transpose_pad16_kernel, g, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(b.dout), T, int32_t(D), b.tokens, L.V0,
+                           static_cast<uint16_t*>(b.doutT), Tp);
+      else
+        hipLaunchKernelGGL(transpose_pad_kernel<uint16_t>, g, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(b.dout), T, int32_t(D), b.tokens, L.V0,
+                           static_cast<uint16_t*>(b.doutT), Tp);
+      if (L.d % kTile == 0)
+        hipLaunchKernelGGL(gather_transpose16_kernel, g, dim3(256), 0, st, ga);
+      else
+        hipLaunchKernelGGL(gather_transpose_kernel<uint16_t>, g, dim3(256), 0, st, ga);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_dense_product(L, b.doutT, D, b.GT, int32_t(D), int32_t(Tp), b.ident, b.dW, D, c,
@@ -457,6 +667,7 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     a.src = b.dG;
     a.head = b.head;
     a.tail = b.tail;
+    a.owners = b.owners;
     a.n = n;
     a.ld_src = D;
     a.sentinel = sentinel;
@@ -480,6 +691,7 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     a.src = b.dout;
     a.head = b.head;
     a.tail = b.tail;
+    a.owners = b.owners;
     a.n = T;
     a.ld_src = D;
     a.sentinel = sentinel;

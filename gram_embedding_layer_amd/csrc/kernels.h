@@ -73,6 +73,7 @@ struct BackwardArgs {
   uint32_t* hist;
   float* head;
   float* tail;
+  uint32_t* owners;
 };
 hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_t st);
 

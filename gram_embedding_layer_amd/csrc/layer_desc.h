@@ -45,7 +45,8 @@ constexpr int kSortTile = 4096;   // keys per radix-sort block
 constexpr int kChunk = 32;        // sorted entries per segmented-reduction chunk
 struct BwLayout {
   size_t idx_off, ident_off, wt_off, doutt_off, gt_off, dg_off, part_off;
-  size_t keys0_off, keys1_off, vals0_off, vals1_off, hist_off, head_off, tail_off, total;
+  size_t keys0_off, keys1_off, vals0_off, vals1_off, hist_off, head_off, tail_off, owners_off;
+  size_t total;
 };
 // contraction ranges of dW (c dout^T G, contracted over the rows)
 int32_t backward_splits(const LayerDesc& L, int64_t rows);

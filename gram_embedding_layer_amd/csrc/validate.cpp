@@ -108,9 +108,13 @@ bool bw_layout(const LayerDesc& L, int64_t rows, BwLayout* out) {
   w.keys1_off = take(nsort * 8);
   w.vals0_off = take(nsort * 4);
   w.vals1_off = take(nsort * 4);
-  w.hist_off = take(256 * (nblocks > 0 ? nblocks : 1) * 4);
+  // radix histograms [256 * nblocks] and the scan's tile totals after them
+  const size_t m = 256 * (nblocks > 0 ? nblocks : 1);
+  w.hist_off = take((m + (m + 1023) / 1024) * 4);
   w.head_off = take(seg * 4);
   w.tail_off = take(seg * 4);
+  const size_t nchunks = (nsort + kChunk - 1) / kChunk;
+  w.owners_off = take((1 + nchunks) * 4);
   w.total = o;
   *out = w;
   return true;
