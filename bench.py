@@ -441,9 +441,58 @@ def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
         raise RuntimeError("device error flags set during decode")
     toks = nsteps * nseq * tmax
     log(f"decode graph: {t/nsteps*1e6:.1f} us/step, eager {eager_us:.1f} us/step")
+
+    # Speculative decoding with the rows computed while the draft ids appear (the deep notes'
+    # section 4.2): each draft id's row is one call (ngram_embed_decode_rows, window of one
+    # row); verify then only commits. Graphs of the same 1000 steps: rows one at a time +
+    # commit (all N-gram work of a step), and the commit alone (what stays on the verify
+    # step's path).
+    n_j = [torch.full((nseq,), j + 1, dtype=torch.int32, device=dev) for j in range(tmax)]
+
+    def graph_time(body):
+        gr = torch.cuda.CUDAGraph()
+        cache.ring.copy_(ring0)
+        cache.len.copy_(len0)
+        torch.cuda.synchronize(dev)
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream()
+            for s in range(nsteps):
+                body(s, cs)
+        ts = []
+        for rep in range(3):
+            cache.ring.copy_(ring0)
+            cache.len.copy_(len0)
+            torch.cuda.synchronize(dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize(dev)
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts)) / nsteps
+
+    def rows_then_commit(s, cs):
+        for j in range(tmax):
+            g.ngram_embed_decode_rows(cfg, tables, cache, ids[s], n_j[j], out, ws, row_begin=j,
+                                      row_end=j + 1, stream=cs)
+        g.ngram_cache_commit(cfg, cache, ids[s], n_new, stream=cs)
+
+    def commit_only(s, cs):
+        g.ngram_cache_commit(cfg, cache, ids[s], n_new, stream=cs)
+
+    t_rows = graph_time(rows_then_commit)
+    t_commit = graph_time(commit_only)
+    if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+        raise RuntimeError("device error flags set during the draft-phase decode")
+    draft = {"us_per_step_rows_one_at_a_time": round(t_rows * 1e6, 2),
+             "us_per_row_call": round((t_rows - t_commit) / tmax * 1e6, 2),
+             "us_verify_path_commit_only": round(t_commit * 1e6, 2)}
+    log(f"draft-phase rows: {t_rows*1e6:.1f} us/step in {tmax} calls, verify path "
+        f"{t_commit*1e6:.1f} us (one-shot decode {t/nsteps*1e6:.1f} us)")
     return {"workload": DECODE_WORKLOAD, "steps": nsteps, "seqs": nseq, "ids_per_step": tmax,
             "tokens_per_s": round(toks / t, 1), "us_per_step_graph": round(t / nsteps * 1e6, 2),
-            "us_per_step_eager": round(eager_us, 2), "replays": len(times)}
+            "us_per_step_eager": round(eager_us, 2), "replays": len(times),
+            "draft_phase": draft}
 
 
 if __name__ == "__main__":

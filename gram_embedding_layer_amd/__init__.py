@@ -20,6 +20,8 @@ __all__ = [
     "LIB_PATH", "NgramError", "Config", "Tables", "Cache", "load",
     "NGRAM_OK", "NGRAM_F32", "NGRAM_BF16", "AMP_MODES",
     "NGRAM_FLAG_BAD_TOKEN", "NGRAM_FLAG_BAD_SEQLENS", "NGRAM_FLAG_BAD_COUNT",
+    "NGRAM_FLAG_BAD_SLOT", "ngram_embed_decode_rows", "ngram_cache_init_slots",
+    "ngram_cache_commit_slots",
     "ngram_embed_workspace_size", "ngram_embed_workspace_layout", "ngram_embed_hash",
     "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
     "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
@@ -32,6 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libngram_em
 NGRAM_OK = 0
 NGRAM_F32, NGRAM_BF16 = 0, 1
 NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS, NGRAM_FLAG_BAD_COUNT = 1, 2, 4
+NGRAM_FLAG_BAD_SLOT = 8
 NGRAM_MAX_DECODE_TOKENS = 8
 # embedding amplification modes (NGRAM_AMP_NONE / SCALE / LAYERNORM)
 AMP_MODES = {"none": 0, "scale": 1, "layernorm": 2}
@@ -91,6 +94,10 @@ def load():
         "ngram_cache_init": (ctypes.c_int, [cfgp, cachep, P, P, I64, P]),
         "ngram_embed_decode": (ctypes.c_int, [cfgp, tabp, cachep, P, P, I32, P, P, P, SZ, P]),
         "ngram_cache_commit": (ctypes.c_int, [cfgp, cachep, P, P, I32, P, P]),
+        "ngram_embed_decode_rows": (ctypes.c_int, [cfgp, tabp, cachep, P, I32, P, P, I32, I32,
+                                                   I32, P, P, P, SZ, P]),
+        "ngram_cache_init_slots": (ctypes.c_int, [cfgp, cachep, P, I32, P, P, I64, P, P]),
+        "ngram_cache_commit_slots": (ctypes.c_int, [cfgp, cachep, P, I32, P, P, I32, P, P]),
         "ngram_embed_backward_workspace_size": (SZ, [cfgp, I64]),
         "ngram_embed_backward": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, P,
                                                 ctypes.POINTER(P), P, P, SZ, P]),
@@ -311,6 +318,41 @@ def ngram_embed_decode(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_
         ctypes.byref(c), ctypes.byref(t), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
         int(new_tokens.shape[1]), _ptr(n_commit), _ptr(out), _ptr(ws),
         int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def ngram_embed_decode_rows(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_new, out,
+                            ws, row_begin=0, row_end=None, slots=None, n_commit=None,
+                            stream=None):
+    """Rows [row_begin, min(row_end, n_new[b])) of every batch entry b (batch entry b uses
+    cache slot slots[b], or b); other rows of out are left as they are."""
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    cc = cache._c()
+    tmax = int(new_tokens.shape[1])
+    _check("ngram_embed_decode_rows", load().ngram_embed_decode_rows(
+        ctypes.byref(c), ctypes.byref(t), ctypes.byref(cc), _ptr(slots),
+        int(new_tokens.shape[0]), _ptr(new_tokens), _ptr(n_new), tmax, int(row_begin),
+        int(tmax if row_end is None else row_end), _ptr(n_commit), _ptr(out), _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def ngram_cache_init_slots(cfg: Config, cache: Cache, slots, tokens, cu_seqlens,
+                           err_flags=None, stream=None):
+    c, keep = cfg._c()
+    cc = cache._c()
+    _check("ngram_cache_init_slots", load().ngram_cache_init_slots(
+        ctypes.byref(c), ctypes.byref(cc), _ptr(slots), int(cu_seqlens.numel()) - 1,
+        _ptr(tokens), _ptr(cu_seqlens), int(tokens.numel()), _ptr(err_flags), _stream(stream)))
+
+
+def ngram_cache_commit_slots(cfg: Config, cache: Cache, slots, new_tokens, n_accept,
+                             err_flags=None, stream=None):
+    c, keep = cfg._c()
+    cc = cache._c()
+    _check("ngram_cache_commit_slots", load().ngram_cache_commit_slots(
+        ctypes.byref(c), ctypes.byref(cc), _ptr(slots), int(new_tokens.shape[0]),
+        _ptr(new_tokens), _ptr(n_accept), int(new_tokens.shape[1]), _ptr(err_flags),
+        _stream(stream)))
 
 
 def ngram_cache_commit(cfg: Config, cache: Cache, new_tokens, n_accept, err_flags=None,

@@ -29,17 +29,20 @@ int check_tables(const LayerDesc& L, const ngram_embed_tables* T, bool need_e0_w
 // Projection of `rows` rows into `out`, then the amplification: the scale is part of the
 // projection's epilogue; the layer normalisation reads the unrounded rows from the
 // workspace.
+// `map` places the compact rows in `out` (decode windows); the unrounded rows of the layer
+// normalisation stay compact in the workspace.
 int project_amplified(const LayerDesc& L, const ngram_embed_tables* T, const int32_t* idx,
                       const int32_t* tok, int64_t rows, void* out, void* ws,
-                      const ngram::WsLayout& lay, hipStream_t st) {
+                      const ngram::WsLayout& lay, const ngram::RowMap& map, hipStream_t st) {
   if (L.amp != NGRAM_AMP_LAYERNORM)
     return hip_status(ngram::launch_project(L, T->E0, T->E, T->W, idx, tok, rows, out, false,
-                                            st));
+                                            map, st));
   float* pre = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.pre_off);
-  int rc = hip_status(ngram::launch_project(L, T->E0, T->E, T->W, idx, tok, rows, pre, true, st));
+  int rc = hip_status(ngram::launch_project(L, T->E0, T->E, T->W, idx, tok, rows, pre, true,
+                                            ngram::RowMap{}, st));
   if (rc != NGRAM_OK) return rc;
   return hip_status(ngram::launch_layernorm(L, pre, tok, T->ln_weight, T->ln_bias, rows, out,
-                                            st));
+                                            map, st));
 }
 
 int check_ws(const LayerDesc& L, const void* ws, size_t ws_bytes, int64_t rows,
@@ -117,7 +120,8 @@ int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables*
       !ngram::aligned(out, 16))
     return NGRAM_EALIGN;
   return hip_status(ngram::launch_project(L, tables->E0, tables->E, tables->W, idx, tok, nrows,
-                                          out, false, static_cast<hipStream_t>(stream)));
+                                          out, false, ngram::RowMap{},
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
@@ -140,7 +144,7 @@ int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables*
                                                ws_flags(ws), st));
     if (rc != NGRAM_OK) return rc;
   }
-  return project_amplified(L, tables, idx, tokens, ntok, out, ws, lay, st);
+  return project_amplified(L, tables, idx, tokens, ntok, out, ws, lay, ngram::RowMap{}, st);
 }
 
 int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const int32_t* tokens,
@@ -153,8 +157,8 @@ int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const in
   if (!ngram::aligned(cache->len, 8) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
   if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
   if (ntok > 0 && !ngram::aligned(tokens, 4)) return NGRAM_EALIGN;
-  return hip_status(ngram::launch_cache_init(L, cache->ring, cache->len, tokens, cu_seqlens,
-                                             cache->nseq, ntok, nullptr,
+  return hip_status(ngram::launch_cache_init(L, cache->ring, cache->len, nullptr, cache->nseq,
+                                             tokens, cu_seqlens, cache->nseq, ntok, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -183,11 +187,11 @@ int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* 
   int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
   // hash (and commit, when asked) in one kernel; the projection reads only tok/idx, so the
   // cache may advance before it runs
-  rc = hip_status(ngram::launch_hash_decode(L, cache->ring, cache->len, new_tokens, n_new,
-                                            n_commit, cache->nseq, tmax, tok, idx, ws_flags(ws),
-                                            st));
+  ngram::DecodeArgs d{cache->ring, cache->len, nullptr, cache->nseq, new_tokens, n_new,
+                      n_commit, cache->nseq, tmax, 0, tmax, -1, tok, idx, ws_flags(ws)};
+  rc = hip_status(ngram::launch_hash_decode(L, d, st));
   if (rc != NGRAM_OK) return rc;
-  return project_amplified(L, tables, idx, tok, rows, out, ws, lay, st);
+  return project_amplified(L, tables, idx, tok, rows, out, ws, lay, ngram::RowMap{}, st);
 }
 
 int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
@@ -204,8 +208,93 @@ int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
     return NGRAM_EALIGN;
   if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
   if (err_flags != nullptr && !ngram::aligned(err_flags, 4)) return NGRAM_EALIGN;
-  return hip_status(ngram::launch_cache_commit(L, cache->ring, cache->len, new_tokens, n_accept,
-                                               nullptr, cache->nseq, tmax, err_flags,
+  return hip_status(ngram::launch_cache_commit(L, cache->ring, cache->len, nullptr, cache->nseq,
+                                               new_tokens, n_accept, cache->nseq, tmax,
+                                               err_flags, static_cast<hipStream_t>(stream)));
+}
+
+int ngram_embed_decode_rows(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                            ngram_cache* cache, const int32_t* slots, int32_t nbatch,
+                            const int32_t* new_tokens, const int32_t* n_new, int32_t tmax,
+                            int32_t row_begin, int32_t row_end, const int32_t* n_commit,
+                            void* out, void* ws, size_t ws_bytes, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0 || nbatch < 0) return NGRAM_EINVAL;
+  if (slots == nullptr && nbatch > cache->nseq) return NGRAM_EINVAL;
+  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
+  if (row_begin < 0 || row_end <= row_begin || row_end > tmax) return NGRAM_EINVAL;
+  const int32_t width = row_end - row_begin;
+  const int64_t rows = int64_t(nbatch) * width;
+  ngram::WsLayout lay;
+  if ((rc = check_ws(L, ws, ws_bytes, rows, &lay)) != NGRAM_OK) return rc;
+  if (rows == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
+      !ngram::aligned(n_new, 4) || !ngram::aligned(out, 16))
+    return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if ((n_commit != nullptr && !ngram::aligned(n_commit, 4)) ||
+      (slots != nullptr && !ngram::aligned(slots, 4)))
+    return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* tok = reinterpret_cast<int32_t*>(w + lay.tok_off);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
+  ngram::DecodeArgs d{cache->ring, cache->len, slots, cache->nseq, new_tokens, n_new, n_commit,
+                      nbatch, tmax, row_begin, width, ngram::kSkipRow, tok, idx, ws_flags(ws)};
+  rc = hip_status(ngram::launch_hash_decode(L, d, st));
+  if (rc != NGRAM_OK) return rc;
+  // compact row b * width + (j - row_begin) is row b * tmax + j of out
+  ngram::RowMap map;
+  map.group = width;
+  map.stride = tmax;
+  map.off = row_begin;
+  return project_amplified(L, tables, idx, tok, rows, out, ws, lay, map, st);
+}
+
+int ngram_cache_init_slots(const ngram_embed_config* cfg, ngram_cache* cache,
+                           const int32_t* slots, int32_t nbatch, const int32_t* tokens,
+                           const int32_t* cu_seqlens, int64_t ntok, int32_t* err_flags,
+                           void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0 || nbatch < 0 || ntok < 0) return NGRAM_EINVAL;
+  if (slots == nullptr && nbatch > cache->nseq) return NGRAM_EINVAL;
+  if (nbatch == 0) return NGRAM_OK;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if (ntok > 0 && !ngram::aligned(tokens, 4)) return NGRAM_EALIGN;
+  if ((slots != nullptr && !ngram::aligned(slots, 4)) ||
+      (err_flags != nullptr && !ngram::aligned(err_flags, 4)))
+    return NGRAM_EALIGN;
+  return hip_status(ngram::launch_cache_init(L, cache->ring, cache->len, slots, cache->nseq,
+                                             tokens, cu_seqlens, nbatch, ntok, err_flags,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int ngram_cache_commit_slots(const ngram_embed_config* cfg, ngram_cache* cache,
+                             const int32_t* slots, int32_t nbatch, const int32_t* new_tokens,
+                             const int32_t* n_accept, int32_t tmax, int32_t* err_flags,
+                             void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0 || nbatch < 0) return NGRAM_EINVAL;
+  if (slots == nullptr && nbatch > cache->nseq) return NGRAM_EINVAL;
+  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
+  if (nbatch == 0) return NGRAM_OK;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
+      !ngram::aligned(n_accept, 4))
+    return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if ((slots != nullptr && !ngram::aligned(slots, 4)) ||
+      (err_flags != nullptr && !ngram::aligned(err_flags, 4)))
+    return NGRAM_EALIGN;
+  return hip_status(ngram::launch_cache_commit(L, cache->ring, cache->len, slots, cache->nseq,
+                                               new_tokens, n_accept, nbatch, tmax, err_flags,
                                                static_cast<hipStream_t>(stream)));
 }
 

@@ -73,42 +73,49 @@ __global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
   hash_position<NMAX>(L, c, idx + i * L.S);
 }
 
-// One decode step: every thread hashes one (sequence, slot) row from the N-gram cache and
-// the step's new ids. A block holds whole sequences (kThreads / tmax of them), so when the
-// step also commits, all reads of a sequence's ring precede the barrier and the commit's
-// writes follow it.
+// One decode step: every thread hashes one (batch entry, row) of the window from the
+// N-gram cache and the step's new ids. Batch entry b uses cache slot slots[b] (or b); its
+// rows j in [row_begin, row_begin + width) become compact rows b * width + (j - row_begin).
+// A block holds whole batch entries (kThreads / width of them), so when the step also
+// commits, all reads of an entry's ring precede the barrier and the commit's writes follow.
+// Rows past n_new[b] (and every row of an entry whose slot is out of range) get the token
+// `unused_tok`: -1 (the projection writes a zero row) or kSkipRow (the row is not written).
 template <int NMAX>
-__global__ __launch_bounds__(kThreads) void hash_decode_kernel(
-    const LayerDesc L, int32_t* __restrict__ ring, int64_t* __restrict__ len,
-    const int32_t* __restrict__ newtok, const int32_t* __restrict__ n_new,
-    const int32_t* __restrict__ n_commit, int32_t nseq, int32_t tmax, int32_t* __restrict__ tok,
-    int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
-  const int spb = kThreads / tmax;                 // sequences per block
-  const int b = blockIdx.x * spb + threadIdx.x / tmax;
-  const int j = threadIdx.x % tmax;
-  const bool active = threadIdx.x < spb * tmax && b < nseq;
+__global__ __launch_bounds__(kThreads) void hash_decode_kernel(const LayerDesc L,
+                                                               const DecodeArgs a) {
+  const int spb = kThreads / a.width;              // batch entries per block
+  const int b = blockIdx.x * spb + threadIdx.x / a.width;
+  const int jj = threadIdx.x % a.width;
+  const int j = a.row_begin + jj;
+  const bool active = threadIdx.x < spb * a.width && b < a.nbatch;
   const int nm1 = L.N - 1;
-  int nn = 0;
+  int nn = 0, slot = 0;
+  bool slot_ok = false;
   int64_t committed = 0;
   if (active) {
-    nn = n_new[b];
-    if (nn < 0 || nn > tmax) {
-      if (flags != nullptr && j == 0) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
-      nn = nn < 0 ? 0 : tmax;
+    slot = a.slots != nullptr ? a.slots[b] : b;
+    slot_ok = slot >= 0 && slot < a.nslots;
+    if (!slot_ok && a.flags != nullptr && jj == 0) atomicOr(a.flags, NGRAM_FLAG_BAD_SLOT);
+    nn = a.n_new[b];
+    if (nn < 0 || nn > a.tmax) {
+      if (a.flags != nullptr && jj == 0) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
+      nn = nn < 0 ? 0 : a.tmax;
     }
-    committed = len[b];
-    if (committed < 0) committed = 0;
-    const int64_t r = int64_t(b) * tmax + j;
-    int32_t* out = idx + r * L.S;
-    const int32_t* nt = newtok + int64_t(b) * tmax;
-    if (j >= nn) {  // unused slot: E_0 token -1 makes the projection write a zero row
-      tok[r] = -1;
+    if (slot_ok) {
+      committed = a.len[slot];
+      if (committed < 0) committed = 0;
+    }
+    const int64_t r = int64_t(b) * a.width + jj;
+    int32_t* out = a.idx + r * L.S;
+    const int32_t* nt = a.newtok + int64_t(b) * a.tmax;
+    if (j >= nn || !slot_ok) {
+      a.tok[r] = a.unused_tok;
       for (int s = 0; s < L.S; ++s) out[s] = 0;
     } else {
       const int32_t t = nt[j];
-      if (flags != nullptr && uint32_t(t) >= uint32_t(L.V0))
-        atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
-      tok[r] = t;
+      if (a.flags != nullptr && uint32_t(t) >= uint32_t(L.V0))
+        atomicOr(a.flags, NGRAM_FLAG_BAD_TOKEN);
+      a.tok[r] = t;
       uint32_t c[NMAX];
 #pragma unroll
       for (int i = 0; i < NMAX; ++i) {
@@ -118,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void hash_decode_kernel(
             v = uint32_t(nt[j - i]);                 // a new id of this step
           } else {
             const int64_t q = committed + (j - i);   // committed position, from the cache
-            if (q >= 0) v = uint32_t(ring[int64_t(b) * nm1 + q % nm1]);
+            if (q >= 0) v = uint32_t(a.ring[int64_t(slot) * nm1 + q % nm1]);
           }
         }
         c[i] = v;
@@ -126,29 +133,35 @@ __global__ __launch_bounds__(kThreads) void hash_decode_kernel(
       hash_position<NMAX>(L, c, out);
     }
   }
-  if (n_commit == nullptr) return;
+  if (a.n_commit == nullptr) return;
   __syncthreads();
-  if (!active || j != 0) return;
+  if (!active || jj != 0 || !slot_ok) return;
   // commit the first n_commit[b] (<= n_new[b]) new ids
-  int a = n_commit[b];
-  if (a < 0 || a > nn) {
-    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
-    a = a < 0 ? 0 : nn;
+  int acc = a.n_commit[b];
+  if (acc < 0 || acc > nn) {
+    if (a.flags != nullptr) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
+    acc = acc < 0 ? 0 : nn;
   }
   if (nm1 > 0) {
-    int32_t* rb = ring + int64_t(b) * nm1;
-    const int32_t* nt = newtok + int64_t(b) * tmax;
-    for (int q = (a > nm1 ? a - nm1 : 0); q < a; ++q) rb[(committed + q) % nm1] = nt[q];
+    int32_t* rb = a.ring + int64_t(slot) * nm1;
+    const int32_t* nt = a.newtok + int64_t(b) * a.tmax;
+    for (int q = (acc > nm1 ? acc - nm1 : 0); q < acc; ++q) rb[(committed + q) % nm1] = nt[q];
   }
-  len[b] = committed + a;
+  a.len[slot] = committed + acc;
 }
 
+// Batch entry b (sequence b of the packed tokens) fills cache slot slots[b] (or b).
 __global__ __launch_bounds__(kThreads) void cache_init_kernel(
     int32_t nm1, int32_t* __restrict__ ring, int64_t* __restrict__ len,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu, int32_t nseq,
-    int64_t ntok, int32_t* __restrict__ flags) {
+    const int32_t* __restrict__ slots, int32_t nslots, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ cu, int32_t nbatch, int64_t ntok, int32_t* __restrict__ flags) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nseq) return;
+  if (b >= nbatch) return;
+  const int slot = slots != nullptr ? slots[b] : b;
+  if (slot < 0 || slot >= nslots) {
+    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_SLOT);
+    return;
+  }
   int64_t lo = cu[b], hi = cu[b + 1];
   if (lo < 0 || hi < lo || hi > ntok) {
     if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_SEQLENS);
@@ -156,34 +169,38 @@ __global__ __launch_bounds__(kThreads) void cache_init_kernel(
     hi = hi < lo ? lo : (hi > ntok ? ntok : hi);
   }
   const int64_t n = hi - lo;
-  len[b] = n;
+  len[slot] = n;
   if (nm1 <= 0) return;
-  int32_t* rb = ring + int64_t(b) * nm1;
+  int32_t* rb = ring + int64_t(slot) * nm1;
   for (int s = 0; s < nm1; ++s) rb[s] = 0;
   for (int64_t q = (n > nm1 ? n - nm1 : 0); q < n; ++q) rb[q % nm1] = tokens[lo + q];
 }
 
 __global__ __launch_bounds__(kThreads) void cache_commit_kernel(
     int32_t nm1, int32_t* __restrict__ ring, int64_t* __restrict__ len,
-    const int32_t* __restrict__ newtok, const int32_t* __restrict__ n_accept,
-    const int32_t* __restrict__ n_new, int32_t nseq, int32_t tmax,
+    const int32_t* __restrict__ slots, int32_t nslots, const int32_t* __restrict__ newtok,
+    const int32_t* __restrict__ n_accept, int32_t nbatch, int32_t tmax,
     int32_t* __restrict__ flags) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nseq) return;
-  int a = n_accept[b];
-  const int cap = n_new != nullptr ? min(max(n_new[b], 0), tmax) : tmax;
-  if (a < 0 || a > cap) {
-    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
-    a = a < 0 ? 0 : cap;
+  if (b >= nbatch) return;
+  const int slot = slots != nullptr ? slots[b] : b;
+  if (slot < 0 || slot >= nslots) {
+    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_SLOT);
+    return;
   }
-  int64_t committed = len[b];
+  int a = n_accept[b];
+  if (a < 0 || a > tmax) {
+    if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_COUNT);
+    a = a < 0 ? 0 : tmax;
+  }
+  int64_t committed = len[slot];
   if (committed < 0) committed = 0;
   if (nm1 > 0) {
-    int32_t* rb = ring + int64_t(b) * nm1;
+    int32_t* rb = ring + int64_t(slot) * nm1;
     const int32_t* nt = newtok + int64_t(b) * tmax;
     for (int q = (a > nm1 ? a - nm1 : 0); q < a; ++q) rb[(committed + q) % nm1] = nt[q];
   }
-  len[b] = committed + a;
+  len[slot] = committed + a;
 }
 
 __global__ void clear_flags_kernel(int32_t* flags) { flags[0] = 0; }
@@ -200,14 +217,10 @@ hipError_t hash_prefill_n(const LayerDesc& L, const int32_t* tokens, const int32
 }
 
 template <int NMAX>
-hipError_t hash_decode_n(const LayerDesc& L, int32_t* ring, int64_t* len,
-                         const int32_t* newtok, const int32_t* n_new, const int32_t* n_commit,
-                         int32_t nseq, int32_t tmax, int32_t* tok, int32_t* idx, int32_t* flags,
-                         hipStream_t st) {
-  const int spb = kThreads / tmax;
-  const unsigned blocks = unsigned((nseq + spb - 1) / spb);
-  hipLaunchKernelGGL(hash_decode_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, L, ring,
-                     len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags);
+hipError_t hash_decode_n(const LayerDesc& L, const DecodeArgs& a, hipStream_t st) {
+  const int spb = kThreads / a.width;
+  const unsigned blocks = unsigned((a.nbatch + spb - 1) / spb);
+  hipLaunchKernelGGL(hash_decode_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, L, a);
   return hipGetLastError();
 }
 
@@ -223,39 +236,31 @@ hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const 
   return hash_prefill_n<NGRAM_MAX_ORDER>(L, tokens, cu, nseq, ntok, idx, flags, st);
 }
 
-hipError_t launch_hash_decode(const LayerDesc& L, int32_t* ring, int64_t* len,
-                              const int32_t* newtok, const int32_t* n_new,
-                              const int32_t* n_commit, int32_t nseq, int32_t tmax, int32_t* tok,
-                              int32_t* idx, int32_t* flags, hipStream_t st) {
-  if (L.N <= 2)
-    return hash_decode_n<2>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags,
-                            st);
-  if (L.N <= 4)
-    return hash_decode_n<4>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags,
-                            st);
-  if (L.N <= 8)
-    return hash_decode_n<8>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok, idx, flags,
-                            st);
-  return hash_decode_n<NGRAM_MAX_ORDER>(L, ring, len, newtok, n_new, n_commit, nseq, tmax, tok,
-                                        idx, flags, st);
+hipError_t launch_hash_decode(const LayerDesc& L, const DecodeArgs& a, hipStream_t st) {
+  if (a.nbatch <= 0 || a.width <= 0) return hipSuccess;
+  if (L.N <= 2) return hash_decode_n<2>(L, a, st);
+  if (L.N <= 4) return hash_decode_n<4>(L, a, st);
+  if (L.N <= 8) return hash_decode_n<8>(L, a, st);
+  return hash_decode_n<NGRAM_MAX_ORDER>(L, a, st);
 }
 
 hipError_t launch_cache_init(const LayerDesc& L, int32_t* ring, int64_t* len,
-                             const int32_t* tokens, const int32_t* cu, int32_t nseq,
-                             int64_t ntok, int32_t* flags, hipStream_t st) {
-  const unsigned blocks = unsigned((nseq + kThreads - 1) / kThreads);
+                             const int32_t* slots, int32_t nslots, const int32_t* tokens,
+                             const int32_t* cu, int32_t nbatch, int64_t ntok, int32_t* flags,
+                             hipStream_t st) {
+  const unsigned blocks = unsigned((nbatch + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(cache_init_kernel, dim3(blocks), dim3(kThreads), 0, st, L.N - 1, ring, len,
-                     tokens, cu, nseq, ntok, flags);
+                     slots, nslots, tokens, cu, nbatch, ntok, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_cache_commit(const LayerDesc& L, int32_t* ring, int64_t* len,
-                               const int32_t* newtok, const int32_t* n_accept,
-                               const int32_t* n_new, int32_t nseq, int32_t tmax,
+                               const int32_t* slots, int32_t nslots, const int32_t* newtok,
+                               const int32_t* n_accept, int32_t nbatch, int32_t tmax,
                                int32_t* flags, hipStream_t st) {
-  const unsigned blocks = unsigned((nseq + kThreads - 1) / kThreads);
+  const unsigned blocks = unsigned((nbatch + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(cache_commit_kernel, dim3(blocks), dim3(kThreads), 0, st, L.N - 1, ring,
-                     len, newtok, n_accept, n_new, nseq, tmax, flags);
+                     len, slots, nslots, newtok, n_accept, nbatch, tmax, flags);
   return hipGetLastError();
 }
 

@@ -12,21 +12,44 @@ hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const 
                                int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
                                hipStream_t st);
 
-// kernel 4 (front half): context from the N-gram cache + new ids -> tok, idx; then, if
-// n_commit is not null, the step's commit into the cache
-hipError_t launch_hash_decode(const LayerDesc& L, int32_t* ring, int64_t* len,
-                              const int32_t* newtok, const int32_t* n_new,
-                              const int32_t* n_commit, int32_t nseq, int32_t tmax, int32_t* tok,
-                              int32_t* idx, int32_t* flags, hipStream_t st);
+// Token of a row that must not be written (rows outside a decode window's n_new).
+constexpr int32_t kSkipRow = -2;
 
-// kernel 4 (cache upkeep)
+// kernel 4 (front half): context from the N-gram cache + new ids -> tok, idx for the rows
+// [row_begin, row_begin + width) of every batch entry (compact: b * width + j - row_begin);
+// then, if n_commit is not null, the step's commit into the cache
+struct DecodeArgs {
+  int32_t* ring;            // [nslots, N-1]
+  int64_t* len;             // [nslots]
+  const int32_t* slots;     // [nbatch] cache slot of each batch entry, or null (slot b)
+  int32_t nslots;
+  const int32_t* newtok;    // [nbatch, tmax]
+  const int32_t* n_new;     // [nbatch]
+  const int32_t* n_commit;  // [nbatch] or null
+  int32_t nbatch, tmax, row_begin, width;
+  int32_t unused_tok;       // token of rows past n_new: -1 (zero row) or kSkipRow
+  int32_t* tok;             // [nbatch * width]
+  int32_t* idx;             // [nbatch * width, S]
+  int32_t* flags;
+};
+hipError_t launch_hash_decode(const LayerDesc& L, const DecodeArgs& a, hipStream_t st);
+
+// kernel 4 (cache upkeep); slots as above
 hipError_t launch_cache_init(const LayerDesc& L, int32_t* ring, int64_t* len,
-                             const int32_t* tokens, const int32_t* cu, int32_t nseq,
-                             int64_t ntok, int32_t* flags, hipStream_t st);
+                             const int32_t* slots, int32_t nslots, const int32_t* tokens,
+                             const int32_t* cu, int32_t nbatch, int64_t ntok, int32_t* flags,
+                             hipStream_t st);
 hipError_t launch_cache_commit(const LayerDesc& L, int32_t* ring, int64_t* len,
-                               const int32_t* newtok, const int32_t* n_accept,
-                               const int32_t* n_new, int32_t nseq, int32_t tmax,
+                               const int32_t* slots, int32_t nslots, const int32_t* newtok,
+                               const int32_t* n_accept, int32_t nbatch, int32_t tmax,
                                int32_t* flags, hipStream_t st);
+
+// Where the final output rows go: compact row m is written to row
+// (m / group) * stride + off + m % group of `out` (group 0: row m). Rows whose token is
+// kSkipRow are not written.
+struct RowMap {
+  int32_t group = 0, stride = 0, off = 0;
+};
 hipError_t launch_clear_flags(int32_t* flags, hipStream_t st);
 
 // kernel 2: stand-alone gather of sub-table rows into G [nrows, D]
@@ -37,7 +60,8 @@ hipError_t launch_gather(const LayerDesc& L, const void* const* E, const int32_t
 // f32out, `out` is fp32 [nrows, D] and holds the unrounded rows
 hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
                           const void* W, const int32_t* idx, const int32_t* tok,
-                          int64_t nrows, void* out, bool f32out, hipStream_t st);
+                          int64_t nrows, void* out, bool f32out, const RowMap& map,
+                          hipStream_t st);
 
 // dense product for the backward: out = inv * A B^T (fp32, overwritten) or, with
 // accumulate, out += inv * A B^T through `splits` fp32 partial sums in `part`
@@ -81,6 +105,6 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
 // weight / bias: [D] in the config dtype or null
 hipError_t launch_layernorm(const LayerDesc& L, const float* pre, const int32_t* tok,
                             const void* weight, const void* bias, int64_t nrows, void* out,
-                            hipStream_t st);
+                            const RowMap& map, hipStream_t st);
 
 }  // namespace ngram

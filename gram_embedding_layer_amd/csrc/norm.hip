@@ -76,13 +76,16 @@ template <typename T, int NV>
 __global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
     const float* __restrict__ pre, const int32_t* __restrict__ tok, int32_t V0,
     const T* __restrict__ weight, const T* __restrict__ bias, float eps, int32_t D,
-    int64_t nrows, T* __restrict__ out) {
+    int64_t nrows, T* __restrict__ out, RowMap map) {
   const int64_t r = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= nrows) return;                        // whole waves leave; no barrier follows
+  const int32_t tk = tok[r];
+  if (tk == kSkipRow) return;                    // a row that is not written
   const int D4 = D / 4;
-  T* o = out + r * D;
-  if (uint32_t(tok[r]) >= uint32_t(V0)) {        // the whole wave takes this branch
+  const int64_t orow = map.group ? (r / map.group) * map.stride + map.off + r % map.group : r;
+  T* o = out + orow * D;
+  if (uint32_t(tk) >= uint32_t(V0)) {            // the whole wave takes this branch
     for (int c4 = lane; c4 < D4; c4 += 64) store4<T>(o, c4, f32x4_t{0.f, 0.f, 0.f, 0.f});
     return;
   }
@@ -120,15 +123,16 @@ __global__ __launch_bounds__(kThreads) void layernorm_rows_kernel(
 template <typename T, int NV>
 hipError_t launch_rows(const LayerDesc& L, const float* pre, const int32_t* tok,
                        const void* weight, const void* bias, int64_t nrows, void* out,
-                       hipStream_t st) {
+                       const RowMap& map, hipStream_t st) {
   const int64_t chunk = int64_t(1) << 30;        // rows per launch keeps the grid in range
+  if (map.group != 0 && nrows > chunk) return hipErrorInvalidValue;
   for (int64_t r0 = 0; r0 < nrows; r0 += chunk) {
     const int64_t n = std::min(chunk, nrows - r0);
     hipLaunchKernelGGL((layernorm_rows_kernel<T, NV>),
                        dim3(unsigned((n + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(kThreads),
                        0, st, pre + r0 * L.D, tok + r0, L.V0, static_cast<const T*>(weight),
                        static_cast<const T*>(bias), L.ln_eps, L.D, n,
-                       static_cast<T*>(out) + r0 * L.D);
+                       static_cast<T*>(out) + r0 * L.D, map);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -138,27 +142,27 @@ hipError_t launch_rows(const LayerDesc& L, const float* pre, const int32_t* tok,
 template <typename T>
 hipError_t launch_typed(const LayerDesc& L, const float* pre, const int32_t* tok,
                         const void* weight, const void* bias, int64_t nrows, void* out,
-                        hipStream_t st) {
+                        const RowMap& map, hipStream_t st) {
   // 16-byte vectors per lane: the smallest listed size that holds D / 256 of them
   const int need = (L.D / 4 + 63) / 64;
-  if (need <= 2) return launch_rows<T, 2>(L, pre, tok, weight, bias, nrows, out, st);
-  if (need <= 4) return launch_rows<T, 4>(L, pre, tok, weight, bias, nrows, out, st);
-  if (need <= 8) return launch_rows<T, 8>(L, pre, tok, weight, bias, nrows, out, st);
-  if (need <= 12) return launch_rows<T, 12>(L, pre, tok, weight, bias, nrows, out, st);
-  if (need <= 16) return launch_rows<T, 16>(L, pre, tok, weight, bias, nrows, out, st);
-  if (need <= 24) return launch_rows<T, 24>(L, pre, tok, weight, bias, nrows, out, st);
-  return launch_rows<T, kMaxNormD / 256>(L, pre, tok, weight, bias, nrows, out, st);
+  if (need <= 2) return launch_rows<T, 2>(L, pre, tok, weight, bias, nrows, out, map, st);
+  if (need <= 4) return launch_rows<T, 4>(L, pre, tok, weight, bias, nrows, out, map, st);
+  if (need <= 8) return launch_rows<T, 8>(L, pre, tok, weight, bias, nrows, out, map, st);
+  if (need <= 12) return launch_rows<T, 12>(L, pre, tok, weight, bias, nrows, out, map, st);
+  if (need <= 16) return launch_rows<T, 16>(L, pre, tok, weight, bias, nrows, out, map, st);
+  if (need <= 24) return launch_rows<T, 24>(L, pre, tok, weight, bias, nrows, out, map, st);
+  return launch_rows<T, kMaxNormD / 256>(L, pre, tok, weight, bias, nrows, out, map, st);
 }
 
 }  // namespace
 
 hipError_t launch_layernorm(const LayerDesc& L, const float* pre, const int32_t* tok,
                             const void* weight, const void* bias, int64_t nrows, void* out,
-                            hipStream_t st) {
+                            const RowMap& map, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (L.dtype == NGRAM_F32)
-    return launch_typed<float>(L, pre, tok, weight, bias, nrows, out, st);
-  return launch_typed<uint16_t>(L, pre, tok, weight, bias, nrows, out, st);
+    return launch_typed<float>(L, pre, tok, weight, bias, nrows, out, map, st);
+  return launch_typed<uint16_t>(L, pre, tok, weight, bias, nrows, out, map, st);
 }
 
 }  // namespace ngram

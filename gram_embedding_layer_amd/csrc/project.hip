@@ -68,7 +68,13 @@ struct ProjArgs {
   float inv;                          // output factor / (S + 1), or the product's factor
   int32_t tiles_m, tiles_n;
   int32_t splits;                     // contraction ranges (partial-sum output only)
+  int32_t row_group, row_stride, row_off;   // output row of compact row m (see RowMap)
 };
+
+// Output row of compact row m; rows whose token is kSkipRow are not written at all.
+__device__ __forceinline__ int64_t out_row(const ProjArgs& a, int64_t m) {
+  return a.row_group ? (m / a.row_group) * a.row_stride + a.row_off + m % a.row_group : m;
+}
 
 // Output modes of the matrix-core kernel.
 enum OutMode {
@@ -356,7 +362,8 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
       const int64_t m = mrow + it * RPI;
       const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
                                                            ec * 16);
-      if (m < a.nrows) {
+      if (m < a.nrows && tk[it] != kSkipRow) {
+        const int64_t om = out_row(a, m);
         const bool ok = !has_e0 || uint32_t(tk[it]) < uint32_t(a.V0);
         const float y0 = (y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv;
         const float y1 = (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv;
@@ -364,14 +371,14 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
         const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
         if constexpr (OM == kOutF32) {
           const f32x4_t res = ok ? f32x4_t{y0, y1, y2, y3} : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + m * a.ldo + n) = res;
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + om * a.ldo + n) = res;
         } else {
           u32x2_t res = {0u, 0u};
           if (ok) {
             res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
             res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
           }
-          __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + m * a.ldo + n));
+          __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + om * a.ldo + n));
         }
       }
     }
@@ -443,6 +450,8 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
     if (m >= a.nrows) continue;
     const bool has_e0 = a.E0 != nullptr;        // without E_0 every row is valid
     const int32_t tk = has_e0 ? a.tok[m] : 0;
+    if (tk == kSkipRow) continue;
+    const int64_t om = out_row(a, m);
     const bool ok = !has_e0 || uint32_t(tk) < uint32_t(a.V0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
       if (n >= a.N) continue;
       const float e0 = has_e0 && ok ? ld<T>(E0 + int64_t(tk) * a.N + n) : 0.f;
       const float y = ok ? (acc[i][j] + e0) * a.inv : 0.f;
-      st<TO>(out + m * a.ldo + n, y);
+      st<TO>(out + om * a.ldo + n, y);
     }
   }
 }
@@ -463,10 +472,11 @@ __global__ __launch_bounds__(256) void e0_lookup_kernel(const ProjArgs a, int32_
   if (item >= a.nrows * cpr) return;
   const int64_t r = item / cpr, c = item - r * cpr;
   const int32_t tk = a.tok[r];
+  if (tk == kSkipRow) return;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (uint32_t(tk) < uint32_t(a.V0))
     v = reinterpret_cast<const uint4*>(static_cast<const char*>(a.E0) + int64_t(tk) * row_bytes)[c];
-  reinterpret_cast<uint4*>(static_cast<char*>(a.out) + r * row_bytes)[c] = v;
+  reinterpret_cast<uint4*>(static_cast<char*>(a.out) + out_row(a, r) * row_bytes)[c] = v;
 }
 
 // Scaled (or fp32-output) rows: one element per thread, fp32 product, one rounding.
@@ -476,10 +486,11 @@ __global__ __launch_bounds__(256) void e0_scaled_kernel(const ProjArgs a) {
   if (item >= a.nrows * a.N) return;
   const int64_t r = item / a.N;
   const int32_t tk = a.tok[r];
+  if (tk == kSkipRow) return;
   float v = 0.f;
   if (uint32_t(tk) < uint32_t(a.V0))
     v = ld<T>(static_cast<const T*>(a.E0) + int64_t(tk) * a.N + (item - r * a.N)) * a.inv;
-  st<TO>(static_cast<TO*>(a.out) + item, v);
+  st<TO>(static_cast<TO*>(a.out) + out_row(a, r) * a.N + (item - r * a.N), v);
 }
 
 // out[m, n] += f * sum_s part[s, m, n]: the split partial sums added in split order (the
@@ -505,7 +516,7 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int osz, hipStream_t st) {
   // at most 2^20 row tiles per launch keeps the tile numbering in 32-bit ints (partial sums
   // are laid out per launch, so they take one launch)
   const int64_t chunk = int64_t(BM) << 20;
-  if (OM == kOutPartial && nrows > chunk) return hipErrorInvalidValue;
+  if ((OM == kOutPartial || a.row_group != 0) && nrows > chunk) return hipErrorInvalidValue;
   const int32_t* idx = a.idx;
   const int32_t* tok = a.tok;
   char* out = static_cast<char*>(a.out);
@@ -557,6 +568,7 @@ hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStre
   const int32_t* idx = a.idx;
   const int32_t* tok = a.tok;
   char* out = static_cast<char*>(a.out);
+  if (a.row_group != 0 && nrows > (int64_t(1) << 30)) return hipErrorInvalidValue;
   for (int64_t r0 = 0; r0 < nrows; r0 += (int64_t(1) << 30)) {
     ProjArgs b = a;
     const int64_t n = nrows - r0 < (int64_t(1) << 30) ? nrows - r0 : (int64_t(1) << 30);
@@ -606,7 +618,8 @@ ProjArgs dense_args(const void* A, int64_t M, const void* B, int32_t N, int32_t 
 
 hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
                           const void* W, const int32_t* idx, const int32_t* tok,
-                          int64_t nrows, void* out, bool f32out, hipStream_t st) {
+                          int64_t nrows, void* out, bool f32out, const RowMap& map,
+                          hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   ProjArgs a{};
   for (int s = 0; s < L.S; ++s) {
@@ -628,6 +641,9 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
   a.V0 = L.V0;
   a.inv = L.scale / float(L.S + 1);
   a.splits = 1;
+  a.row_group = map.group;
+  a.row_stride = map.stride;
+  a.row_off = map.off;
   const int osz = f32out ? 4 : L.esz;   // bytes per output element
   if (L.S == 0) {
     if (!f32out && L.scale == 1.0f) {
@@ -639,6 +655,7 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
     }
     // at most 2^30 rows x D elements per launch keeps the grid in range
     const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 38) / L.D);
+    if (map.group != 0 && nrows > rows_per) return hipErrorInvalidValue;
     for (int64_t r0 = 0; r0 < nrows; r0 += rows_per) {
       ProjArgs b = a;
       b.nrows = std::min(rows_per, nrows - r0);

@@ -63,7 +63,8 @@ enum { NGRAM_F32 = 0, NGRAM_BF16 = 1 };
 enum {
   NGRAM_FLAG_BAD_TOKEN = 1,   /* a token id outside [0, V0) was hashed */
   NGRAM_FLAG_BAD_SEQLENS = 2, /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_nseq = ntok */
-  NGRAM_FLAG_BAD_COUNT = 4    /* n_new or n_accept outside [0, tmax] */
+  NGRAM_FLAG_BAD_COUNT = 4,   /* n_new or n_accept outside [0, tmax] */
+  NGRAM_FLAG_BAD_SLOT = 8     /* a cache slot outside [0, cache->nseq) */
 };
 
 /* Embedding amplification (section 3.2.4): what is applied to e_i before it is written.
@@ -199,6 +200,41 @@ int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* 
 int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
                        const int32_t* new_tokens, const int32_t* n_accept, int32_t tmax,
                        int32_t* err_flags, void* stream);
+
+/* ---------------------------------------------------------------- pooled cache, row windows
+ * For schedulers with dynamic batches and for speculative decoding (section 4.2: the N-gram
+ * cache is managed like a KV cache; n-gram embeddings computed while the draft model
+ * proposes tokens are reused by the verify step).
+ *
+ * The cache is a pool of cache->nseq slots. Batch entry b (0 <= b < nbatch) uses slot
+ * slots[b] (device int32 [nbatch]; NULL means slot b, and then nbatch <= cache->nseq).
+ * Slots of one call must be distinct. An out-of-range slot sets NGRAM_FLAG_BAD_SLOT in the
+ * workspace (or err_flags) and the entry is ignored (no rows written, no commit).
+ *
+ * ngram_embed_decode_rows computes, for each batch entry b, the rows j in
+ * [row_begin, min(row_end, n_new[b])) exactly as ngram_embed_decode would (same bits), and
+ * writes nothing else: rows outside that range keep their contents. Contexts come from the
+ * slot's committed ids and new_tokens[b, 0..j] (ids before row_begin included), so a caller
+ * can fill out[b, j] as each draft id j appears (row_begin = j, row_end = j + 1) and find
+ * every row ready at verify time. 0 <= row_begin < row_end <= tmax <= 8. n_commit (optional)
+ * commits as in ngram_embed_decode. ws: at least
+ * ngram_embed_workspace_size(cfg, nbatch * (row_end - row_begin)) bytes.
+ * ngram_cache_init_slots fills slot slots[b] from sequence b of the packed tokens (entries
+ * joining the pool; other slots untouched); ngram_cache_commit_slots appends the first
+ * n_accept[b] ids of new_tokens[b, :] to slot slots[b]. */
+int ngram_embed_decode_rows(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                            ngram_cache* cache, const int32_t* slots, int32_t nbatch,
+                            const int32_t* new_tokens, const int32_t* n_new, int32_t tmax,
+                            int32_t row_begin, int32_t row_end, const int32_t* n_commit,
+                            void* out, void* ws, size_t ws_bytes, void* stream);
+int ngram_cache_init_slots(const ngram_embed_config* cfg, ngram_cache* cache,
+                           const int32_t* slots, int32_t nbatch, const int32_t* tokens,
+                           const int32_t* cu_seqlens, int64_t ntok, int32_t* err_flags,
+                           void* stream);
+int ngram_cache_commit_slots(const ngram_embed_config* cfg, ngram_cache* cache,
+                             const int32_t* slots, int32_t nbatch, const int32_t* new_tokens,
+                             const int32_t* n_accept, int32_t tmax, int32_t* err_flags,
+                             void* stream);
 
 /* ---------------------------------------------------------------- backward (training)
  * Gradients of the layer for one batch, given the upstream gradient dout = dL/dout

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "ngram_cache_commit", "ngram_embed_backward",
               "ngram_embed_backward_workspace_size"):
         assert n in names
-    assert len(names) == 14
+    assert len(names) == 17
 
 
 def test_library_exports_every_declared_symbol(lib):
