@@ -17,6 +17,14 @@ Section 4.2 (N-gram cache) motivates the decode oracle; its semantics are a read
 the cache holds committed ids, a decode step's outputs equal a prefill over the whole
 history followed by the new ids, and a commit appends accepted ids.
 
+The same section's basic form (Eq. 1), e_i = (E_0(t_i) + sum_{n=2}^{N} E_n(H_n(...))) / N with
+one full-width table E_n in R^{V_n x D} per order and no projection: embed_basic(). Its hash
+H_n is the rolling hash above with one modulus per order (hash_indices with K = 1).
+Per-layer N-gram embedding (PLNE, section 5.2 of the same page): every layer l computes the
+final form with tables and projections of its own; the oracle of layer l is prefill() with
+layer l's parameters (no new arithmetic).
+Hash collisions and vocabulary hit rate (section 3.2.2, Fig. 3): hash_slot_stats().
+
 Readings where the pages are silent:
   * positions before a sequence's first token take the pad id 0, never ids of another
     sequence packed in the same batch;
@@ -123,6 +131,24 @@ def embed_from_indices(D: int, N: int, K: int, tokens: Sequence[int], idx: np.nd
             raise ValueError("sub-table rows must be [T, D/S] and W_{n,k} [D, D/S]")
         acc += rows @ Wnk.T                                                 # W_{n,k} E_{n,k}(.)
     return acc / float(S + 1)                                               # / ((N-1)K + 1)
+
+
+def embed_basic(D: int, N: int, tokens: Sequence[int], idx: np.ndarray,
+                fetch: RowFetch) -> np.ndarray:
+    """float64 [T, D]: the basic N-gram embedding (section A2, Eq. 1) given the hash indices,
+        e_i = ( E_0(t_i) + sum_{n=2}^{N} E_n(H_n(t_{i-n+1..i})) ) / N,
+    with one full-width table E_n [V_n, D] per order and no projection. idx[:, n-2] holds
+    H_n (hash_indices with K = 1); fetch(n-2, rows) reads E_n."""
+    tok = np.asarray(tokens, dtype=np.int64)
+    acc = np.asarray(fetch(-1, tok), dtype=np.float64).copy()              # E_0(t_i)
+    if acc.shape != (len(tok), D):
+        raise ValueError("E_0 rows must be [T, D]")
+    for n in range(2, N + 1):
+        rows = np.asarray(fetch(n - 2, idx[:, n - 2]), dtype=np.float64)   # E_n(H_n)
+        if rows.shape != (len(tok), D):
+            raise ValueError("basic-form tables have full rows [T, D]")
+        acc += rows
+    return acc / float(N)
 
 
 def table_fetch(E0, E_list) -> RowFetch:
@@ -261,3 +287,27 @@ def param_count(V0: int, D: int, N: int, K: int, V: Sequence[int]) -> dict:
     S = num_subtables(N, K)
     d = D // S if S else 0
     return {"E0": V0 * D, "ngram_tables": sum(int(v) * d for v in V), "projections": S * D * d}
+
+
+def hash_slot_stats(V0: int, n: int, tokens: Sequence[int], cu_seqlens: Sequence[int],
+                    vocab_sizes: Sequence[int]):
+    """Hash collisions of the n-gram hash (section 3.2.2 and Fig. 3 of the deep-notes page).
+
+    Over every position of the packed sequences (the n-grams the layer hashes, pad id 0
+    before a sequence's start), returns (distinct, slots): `distinct` is the number of
+    different n-grams, and slots[v] the number of different table rows H_n = (n-gram value)
+    mod vocab_sizes[v] that they occupy. The pages count collisions as the unique n-grams
+    lost to the modulo (reading: distinct - slots) and the hit rate as the share of table
+    rows used at least once (slots / V)."""
+    tokens = [int(t) for t in tokens]
+    if any(t < 0 or t >= V0 for t in tokens):
+        raise ValueError("token id outside [0, V0)")
+    if n < 1:
+        raise ValueError("n must be positive")
+    values = set()
+    for b in range(len(cu_seqlens) - 1):
+        seq = tokens[int(cu_seqlens[b]):int(cu_seqlens[b + 1])]
+        for i in range(len(seq)):
+            values.add(ngram_value(context(seq, i, n), n, V0))
+    slots = [len({x % int(V) for x in values}) for V in vocab_sizes]
+    return len(values), slots
