@@ -19,7 +19,8 @@ history followed by the new ids, and a commit appends accepted ids.
 
 The same section's basic form (Eq. 1), e_i = (E_0(t_i) + sum_{n=2}^{N} E_n(H_n(...))) / N with
 one full-width table E_n in R^{V_n x D} per order and no projection: embed_basic(). Its hash
-H_n is the rolling hash above with one modulus per order (hash_indices with K = 1).
+H_n is the rolling hash above with one modulus per order (hash_indices with K = 1);
+backward_basic() gives its plain gradients.
 Per-layer N-gram embedding (PLNE, section 5.2 of the same page): every layer l computes the
 final form with tables and projections of its own; the oracle of layer l is prefill() with
 layer l's parameters (no new arithmetic).
@@ -280,6 +281,28 @@ def backward(D: int, N: int, K: int, tokens: Sequence[int], idx: np.ndarray, dou
         np.add.at(dEs, np.asarray(idx[:, s], dtype=np.int64), grad_rows)
         dE.append(dEs)
     return dE0, dE, dW
+
+
+def backward_basic(D: int, N: int, tokens: Sequence[int], idx: np.ndarray, dout: np.ndarray,
+                   V0: int, V: Sequence[int], scale: float = 1.0):
+    """Gradients of the basic form (section A2, Eq. 1) for one batch, float64: with
+    e_i = c (E_0(t_i) + sum_n E_n(h_{i,n})), c = scale / N and dout = dL/de [T, D],
+      dE_0[t] = c * sum over positions i with t_i = t of dout_i,
+      dE_n[r] = c * sum over positions i with h_{i,n} = r of dout_i   (no projection).
+    Returns (dE0 [V0, D], [dE_n [V_n, D] for n = 2..N])."""
+    tok = np.asarray(tokens, dtype=np.int64)
+    g = np.asarray(dout, dtype=np.float64)
+    if g.shape != (len(tok), D):
+        raise ValueError("dout must be [T, D]")
+    c = float(scale) / float(N)
+    dE0 = np.zeros((V0, D))
+    np.add.at(dE0, tok, c * g)
+    dE = []
+    for n in range(2, N + 1):
+        dEn = np.zeros((int(V[n - 2]), D))
+        np.add.at(dEn, np.asarray(idx[:, n - 2], dtype=np.int64), c * g)
+        dE.append(dEn)
+    return dE0, dE
 
 
 def param_count(V0: int, D: int, N: int, K: int, V: Sequence[int]) -> dict:

@@ -2,7 +2,8 @@
 
 Basic form (section A2, Eq. 1: full-width tables, no projection, divided by N): hand-worked
 rational values, N = 1, the special case N = 2 where the final form with K = 1 and an
-identity projection is the same layer, linearity, and planted mistakes.
+identity projection is the same layer, linearity, and planted mistakes; its backward
+against finite differences and the final form's backward in that special case.
 Hash collisions and hit counts (section 3.2.2, Fig. 3): hand-worked counts, brute force over
 context tuples, the closed form at table sizes that are multiples of V0 (the spikes of
 Fig. 3b), sizes above every n-gram value, and planted mistakes.
@@ -113,6 +114,69 @@ def test_basic_pins_catch_planted_mistakes(monkeypatch, mistake):
         return real(D, N, tokens, idx, swapped)
     monkeypatch.setattr(O, "embed_basic", planted)
     assert _fails(check_basic_golden)
+
+
+def check_basic_backward():
+    """Directional finite differences of L = <dout, e> through embed_basic (exact for a
+    linear map, up to rounding), and the final form's backward with N = 2, K = 1, W = I."""
+    rng = np.random.default_rng(8)
+    V0, D, N, V, E0, E, tokens, cu = _basic_case(rng, V0=9, N=4, lengths=(30, 2, 11))
+    idx = oracle.hash_indices(V0, N, 1, V, tokens, cu)
+    dout = rng.standard_normal((len(tokens), D))
+    scale = 1.7
+    dE0, dE = O.backward_basic(D, N, tokens, idx, dout, V0, V, scale)
+
+    def loss(E0_, E_):
+        return float((dout * scale * O.embed_basic(D, N, tokens, idx,
+                                                   oracle.table_fetch(E0_, E_))).sum())
+    P0 = rng.standard_normal(E0.shape)
+    P = [rng.standard_normal(e.shape) for e in E]
+    h = 1e-3
+    fd = (loss(E0 + h * P0, [e + h * p for e, p in zip(E, P)]) -
+          loss(E0 - h * P0, [e - h * p for e, p in zip(E, P)])) / (2 * h)
+    an = float((dE0 * P0).sum() + sum((g * p).sum() for g, p in zip(dE, P)))
+    assert abs(fd - an) <= 1e-8 * max(1.0, abs(an)), (fd, an)
+    # per table, not only in sum: each table alone
+    for n in range(N - 1):
+        Pn = [np.zeros_like(e) for e in E]
+        Pn[n] = P[n]
+        fdn = (loss(E0, [e + h * p for e, p in zip(E, Pn)]) -
+               loss(E0, [e - h * p for e, p in zip(E, Pn)])) / (2 * h)
+        assert abs(fdn - float((dE[n] * P[n]).sum())) <= 1e-8 * max(1.0, abs(fdn)), n
+    # N = 2: the final form with K = 1 and W = I has the same table gradients
+    V0, D, N, V, E0, E, tokens, cu = _basic_case(rng, V0=9, N=2, lengths=(25,))
+    idx = oracle.hash_indices(V0, 2, 1, V, tokens, cu)
+    dout = rng.standard_normal((len(tokens), D))
+    a0, a = O.backward_basic(D, 2, tokens, idx, dout, V0, V, scale)
+    b0, b, _ = oracle.backward(D, 2, 1, tokens, idx, dout, oracle.table_fetch(E0, E),
+                               [np.eye(D)], V0, V, scale)
+    np.testing.assert_allclose(a0, b0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-13)
+
+
+def test_basic_backward():
+    check_basic_backward()
+
+
+@pytest.mark.parametrize("mistake", ["norm_over_N_minus_1", "orders_swapped", "no_repeats"])
+def test_basic_backward_pins_catch_planted_mistakes(monkeypatch, mistake):
+    real = O.backward_basic
+
+    def planted(D, N, tokens, idx, dout, V0, V, scale=1.0):
+        if mistake == "norm_over_N_minus_1":
+            return real(D, N, tokens, idx, dout, V0, V, scale * N / max(N - 1, 1))
+        if mistake == "orders_swapped":
+            dE0, dE = real(D, N, tokens, idx, dout, V0, V, scale)
+            return dE0, dE[::-1]
+        # duplicates overwrite instead of accumulating
+        dE0, dE = real(D, N, tokens, idx, dout, V0, V, scale)
+        c = scale / N
+        for n in range(N - 1):
+            dE[n][:] = 0
+            dE[n][np.asarray(idx[:, n])] = c * np.asarray(dout)
+        return dE0, dE
+    monkeypatch.setattr(O, "backward_basic", planted)
+    assert _fails(check_basic_backward)
 
 
 # ------------------------------------------------------------------ collisions (section 3.2.2)
