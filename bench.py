@@ -140,6 +140,8 @@ def main():
                     help="skip the backward (training gradients) timing")
     ap.add_argument("--no-amp", action="store_true",
                     help="skip the amplified (scale / layer-norm) prefill timings")
+    ap.add_argument("--no-basic", action="store_true",
+                    help="skip the basic-form (Eq. 1) prefill timing")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-batches", type=int, default=4,
                     help="benchmark batches of 64K tokens the CPU oracle is timed on")
@@ -258,6 +260,10 @@ def main():
     if not args.no_decode:
         decode = bench_decode(g, WL, cfg, tables, dev, stream, args.decode_steps)
 
+    basic = None
+    if not args.no_basic:
+        basic = bench_basic(g, WL, dev, stream, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_batches} batches")
@@ -281,6 +287,7 @@ def main():
         "amplification": amp,
         "backward": backward,
         "decode": decode,
+        "basic_form": basic,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -333,6 +340,61 @@ def bench_amplification(g, w, tables, toks, cu, dev, stream, steps):
     res["layernorm"]["norm_pass_bytes"] = T * w.D * (4 + 2)
     log(f"prefill: plain {res['none']['us_per_step']:.0f} us, x sqrt(D) "
         f"{res['scale']['us_per_step']:.0f} us, layer norm {res['layernorm']['us_per_step']:.0f} us")
+    return res
+
+
+def bench_basic(g, WL, dev, stream, steps):
+    """The basic form (section A2, Eq. 1) with ~30B parameters (3 full-width tables of
+    3.2M x 3072 bf16) on 64K-token batches: hash, then the gather-sum kernel, HIP events
+    around each on the launch stream. No contraction: the sum kernel is bound by HBM, with
+    N rows read and one written per token."""
+    import numpy as np
+    import torch
+
+    torch.cuda.empty_cache()
+    w = WL.workload("prefill_64k_basic_30b")
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V), form="basic")
+    log(f"basic form: generating {sum(w.V) * w.D * 2 / 1e9:.1f} GB of tables")
+    E0, E, _ = WL.device_tables(w, device=dev)
+    tables = g.Tables(E0, E, None)
+    T = w.T
+    toks = [torch.as_tensor(WL.token_batch(w, purpose=p).reshape(-1)).to(dev) for p in range(4)]
+    cu = torch.as_tensor(np.arange(w.batch + 1, dtype=np.int32) * w.seqlen).to(dev)
+    out = torch.empty((T, w.D), dtype=torch.bfloat16, device=dev)
+    ws = g.alloc_workspace(cfg, T, device=dev)
+    _, idx_off = g.ngram_embed_workspace_layout(cfg, T)
+    idx = ws[idx_off:].view(torch.int32)
+    for k in range(3):
+        g.ngram_embed_prefill(cfg, tables, toks[k % 4], cu, out, ws, stream=stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        g.ngram_embed_hash(cfg, toks[k % 4], cu, idx, ws, stream=stream)
+        ev[k][1].record(stream)
+        g.ngram_embed_project(cfg, tables, idx, toks[k % 4], out, stream=stream)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = (time.perf_counter() - t0) / steps
+    if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+        raise RuntimeError("device error flags set in the basic-form prefill")
+    t_hash = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_sum = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    # per token: N rows of D bf16 read (E_0 and the N-1 tables), one written, the ids
+    per_tok = w.N * w.D * 2 + w.D * 2 + w.S * 4 + 4
+    gbs = T * per_tok / t_sum / 1e9
+    res = {"workload": w.name, "form": "basic (Eq. 1)", "ngram_params": sum(w.V) * w.D,
+           "tokens_per_s": round(T / wall, 1), "ms_per_step": round(wall * 1e3, 4),
+           "kernels_us": {"hash": round(t_hash * 1e6, 1), "sum": round(t_sum * 1e6, 1)},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "kernel": "basic_sum_kernel<unsigned short, unsigned short>",
+                        "bytes_per_token": per_tok}}
+    log(f"basic form: step {wall*1e6:.0f} us, hash {t_hash*1e6:.1f} us, sum {t_sum*1e6:.1f} us "
+        f"({gbs:.0f} GB/s)")
+    del E0, E, tables, out, ws, idx
+    torch.cuda.empty_cache()
     return res
 
 

@@ -38,6 +38,9 @@ NGRAM_FLAG_BAD_SLOT = 8
 NGRAM_MAX_DECODE_TOKENS = 8
 # embedding amplification modes (NGRAM_AMP_NONE / SCALE / LAYERNORM)
 AMP_MODES = {"none": 0, "scale": 1, "layernorm": 2}
+# forms of the layer (NGRAM_FORM_FINAL / NGRAM_FORM_BASIC)
+NGRAM_FORM_FINAL, NGRAM_FORM_BASIC = 0, 1
+FORMS = {"final": NGRAM_FORM_FINAL, "basic": NGRAM_FORM_BASIC}
 
 
 class NgramError(RuntimeError):
@@ -50,7 +53,8 @@ class _CConfig(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("V0", ctypes.c_int64),
                 ("V", ctypes.POINTER(ctypes.c_int64)), ("amp", ctypes.c_int32),
-                ("amp_scale", ctypes.c_float), ("ln_eps", ctypes.c_float)]
+                ("amp_scale", ctypes.c_float), ("ln_eps", ctypes.c_float),
+                ("form", ctypes.c_int32)]
 
 
 class _CTables(ctypes.Structure):
@@ -116,8 +120,9 @@ def load():
 
 @dataclass
 class Config:
-    """Mirror of ngram_embed_config: N, K, D, dtype ("f32"/"bf16" or 0/1), V0, V_{n,k}, and
-    the amplification: amp in AMP_MODES, amp_scale (None: sqrt(D)), ln_eps."""
+    """Mirror of ngram_embed_config: N, K, D, dtype ("f32"/"bf16" or 0/1), V0, V_{n,k}, the
+    amplification (amp in AMP_MODES, amp_scale (None: sqrt(D)), ln_eps) and the form
+    ("final", or "basic": Eq. 1 with K = 1, full-width tables, no projection)."""
     N: int
     K: int
     D: int
@@ -127,14 +132,21 @@ class Config:
     amp: object = "none"
     amp_scale: Optional[float] = None
     ln_eps: float = 1e-5
+    form: object = "final"
 
     @property
     def S(self) -> int:
         return (self.N - 1) * self.K
 
     @property
+    def form_code(self) -> int:
+        return FORMS[self.form] if isinstance(self.form, str) else int(self.form)
+
+    @property
     def d(self) -> int:
-        return self.D // self.S if self.S else 0
+        if not self.S:
+            return 0
+        return self.D if self.form_code == NGRAM_FORM_BASIC else self.D // self.S
 
     @property
     def dtype_code(self) -> int:
@@ -153,7 +165,7 @@ class Config:
         scale = float(self.D) ** 0.5 if self.amp_scale is None else float(self.amp_scale)
         c = _CConfig(int(self.N), int(self.K), int(self.D), self.dtype_code, int(self.V0),
                      ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), self.amp_code, scale,
-                     float(self.ln_eps))
+                     float(self.ln_eps), self.form_code)
         return c, arr
 
 

@@ -11,7 +11,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 // Tables: E0 and W always; the S sub-table pointers when S > 0. All 16-byte aligned.
 int check_tables(const LayerDesc& L, const ngram_embed_tables* T, bool need_e0_w) {
   if (T == nullptr) return NGRAM_EALIGN;
-  if (need_e0_w && (!ngram::aligned(T->E0, 16) || !ngram::aligned(T->W, 16)))
+  // the basic form has no projection: W is not read
+  if (need_e0_w && (!ngram::aligned(T->E0, 16) ||
+                    (L.form == NGRAM_FORM_FINAL && !ngram::aligned(T->W, 16))))
     return NGRAM_EALIGN;
   if (L.S > 0) {
     if (T->E == nullptr) return NGRAM_EALIGN;
@@ -315,6 +317,7 @@ int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables
   int rc = ngram::describe(cfg, &L);
   if (rc != NGRAM_OK) return rc;
   if (L.amp == NGRAM_AMP_LAYERNORM) return NGRAM_EINVAL;   // not differentiated here
+  if (L.form == NGRAM_FORM_BASIC && dW != nullptr) return NGRAM_EINVAL;   // no projection
   if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
   // positions are sort values (uint32) and the tile numbering stays in range
   if (ntok > (int64_t(1) << 31) / (L.S > 0 ? L.S : 1)) return NGRAM_EINVAL;

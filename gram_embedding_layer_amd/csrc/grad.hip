@@ -19,14 +19,13 @@
 // which adds the later chunks' partial sums in order.
 #include <algorithm>
 
+#include "bf16.h"
 #include "kernels.h"
 
 namespace ngram {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 template <typename T> __device__ __forceinline__ float ldf(const T* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
@@ -344,7 +343,8 @@ struct SegArgs {
   uint64_t sentinel;
   int32_t width;                     // gradient row width (D for E_0, d for sub-tables)
   int32_t chunk;                     // sorted entries per chunk
-  int32_t by_table;                  // 1: key = (s << 31) | r, source columns s*width...
+  int32_t by_table;                  // 1: key = (s << 31) | r, source columns s*col_step...
+  int32_t col_step;                  // source columns per key class (0: all read column 0)
   float factor;                      // applied to source rows (c for dout, 1 for dG)
 };
 
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(THREADS) void segsum_level1_kernel(const SegArgs a)
       const uint64_t key = live ? skey[j + 1] : 0;
       const int s = a.by_table ? int(key >> 31) : 0;
       const T* row = static_cast<const T*>(a.src) + int64_t(live ? sval[j] : 0) * a.ld_src +
-                     s * a.width;
+                     s * a.col_step;
       const bool last = j + 1 == cnt;
       const bool ends = live && (last ? !(has_next && skey[cnt + 1] == key) : skey[j + 2] != key);
       const bool owned = ends && !(cont_in && key == skey[1]);   // added here, directly
@@ -586,15 +586,17 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
   const int64_t Tp = (T + 63) / 64 * 64;
   const int64_t D = L.D;
   const float c = L.scale / float(L.S + 1);
+  // the basic form has no projection: dE_s sums c dout rows directly, and there is no dW
+  const bool basic = L.form == NGRAM_FORM_BASIC;
   const bool need_dg = L.S > 0 && b.dE != nullptr;
-  const bool need_dw = L.S > 0 && b.dW != nullptr;
+  const bool need_dw = L.S > 0 && b.dW != nullptr && !basic;
   hipError_t e;
   const int64_t nid = std::max<int64_t>(T, D);
   hipLaunchKernelGGL(iota_kernel, dim3(unsigned((nid + 255) / 256)), dim3(256), 0, st, b.ident,
                      nid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const bool f32 = L.dtype == NGRAM_F32;
-  if (need_dg) {
+  if (need_dg && !basic) {
     // W^T, then dG = c dout (W^T)^T = c dout W
     const dim3 g((unsigned((D + kTile - 1) / kTile)), unsigned((D + kTile - 1) / kTile));
     if (f32)
@@ -664,7 +666,7 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     for (int s = 0; s < L.S; ++s) a.dst[s] = b.dE[s];
     a.keys = b.keys0;
     a.vals = b.vals0;
-    a.src = b.dG;
+    a.src = basic ? b.dout : static_cast<const void*>(b.dG);
     a.head = b.head;
     a.tail = b.tail;
     a.owners = b.owners;
@@ -673,8 +675,9 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     a.sentinel = sentinel;
     a.width = L.d;
     a.by_table = 1;
-    a.factor = 1.0f;
-    if ((e = segsum(a, true, st)) != hipSuccess) return e;
+    a.col_step = basic ? 0 : L.d;
+    a.factor = basic ? c : 1.0f;
+    if ((e = segsum(a, basic ? f32 : true, st)) != hipSuccess) return e;
   }
   if (b.dE0 != nullptr) {
     // dE_0: sort tokens, sum c * dout rows of each run

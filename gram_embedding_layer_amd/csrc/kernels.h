@@ -63,6 +63,12 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
                           int64_t nrows, void* out, bool f32out, const RowMap& map,
                           hipStream_t st);
 
+// the basic form (Eq. 1): out = (E_0 row + the S full-width table rows) / (S + 1), times the
+// output factor; f32out and map as for launch_project (which calls it in that form)
+hipError_t launch_basic(const LayerDesc& L, const void* E0, const void* const* E,
+                        const int32_t* idx, const int32_t* tok, int64_t nrows, void* out,
+                        bool f32out, const RowMap& map, hipStream_t st);
+
 // dense product for the backward: out = inv * A B^T (fp32, overwritten) or, with
 // accumulate, out += inv * A B^T through `splits` fp32 partial sums in `part`
 // ([splits, M, ldo]) added in split order. A [M, K] and B [N, K] row-major in the config

@@ -14,7 +14,8 @@ struct LayerDesc {
   int32_t K;       // sub-tables per order
   int32_t S;       // (N-1)K
   int32_t D;       // hidden size
-  int32_t d;       // sub-table width D/S (0 when S == 0)
+  int32_t d;       // sub-table width: D/S in the final form, D in the basic form (0 when S == 0)
+  int32_t form;    // NGRAM_FORM_FINAL / NGRAM_FORM_BASIC
   int32_t dtype;   // NGRAM_F32 / NGRAM_BF16
   int32_t esz;     // bytes per element
   int32_t V0;      // base vocabulary

@@ -15,6 +15,7 @@
 // 2% faster on the 64K-token batch). HBM-bound: 4D bytes read and D * esz written per row.
 #include <algorithm>
 
+#include "bf16.h"
 #include "kernels.h"
 
 namespace ngram {
@@ -25,16 +26,6 @@ constexpr int kRowsPerBlock = kThreads / 64;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 // Sum over the wave in a fixed order (butterfly): every lane ends with the same total.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -27,6 +27,7 @@
 // tiles x 8 output tiles, which keeps their A rows and W panels in that XCD's L2.
 #include <algorithm>
 
+#include "bf16.h"
 #include "kernels.h"
 
 namespace ngram {
@@ -37,16 +38,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte vector
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 // One product out[m, n] = inv * (E0[tok[m], n] + sum_k A[m, k] B[n, k]) over nrows rows m and
 // N outputs n, with A's row m the concatenation of the S gathered rows E[s][idx[m, s]] (K
@@ -621,6 +612,8 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
                           int64_t nrows, void* out, bool f32out, const RowMap& map,
                           hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
+  if (L.form == NGRAM_FORM_BASIC && L.S > 0)
+    return launch_basic(L, E0, E, idx, tok, nrows, out, f32out, map, st);
   ProjArgs a{};
   for (int s = 0; s < L.S; ++s) {
     a.E[s] = E[s];

@@ -22,10 +22,15 @@ int describe(const ngram_embed_config* cfg, LayerDesc* out) {
   L.dtype = cfg->dtype;
   L.esz = esz;
   L.V0 = int32_t(cfg->V0);
+  // The final form, or the basic form of Eq. 1 (one full-width table per order).
+  if (cfg->form != NGRAM_FORM_FINAL && cfg->form != NGRAM_FORM_BASIC) return NGRAM_EINVAL;
+  if (cfg->form == NGRAM_FORM_BASIC && cfg->K != 1) return NGRAM_EINVAL;
+  L.form = cfg->form;
   if (S > 0) {
-    // Sub-table width D/((N-1)K) (section A2); rows must be whole 16-byte vectors.
-    if (cfg->D % S != 0) return NGRAM_EINVAL;
-    L.d = int32_t(cfg->D / S);
+    // Sub-table width D/((N-1)K) (section A2), or D in the basic form; rows must be whole
+    // 16-byte vectors.
+    if (L.form == NGRAM_FORM_FINAL && cfg->D % S != 0) return NGRAM_EINVAL;
+    L.d = L.form == NGRAM_FORM_BASIC ? cfg->D : int32_t(cfg->D / S);
     if ((int64_t(L.d) * esz) % 16 != 0) return NGRAM_EINVAL;
     if (cfg->V == nullptr) return NGRAM_EINVAL;
     uint64_t vmax = 0;
@@ -93,7 +98,7 @@ bool bw_layout(const LayerDesc& L, int64_t rows, BwLayout* out) {
   const size_t seg_s = (T * S + kChunk - 1) / kChunk * size_t(L.d);
   const size_t seg_0 = (T + kChunk - 1) / kChunk * D;
   const size_t seg = seg_s > seg_0 ? seg_s : seg_0;
-  const bool tables = S > 0;
+  const bool tables = S > 0 && L.form == NGRAM_FORM_FINAL;   // the products' operands
   BwLayout w;
   size_t o = 256;                                    // error flags
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };

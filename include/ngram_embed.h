@@ -16,7 +16,12 @@
  * shape [D, d]. Section 4.2 of that page (N-gram cache, KV-cache-like management of n-gram
  * ids on the device) motivates the decode entry points. Section 3.2.4 of the same page
  * (embedding amplification) gives the optional output scale or layer normalisation that
- * the config's `amp` field selects.
+ * the config's `amp` field selects. The config's `form` field selects instead the basic
+ * form of the same section (its Eq. 1):
+ *
+ *   e_i = ( E_0(t_i) + sum_{n=2}^{N} E_n(H_n(t_{i-n+1..i})) ) / N,
+ *
+ * one table E_n of full width D per order (K = 1), no projection.
  *
  * Conventions used throughout:
  *  - S = (N-1)K sub-tables, ordered s = (n-2)*K + (k-1) (n-major, k-minor).
@@ -79,6 +84,16 @@ enum {
                               decode), so ngram_embed_project rejects it */
 };
 
+/* Form of the layer (section A2). In the basic form there are S = N-1 tables E[s] = E_{s+2}
+ * of shape [V_{s+2}, D] (d = D), the hash is the same with one modulus per order, W is not
+ * read (may be NULL), and every entry point works as for the final form with
+ * W_{n,k} E_{n,k}(.) replaced by E_n(.) and (N-1)K + 1 by N. ngram_embed_gather then writes
+ * G [nrows, (N-1)*D]. */
+enum {
+  NGRAM_FORM_FINAL = 0,  /* the final (Over-Encoding) form, with projections */
+  NGRAM_FORM_BASIC = 1   /* the basic form (Eq. 1): K must be 1 */
+};
+
 #define NGRAM_MAX_ORDER 16         /* largest accepted N */
 #define NGRAM_MAX_SUBTABLES 64     /* largest accepted (N-1)K */
 #define NGRAM_MAX_DECODE_TOKENS 8  /* largest accepted tmax (1 + speculative drafts) */
@@ -87,7 +102,8 @@ enum {
 typedef struct ngram_embed_config {
   int32_t N;         /* largest n-gram order, 1 <= N <= NGRAM_MAX_ORDER */
   int32_t K;         /* sub-tables (hash functions) per order, K >= 1, (N-1)K <= 64 */
-  int32_t D;         /* hidden size; D % ((N-1)K) == 0 and the sub-table row
+  int32_t D;         /* hidden size; D * sizeof(dtype) is a multiple of 16 bytes, and in
+                        the final form D % ((N-1)K) == 0 and the sub-table row
                         d * sizeof(dtype) is a multiple of 16 bytes */
   int32_t dtype;     /* NGRAM_F32 or NGRAM_BF16 */
   int64_t V0;        /* base vocabulary, 1 <= V0 < 2^31 */
@@ -97,6 +113,7 @@ typedef struct ngram_embed_config {
   float amp_scale;   /* NGRAM_AMP_SCALE: the factor, finite (ignored otherwise) */
   float ln_eps;      /* NGRAM_AMP_LAYERNORM: variance epsilon, finite and > 0; the layer
                         normalisation also needs D <= 8192 (ignored otherwise) */
+  int32_t form;      /* NGRAM_FORM_*; 0 is the final form */
 } ngram_embed_config;
 
 /* Parameters of the layer, all in device memory, in the config's dtype. Every device
@@ -104,7 +121,8 @@ typedef struct ngram_embed_config {
 typedef struct ngram_embed_tables {
   const void* E0;        /* [V0, D] base embedding E_0 */
   const void* const* E;  /* host array of S device pointers; E[s] is E_{n,k} [V_{n,k}, d] */
-  const void* W;         /* [D, D] stacked projection: W[o, s*d + c] = W_{n,k}[o, c] */
+  const void* W;         /* [D, D] stacked projection: W[o, s*d + c] = W_{n,k}[o, c]
+                            (final form only) */
   const void* ln_weight; /* [D] layer-normalisation weight, or NULL for all ones (read only
                             with NGRAM_AMP_LAYERNORM) */
   const void* ln_bias;   /* [D] layer-normalisation bias, or NULL for zeros (same) */
@@ -250,7 +268,9 @@ int ngram_cache_commit_slots(const ngram_embed_config* cfg, ngram_cache* cache,
  * [D, D]; any of them may be NULL to skip it. Positions whose token is outside [0, V0)
  * contribute nothing (their forward rows are zero). The result does not depend on thread
  * timing: repeated ids are summed in position order (sort + segmented sums, no atomics).
- * NGRAM_AMP_LAYERNORM is not differentiated here (NGRAM_EINVAL). tokens/cu_seqlens/nseq as
+ * NGRAM_AMP_LAYERNORM is not differentiated here (NGRAM_EINVAL). In the basic form there is
+ * no W: dE[s][r, :] += c * sum over positions i with h_{i,s} = r of dout[i, :], with
+ * c = amp_scale / N or 1 / N, and dW must be NULL (else NGRAM_EINVAL). tokens/cu_seqlens/nseq as
  * in ngram_embed_prefill; ntok * max(S, 1) < 2^31. ws: at least
  * ngram_embed_backward_workspace_size(cfg, ntok) bytes, 256-byte aligned, flags at offset 0
  * as for the forward workspace (bad ids set NGRAM_FLAG_BAD_TOKEN). */

@@ -89,6 +89,8 @@ def test_workspace_size_and_layout(lib):
     (dict(V0=2 ** 31), -1),
     (dict(V=[5003, 0, 6007, 8009]), -1),
     (dict(V=[5003, 2 ** 31, 6007, 8009]), -1),
+    (dict(form="basic"), -1),               # the basic form has K = 1
+    (dict(form=2), -1),
 ])
 def test_config_validation(lib, kw, status):
     cfg = tiny_cfg(**kw)
@@ -225,6 +227,13 @@ def test_backward_argument_checks(lib):
     assert bw(P(cl), P(T), FAKE, FAKE, 1, 16, FAKE, None, None, None, FAKE, ws, 0) == -1
     # an empty batch succeeds without touching the device
     assert bw(P(c), P(T), FAKE, FAKE, 0, 0, FAKE, FAKE, None, FAKE, FAKE, ws, 0) == 0
+    # the basic form has no projection: dW must be NULL; W itself is never read
+    cb, keep4 = tiny_cfg(form="basic", K=1, V=[5003, 7001])._c()
+    Tb, keep5 = _tables_c(2, w=None)
+    wsb = g.ngram_embed_backward_workspace_size(tiny_cfg(form="basic", K=1, V=[5003, 7001]), 16)
+    assert 0 < wsb < ws
+    assert bw(P(cb), P(Tb), FAKE, FAKE, 1, 16, FAKE, None, None, FAKE, FAKE, wsb, 0) == -1
+    assert bw(P(cb), P(Tb), FAKE, FAKE, 1, 16, FAKE + 8, None, None, None, FAKE, wsb, 0) == -3
 
 
 def test_zero_sized_calls_enqueue_nothing(lib):

@@ -38,11 +38,12 @@ def small_workload(dtype="bf16", V0=1000, D=256, N=3, K=2, seed=11):
 
 
 def host_to_dev_tables(w):
-    """Seeded tables on the device: drawn on the host when small, else on the device."""
-    n = w.V0 * w.D + sum(w.V) * w.d + w.D * w.D
+    """Seeded tables on the device: drawn on the host when small, else on the device (W is
+    None in the basic form)."""
+    n = w.V0 * w.D + sum(w.V) * w.d + (w.D * w.D if w.form == "final" else 0)
     if n <= 8_000_000:
         E0, E, W = WL.host_tables(w)
-        return E0.cuda(), [e.cuda() for e in E], W.cuda()
+        return E0.cuda(), [e.cuda() for e in E], (W.cuda() if W is not None else None)
     return WL.device_tables(w)
 
 

@@ -14,13 +14,16 @@ def _is_prime(x):
 def test_workload_shapes(name):
     w = W.workload(name)
     assert len(w.V) == w.S and len(set(w.V)) == w.S
-    assert w.D % w.S == 0
-    # sub-table width D/((N-1)K); 16-byte rows so every row load is a whole vector
+    if w.form == "final":
+        assert w.D % w.S == 0
+    else:                                   # Eq. 1: one full-width table per order
+        assert w.K == 1 and w.d == w.D
+    # sub-table width D/((N-1)K) (D in the basic form); 16-byte rows: whole-vector loads
     assert (w.d * w.esz) % 16 == 0
     assert w.V0 * max(w.V) < 2 ** 63
 
 
-@pytest.mark.parametrize("name", [n for n in W.WORKLOADS if n != "tiny_f32"])
+@pytest.mark.parametrize("name", [n for n in W.WORKLOADS if "tiny" not in n])
 def test_subtable_sizes_are_mid_gap_primes(name):
     # Section 3.2.2: keep V_{n,k} away from integer multiples of V0.
     w = W.workload(name)
@@ -42,6 +45,19 @@ def test_param_scale_of_30b_workload():
     n_params = sum(v * w.d for v in w.V)
     assert 29.9e9 < n_params < 30.1e9
     assert w.T == 65536
+
+
+def test_param_scale_of_basic_30b_workload():
+    w = W.workload("prefill_64k_basic_30b")
+    assert sum(v * w.D for v in w.V) == pytest.approx(29.6e9, rel=0.01)
+    assert w.T == 65536 and w.form == "basic"
+    assert W.mid_gap_primes(131072, 3260000, 3) == list(w.V)
+
+
+def test_basic_tables_have_no_projection():
+    E0, E, Wm = W.host_tables(W.workload("basic_tiny_f32"))
+    assert Wm is None and tuple(E0.shape) == (1000, 64)
+    assert [tuple(e.shape) for e in E] == [(5003, 64), (7001, 64)]
 
 
 def test_mid_gap_primes_rule():

@@ -92,6 +92,24 @@ int main() {
   EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
   amp.amp = -1;
   EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
+  // the basic form (Eq. 1): K = 1, full-width tables (d = D, no divisibility by S)
+  ngram_embed_config basic{4, 1, 64, NGRAM_BF16, 1000, V};
+  EXPECT(ngram::describe(&basic, &L) == NGRAM_EINVAL);      // final form: 64 % 3 != 0
+  basic.form = NGRAM_FORM_BASIC;
+  EXPECT(ngram::describe(&basic, &L) == NGRAM_OK && L.S == 3 && L.d == 64 &&
+         L.form == NGRAM_FORM_BASIC);
+  ngram::BwLayout bl;                                        // no product operands
+  EXPECT(ngram::bw_layout(L, 100, &bl) && bl.wt_off == bl.ident_off + 512 &&
+         bl.dg_off == bl.wt_off && bl.part_off == bl.wt_off);
+  LayerDesc Lb{};
+  basic.D = 68;                                              // 136 bytes: not 16-byte rows
+  EXPECT(ngram::describe(&basic, &Lb) == NGRAM_EINVAL);
+  basic.D = 64;
+  basic.K = 2;                                               // one table per order
+  EXPECT(ngram::describe(&basic, &Lb) == NGRAM_EINVAL);
+  basic.K = 1;
+  basic.form = 2;
+  EXPECT(ngram::describe(&basic, &Lb) == NGRAM_EINVAL);
   EXPECT(ngram::aligned(reinterpret_cast<void*>(0x1000), 256));
   EXPECT(!ngram::aligned(reinterpret_cast<void*>(0x1004), 16));
   EXPECT(!ngram::aligned(nullptr, 4));

@@ -10,6 +10,9 @@ Sources (web notes on "Scaling Embeddings Outperforms Scaling Experts in Languag
   * sub-table sizes are kept well away from integer multiples of V0: section 3.2.2 and the
     2-gram collision plot (Fig. 3b). Every size below sits half-way between two multiples.
   * N in 3..5 and K >= 2 are the robust range: section 3.2.3 (Fig. 4).
+  * the basic form (section A2, Eq. 1) has one full-width table E_n [V_n, D] per order and
+    no projection; its workloads keep K = 1 and give the tables about the parameter count of
+    the final-form workload of the same size.
 The pages name no token-id distribution; uniform and Zipf(1.1) ids stand in for real text.
 """
 from __future__ import annotations
@@ -43,6 +46,7 @@ class Workload:
     mode: str = "prefill"      # "prefill" or "decode"
     decode_steps: int = 0      # decode: steps per run
     decode_new: int = 0        # decode: new tokens per sequence per step (1 + drafts)
+    form: str = "final"        # "final" (projected sub-tables) or "basic" (Eq. 1)
 
     @property
     def S(self) -> int:
@@ -50,7 +54,9 @@ class Workload:
 
     @property
     def d(self) -> int:
-        return self.D // self.S if self.S else 0
+        if not self.S:
+            return 0
+        return self.D if self.form == "basic" else self.D // self.S
 
     @property
     def T(self) -> int:
@@ -72,6 +78,8 @@ _V3 = (2031671, 2031691, 2031703, 2031713, 2031749, 2031767, 2031779, 2031791,
        2031811, 2031839, 2031851, 2031863, 2031893, 2031907, 2031937, 2031961)
 _V4 = (9764873, 9764897, 9764899, 9764921, 9764939, 9764957, 9764959, 9764971,
        9764977, 9764981, 9765001, 9765017)
+_VB2 = (1104017, 1104041)                 # basic form, V0 = 32000
+_VB4 = (3211279, 3211289, 3211291)        # basic form, V0 = 131072: 3 x 3.2M x 3072 = 29.6B
 
 WORKLOADS = {
     "tiny_f32": _w("tiny_f32", "f32", 1000, 64, 3, 2, (5003, 7001, 6007, 8009), 2, 128,
@@ -83,6 +91,13 @@ WORKLOADS = {
                           "zipf1.1", 4),
     "decode_spec5_30b": _w("decode_spec5_30b", "bf16", 131072, 3072, 4, 4, _V4, 256, 8192,
                            "zipf1.1", 5, mode="decode", decode_steps=1000, decode_new=5),
+    # the basic form (Eq. 1)
+    "basic_tiny_f32": _w("basic_tiny_f32", "f32", 1000, 64, 3, 1, (5003, 7001), 2, 128,
+                         "uniform", 6, form="basic"),
+    "basic_bf16_d1024": _w("basic_bf16_d1024", "bf16", 32000, 1024, 3, 1, _VB2, 8, 2048,
+                           "uniform", 7, form="basic"),
+    "prefill_64k_basic_30b": _w("prefill_64k_basic_30b", "bf16", 131072, 3072, 4, 1, _VB4, 8,
+                                8192, "zipf1.1", 8, form="basic"),
 }
 
 
@@ -165,18 +180,26 @@ def _torch_dtype(w: Workload):
 
 
 def _shapes(w: Workload):
-    return [(w.V0, w.D)] + [(v, w.d) for v in w.V] + [(w.D, w.D)]
+    # the basic form has no projection W
+    return [(w.V0, w.D)] + [(v, w.d) for v in w.V] + ([] if w.form == "basic" else [(w.D, w.D)])
+
+
+def _split(w: Workload, mats):
+    if w.form == "basic":
+        return mats[0], mats[1:], None
+    return mats[0], mats[1:-1], mats[-1]
 
 
 def host_tables(w: Workload, seed: Optional[int] = None, std: float = 0.02):
     """CPU tables (E0, [E_s], W_stack) drawn N(0, std) in fp32 and rounded to the workload
-    dtype (round-to-nearest-even for bf16). W_stack[o, s*d + c] holds W_{n,k}[o, c]."""
+    dtype (round-to-nearest-even for bf16). W_stack[o, s*d + c] holds W_{n,k}[o, c]; None
+    in the basic form."""
     import torch
     g = torch.Generator().manual_seed(1000 * w.seed + (0 if seed is None else seed))
     dt = _torch_dtype(w)
     mats = [torch.empty(sh, dtype=torch.float32).normal_(0.0, std, generator=g).to(dt)
             for sh in _shapes(w)]
-    return mats[0], mats[1:-1], mats[-1]
+    return _split(w, mats)
 
 
 def device_tables(w: Workload, device="cuda", seed: Optional[int] = None, std: float = 0.02,
@@ -194,7 +217,7 @@ def device_tables(w: Workload, device="cuda", seed: Optional[int] = None, std: f
             t[r0:r1].copy_(torch.empty((r1 - r0, c), dtype=torch.float32, device=device)
                            .normal_(0.0, std, generator=g))
         mats.append(t)
-    return mats[0], mats[1:-1], mats[-1]
+    return _split(w, mats)
 
 
 def split_stacked_w(W_stack, S: int):
