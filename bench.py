@@ -140,6 +140,8 @@ def main():
                     help="skip the backward (training gradients) timing")
     ap.add_argument("--no-amp", action="store_true",
                     help="skip the amplified (scale / layer-norm) prefill timings")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the per-layer (PLNE) batched-launch timing")
     ap.add_argument("--no-basic", action="store_true",
                     help="skip the basic-form (Eq. 1) prefill timing")
     ap.add_argument("--decode-steps", type=int, default=1000)
@@ -264,6 +266,10 @@ def main():
     if not args.no_basic:
         basic = bench_basic(g, WL, dev, stream, args.steps)
 
+    layers = None
+    if not args.no_layers:
+        layers = bench_layers(g, WL, dev, stream, min(args.steps, 10))
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_batches} batches")
@@ -288,6 +294,7 @@ def main():
         "backward": backward,
         "decode": decode,
         "basic_form": basic,
+        "per_layer": layers,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -394,6 +401,114 @@ def bench_basic(g, WL, dev, stream, steps):
     log(f"basic form: step {wall*1e6:.0f} us, hash {t_hash*1e6:.1f} us, sum {t_sum*1e6:.1f} us "
         f"({gbs:.0f} GB/s)")
     del E0, E, tables, out, ws, idx
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_layers(g, WL, dev, stream, steps):
+    """Per-layer N-gram embedding (section 5.2): 8 layers with tables of their own (D = 2048,
+    N = 3, K = 2, 2.0B n-gram parameters each, 38 GB in all). Each layer's embeddings in one
+    call per layer, against all 8 layers in one call (hash once, the projections of the 8
+    layers in one launch): 64K-token prefill batches, and speculative-verify decode steps
+    (256 sequences x 5 ids, no commit so every step does the same work) in HIP graphs of
+    200 steps."""
+    import numpy as np
+    import torch
+
+    torch.cuda.empty_cache()
+    w = WL.workload("plne_8x_d2048")
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    log(f"per-layer: generating {w.layers} x {(sum(w.V) * w.d + w.V0 * w.D) * 2 / 1e9:.1f} GB")
+    tabs = []
+    for l in range(w.layers):
+        E0, E, W = WL.device_tables(w, device=dev, seed=l + 1)
+        tabs.append(g.Tables(E0, E, W))
+    T = w.T
+    toks = torch.as_tensor(WL.token_batch(w).reshape(-1)).to(dev)
+    cu = torch.as_tensor(np.arange(w.batch + 1, dtype=np.int32) * w.seqlen).to(dev)
+    outs = [torch.empty((T, w.D), dtype=torch.bfloat16, device=dev) for _ in range(w.layers)]
+    ws = g.alloc_workspace(cfg, T, device=dev)
+
+    def separate(cs):
+        for l in range(w.layers):
+            g.ngram_embed_prefill(cfg, tabs[l], toks, cu, outs[l], ws, stream=cs)
+
+    def batched(cs):
+        g.ngram_embed_prefill_layers(cfg, tabs, toks, cu, outs, ws, stream=cs)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn(stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            fn(stream)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    # interleave the two forms so that clocks and caches treat them alike
+    t_sep, t_bat = [], []
+    for _ in range(steps):
+        t_sep.append(timed(separate, 1))
+        t_bat.append(timed(batched, 1))
+    t_sep, t_bat = float(np.mean(t_sep)), float(np.mean(t_bat))
+    flops = 2.0 * T * w.D * w.D * w.layers
+    res = {"workload": w.name, "layers": w.layers,
+           "prefill": {"tokens": T, "us_separate_calls": round(t_sep * 1e6, 1),
+                       "us_one_call": round(t_bat * 1e6, 1),
+                       "tflops_one_call": round(flops / t_bat / 1e12, 1)}}
+    del outs, ws
+    # decode: 256 sequences x 5 ids per step, histories of 8192 ids
+    nseq, tmax, nsteps = 256, 5, 200
+    hist = torch.as_tensor(WL.token_batch(w, purpose=2, batch=nseq, seqlen=8192).reshape(-1)
+                           ).to(dev)
+    hcu = torch.as_tensor(np.arange(nseq + 1, dtype=np.int32) * 8192).to(dev)
+    cache = g.Cache.empty(cfg, nseq, device=dev)
+    g.ngram_cache_init(cfg, cache, hist, hcu, stream=stream)
+    ids = torch.as_tensor(WL.token_batch(w, purpose=3, batch=nsteps * nseq, seqlen=tmax)
+                          .reshape(nsteps, nseq, tmax)).to(dev)
+    n_new = torch.full((nseq,), tmax, dtype=torch.int32, device=dev)
+    douts = [torch.empty((nseq, tmax, w.D), dtype=torch.bfloat16, device=dev)
+             for _ in range(w.layers)]
+    dws = g.alloc_workspace(cfg, nseq * tmax, device=dev)
+
+    def graph_time(body):
+        gr = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize(dev)
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream()
+            for s in range(nsteps):
+                body(s, cs)
+        ts = []
+        for _ in range(3):
+            torch.cuda.synchronize(dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize(dev)
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts)) / nsteps
+
+    def dec_separate(s, cs):
+        for l in range(w.layers):
+            g.ngram_embed_decode(cfg, tabs[l], cache, ids[s], n_new, douts[l], dws, stream=cs)
+
+    def dec_batched(s, cs):
+        g.ngram_embed_decode_layers(cfg, tabs, cache, ids[s], n_new, douts, dws, stream=cs)
+
+    d_sep = graph_time(dec_separate)
+    d_bat = graph_time(dec_batched)
+    if g.ngram_embed_read_error_flag(dws, stream=stream) != 0:
+        raise RuntimeError("device error flags set in the per-layer timing")
+    res["decode"] = {"seqs": nseq, "ids_per_step": tmax, "steps": nsteps,
+                     "us_per_step_separate_calls": round(d_sep * 1e6, 2),
+                     "us_per_step_one_call": round(d_bat * 1e6, 2)}
+    log(f"per-layer ({w.layers} layers): prefill {t_sep*1e6:.0f} us in separate calls, "
+        f"{t_bat*1e6:.0f} us in one; decode {d_sep*1e6:.1f} vs {d_bat*1e6:.1f} us/step")
+    del tabs, douts, dws, cache
     torch.cuda.empty_cache()
     return res
 

@@ -21,7 +21,8 @@ __all__ = [
     "NGRAM_OK", "NGRAM_F32", "NGRAM_BF16", "AMP_MODES",
     "NGRAM_FLAG_BAD_TOKEN", "NGRAM_FLAG_BAD_SEQLENS", "NGRAM_FLAG_BAD_COUNT",
     "NGRAM_FLAG_BAD_SLOT", "ngram_embed_decode_rows", "ngram_cache_init_slots",
-    "ngram_cache_commit_slots",
+    "ngram_cache_commit_slots", "ngram_embed_prefill_layers", "ngram_embed_decode_layers",
+    "NGRAM_FORM_FINAL", "NGRAM_FORM_BASIC", "FORMS",
     "ngram_embed_workspace_size", "ngram_embed_workspace_layout", "ngram_embed_hash",
     "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
     "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
@@ -102,6 +103,10 @@ def load():
                                                    I32, P, P, P, SZ, P]),
         "ngram_cache_init_slots": (ctypes.c_int, [cfgp, cachep, P, I32, P, P, I64, P, P]),
         "ngram_cache_commit_slots": (ctypes.c_int, [cfgp, cachep, P, I32, P, P, I32, P, P]),
+        "ngram_embed_prefill_layers": (ctypes.c_int, [cfgp, tabp, I32, P, P, I32, I64,
+                                                      ctypes.POINTER(P), P, SZ, P]),
+        "ngram_embed_decode_layers": (ctypes.c_int, [cfgp, tabp, I32, cachep, P, P, I32, P,
+                                                     ctypes.POINTER(P), P, SZ, P]),
         "ngram_embed_backward_workspace_size": (SZ, [cfgp, I64]),
         "ngram_embed_backward": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, P,
                                                 ctypes.POINTER(P), P, P, SZ, P]),
@@ -329,6 +334,37 @@ def ngram_embed_decode(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_
     _check("ngram_embed_decode", load().ngram_embed_decode(
         ctypes.byref(c), ctypes.byref(t), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
         int(new_tokens.shape[1]), _ptr(n_commit), _ptr(out), _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def _layer_args(tables, outs):
+    """C arrays of the layers' tables and output pointers (kept alive by the caller)."""
+    if len(tables) != len(outs) or not tables:
+        raise ValueError("one output per layer, at least one layer")
+    cts = [t._c() for t in tables]
+    tarr = (_CTables * len(cts))(*[ct for ct, _ in cts])
+    oarr = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    return tarr, oarr, cts
+
+
+def ngram_embed_prefill_layers(cfg: Config, tables, tokens, cu_seqlens, outs, ws, stream=None):
+    """Per-layer embeddings: outs[l] = the layer with tables[l], hash computed once."""
+    c, keep = cfg._c()
+    tarr, oarr, keep2 = _layer_args(tables, outs)
+    _check("ngram_embed_prefill_layers", load().ngram_embed_prefill_layers(
+        ctypes.byref(c), tarr, len(tables), _ptr(tokens), _ptr(cu_seqlens),
+        int(cu_seqlens.numel()) - 1, int(tokens.numel()), oarr, _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def ngram_embed_decode_layers(cfg: Config, tables, cache: Cache, new_tokens, n_new, outs, ws,
+                              n_commit=None, stream=None):
+    c, keep = cfg._c()
+    tarr, oarr, keep2 = _layer_args(tables, outs)
+    cc = cache._c()
+    _check("ngram_embed_decode_layers", load().ngram_embed_decode_layers(
+        ctypes.byref(c), tarr, len(tables), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
+        int(new_tokens.shape[1]), _ptr(n_commit), oarr, _ptr(ws),
         int(ws.numel() * ws.element_size()), _stream(stream)))
 
 

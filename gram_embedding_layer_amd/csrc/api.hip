@@ -1,5 +1,7 @@
 // C-ABI entry points: host validation, then stream-ordered kernel launches.
 // Declarations and the contract of every function: include/ngram_embed.h.
+#include <algorithm>
+
 #include "kernels.h"
 
 using ngram::LayerDesc;
@@ -47,6 +49,52 @@ int project_amplified(const LayerDesc& L, const ngram_embed_tables* T, const int
                                             map, st));
 }
 
+// The same for nlayers layers with tables T[l] and outputs outs[l] (per-layer embeddings):
+// the projections of several layers share one launch; with the layer normalisation the
+// layers go one after another through the workspace's unrounded rows.
+int project_layers(const LayerDesc& L, const ngram_embed_tables* T, int32_t nlayers,
+                   const int32_t* idx, const int32_t* tok, int64_t rows, void* const* outs,
+                   void* ws, const ngram::WsLayout& lay, const ngram::RowMap& map,
+                   hipStream_t st) {
+  if (L.amp == NGRAM_AMP_LAYERNORM || nlayers == 1) {
+    for (int32_t l = 0; l < nlayers; ++l) {
+      const int rc = project_amplified(L, &T[l], idx, tok, rows, outs[l], ws, lay, map, st);
+      if (rc != NGRAM_OK) return rc;
+    }
+    return NGRAM_OK;
+  }
+  ngram::LayerParams p[ngram::kMaxLaunchLayers];
+  for (int32_t l0 = 0; l0 < nlayers; l0 += ngram::kMaxLaunchLayers) {
+    const int32_t n = std::min<int32_t>(ngram::kMaxLaunchLayers, nlayers - l0);
+    for (int32_t l = 0; l < n; ++l) p[l] = {T[l0 + l].E0, T[l0 + l].E, T[l0 + l].W, outs[l0 + l]};
+    const int rc = hip_status(ngram::launch_project_layers(L, p, n, idx, tok, rows, false, map,
+                                                           st));
+    if (rc != NGRAM_OK) return rc;
+  }
+  return NGRAM_OK;
+}
+
+// Tables and outputs of nlayers layers: present and aligned.
+int check_layers(const LayerDesc& L, const ngram_embed_tables* T, int32_t nlayers,
+                 void* const* outs) {
+  if (T == nullptr || outs == nullptr) return NGRAM_EALIGN;
+  for (int32_t l = 0; l < nlayers; ++l) {
+    const int rc = check_tables(L, &T[l], true);
+    if (rc != NGRAM_OK) return rc;
+    if (!ngram::aligned(outs[l], 16)) return NGRAM_EALIGN;
+  }
+  return NGRAM_OK;
+}
+
+int prefill_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                 int32_t nlayers, const int32_t* tokens, const int32_t* cu_seqlens,
+                 int32_t nseq, int64_t ntok, void* const* outs, void* ws, size_t ws_bytes,
+                 void* stream);
+int decode_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                int32_t nlayers, ngram_cache* cache, const int32_t* new_tokens,
+                const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
+                void* const* outs, void* ws, size_t ws_bytes, void* stream);
+
 int check_ws(const LayerDesc& L, const void* ws, size_t ws_bytes, int64_t rows,
              ngram::WsLayout* lay) {
   if (!ngram::ws_layout(L, rows, lay)) return NGRAM_EINVAL;
@@ -55,6 +103,62 @@ int check_ws(const LayerDesc& L, const void* ws, size_t ws_bytes, int64_t rows,
 }
 
 int32_t* ws_flags(void* ws) { return static_cast<int32_t*>(ws); }
+
+int prefill_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                 int32_t nlayers, const int32_t* tokens, const int32_t* cu_seqlens,
+                 int32_t nseq, int64_t ntok, void* const* outs, void* ws, size_t ws_bytes,
+                 void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
+  ngram::WsLayout lay;
+  if ((rc = check_ws(L, ws, ws_bytes, ntok, &lay)) != NGRAM_OK) return rc;
+  if (ntok == 0) return NGRAM_OK;
+  if ((rc = check_layers(L, tables, nlayers, outs)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.idx_off);
+  if (L.S > 0) {
+    rc = hip_status(ngram::launch_hash_prefill(L, tokens, cu_seqlens, nseq, ntok, idx,
+                                               ws_flags(ws), st));
+    if (rc != NGRAM_OK) return rc;
+  }
+  return project_layers(L, tables, nlayers, idx, tokens, ntok, outs, ws, lay, ngram::RowMap{},
+                        st);
+}
+
+int decode_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                int32_t nlayers, ngram_cache* cache, const int32_t* new_tokens,
+                const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
+                void* const* outs, void* ws, size_t ws_bytes, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0) return NGRAM_EINVAL;
+  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
+  const int64_t rows = int64_t(cache->nseq) * tmax;
+  ngram::WsLayout lay;
+  if ((rc = check_ws(L, ws, ws_bytes, rows, &lay)) != NGRAM_OK) return rc;
+  if (rows == 0) return NGRAM_OK;
+  if ((rc = check_layers(L, tables, nlayers, outs)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
+      !ngram::aligned(n_new, 4))
+    return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if (n_commit != nullptr && !ngram::aligned(n_commit, 4)) return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* tok = reinterpret_cast<int32_t*>(w + lay.tok_off);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
+  // hash (and commit, when asked) in one kernel; the projection reads only tok/idx, so the
+  // cache may advance before it runs
+  ngram::DecodeArgs d{cache->ring, cache->len, nullptr, cache->nseq, new_tokens, n_new,
+                      n_commit, cache->nseq, tmax, 0, tmax, -1, tok, idx, ws_flags(ws)};
+  rc = hip_status(ngram::launch_hash_decode(L, d, st));
+  if (rc != NGRAM_OK) return rc;
+  return project_layers(L, tables, nlayers, idx, tok, rows, outs, ws, lay, ngram::RowMap{}, st);
+}
 
 }  // namespace
 
@@ -129,24 +233,18 @@ int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables*
 int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                         const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
                         int64_t ntok, void* out, void* ws, size_t ws_bytes, void* stream) {
-  LayerDesc L;
-  int rc = ngram::describe(cfg, &L);
-  if (rc != NGRAM_OK) return rc;
-  if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
-  ngram::WsLayout lay;
-  if ((rc = check_ws(L, ws, ws_bytes, ntok, &lay)) != NGRAM_OK) return rc;
-  if (ntok == 0) return NGRAM_OK;
-  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
-  if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4) || !ngram::aligned(out, 16))
-    return NGRAM_EALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.idx_off);
-  if (L.S > 0) {
-    rc = hip_status(ngram::launch_hash_prefill(L, tokens, cu_seqlens, nseq, ntok, idx,
-                                               ws_flags(ws), st));
-    if (rc != NGRAM_OK) return rc;
-  }
-  return project_amplified(L, tables, idx, tokens, ntok, out, ws, lay, ngram::RowMap{}, st);
+  void* outs[1] = {out};
+  return prefill_impl(cfg, tables, 1, tokens, cu_seqlens, nseq, ntok, outs, ws, ws_bytes,
+                      stream);
+}
+
+int ngram_embed_prefill_layers(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                               int32_t nlayers, const int32_t* tokens,
+                               const int32_t* cu_seqlens, int32_t nseq, int64_t ntok,
+                               void* const* out, void* ws, size_t ws_bytes, void* stream) {
+  if (nlayers < 1) return NGRAM_EINVAL;
+  return prefill_impl(cfg, tables, nlayers, tokens, cu_seqlens, nseq, ntok, out, ws, ws_bytes,
+                      stream);
 }
 
 int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const int32_t* tokens,
@@ -168,32 +266,18 @@ int ngram_embed_decode(const ngram_embed_config* cfg, const ngram_embed_tables* 
                        ngram_cache* cache, const int32_t* new_tokens, const int32_t* n_new,
                        int32_t tmax, const int32_t* n_commit, void* out, void* ws,
                        size_t ws_bytes, void* stream) {
-  LayerDesc L;
-  int rc = ngram::describe(cfg, &L);
-  if (rc != NGRAM_OK) return rc;
-  if (cache == nullptr || cache->nseq < 0) return NGRAM_EINVAL;
-  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
-  const int64_t rows = int64_t(cache->nseq) * tmax;
-  ngram::WsLayout lay;
-  if ((rc = check_ws(L, ws, ws_bytes, rows, &lay)) != NGRAM_OK) return rc;
-  if (rows == 0) return NGRAM_OK;
-  if ((rc = check_tables(L, tables, true)) != NGRAM_OK) return rc;
-  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
-      !ngram::aligned(n_new, 4) || !ngram::aligned(out, 16))
-    return NGRAM_EALIGN;
-  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
-  if (n_commit != nullptr && !ngram::aligned(n_commit, 4)) return NGRAM_EALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  int32_t* tok = reinterpret_cast<int32_t*>(w + lay.tok_off);
-  int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
-  // hash (and commit, when asked) in one kernel; the projection reads only tok/idx, so the
-  // cache may advance before it runs
-  ngram::DecodeArgs d{cache->ring, cache->len, nullptr, cache->nseq, new_tokens, n_new,
-                      n_commit, cache->nseq, tmax, 0, tmax, -1, tok, idx, ws_flags(ws)};
-  rc = hip_status(ngram::launch_hash_decode(L, d, st));
-  if (rc != NGRAM_OK) return rc;
-  return project_amplified(L, tables, idx, tok, rows, out, ws, lay, ngram::RowMap{}, st);
+  void* outs[1] = {out};
+  return decode_impl(cfg, tables, 1, cache, new_tokens, n_new, tmax, n_commit, outs, ws,
+                     ws_bytes, stream);
+}
+
+int ngram_embed_decode_layers(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                              int32_t nlayers, ngram_cache* cache, const int32_t* new_tokens,
+                              const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
+                              void* const* out, void* ws, size_t ws_bytes, void* stream) {
+  if (nlayers < 1) return NGRAM_EINVAL;
+  return decode_impl(cfg, tables, nlayers, cache, new_tokens, n_new, tmax, n_commit, out, ws,
+                     ws_bytes, stream);
 }
 
 int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,

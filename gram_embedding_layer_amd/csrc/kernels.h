@@ -63,6 +63,21 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
                           int64_t nrows, void* out, bool f32out, const RowMap& map,
                           hipStream_t st);
 
+// Per-layer embeddings: the tables and output of one layer. Layers share the config, the
+// rows and the hash indices; the projections of up to kMaxLaunchLayers layers (at most
+// kMaxLaunchTables sub-table pointers in all) run in one launch.
+struct LayerParams {
+  const void* E0;
+  const void* const* E;   // host array of S device pointers
+  const void* W;
+  void* out;
+};
+constexpr int kMaxLaunchLayers = 8;
+constexpr int kMaxLaunchTables = 128;
+hipError_t launch_project_layers(const LayerDesc& L, const LayerParams* layers, int32_t nlayers,
+                                 const int32_t* idx, const int32_t* tok, int64_t nrows,
+                                 bool f32out, const RowMap& map, hipStream_t st);
+
 // the basic form (Eq. 1): out = (E_0 row + the S full-width table rows) / (S + 1), times the
 // output factor; f32out and map as for launch_project (which calls it in that form)
 hipError_t launch_basic(const LayerDesc& L, const void* E0, const void* const* E,

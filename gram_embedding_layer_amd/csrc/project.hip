@@ -44,15 +44,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // values in all, d per sub-table) and B [N, K] row-major with row stride ldb. The layer's
 // forward has N = K = ldb = ldo = D; its backward runs dense products through the same
 // kernels: a dense A is one "sub-table" read with identity indices, and E0 is null.
+// Per-layer embeddings batch several layers (their own tables, W and output; the same rows
+// and indices) into one launch: blockIdx.z is the layer.
 struct ProjArgs {
-  const void* E[NGRAM_MAX_SUBTABLES];
+  const void* E[kMaxLaunchTables];    // sub-table s of launch layer l: E[l * S + s]
   uint32_t Vm1[NGRAM_MAX_SUBTABLES];  // V_{n,k} - 1: indices are clamped to their table
-  const int32_t* idx;                 // [nrows, S]
+  const int32_t* idx;                 // [nrows, S], shared by the layers
   const int32_t* tok;                 // [nrows]; outside [0, V0) -> zero row (E0 only)
-  const void* E0;                     // [V0, N], or null: no E_0 term, every row valid
-  const void* W;                      // B operand [N, ldb] (the stacked W in the layer)
-  void* out;                          // [nrows, ldo]: config dtype, fp32, or fp32 partials
+  const void* E0[kMaxLaunchLayers];   // [V0, N], or null: no E_0 term, every row valid
+  const void* W[kMaxLaunchLayers];    // B operand [N, ldb] (the stacked W in the layer)
+  void* out[kMaxLaunchLayers];        // [nrows, ldo]: config dtype, fp32, or fp32 partials
                                       // [splits, nrows, ldo]
+  int32_t layers;                     // layers in this launch (gridDim.z)
   int64_t nrows;
   int64_t ldb, ldo;                   // row strides of B and of the output, in elements
   int32_t K, N, S, d, V0;
@@ -175,8 +178,9 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   const int prow = lane >> 3;
   const int pchunk = (lane & 7) ^ prow;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)lds));
-  const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E);
-  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const int layer = blockIdx.z;
+  const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E) + layer * a.S;
+  const uint16_t* W = static_cast<const uint16_t*>(a.W[layer]);
   const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.ldb + pchunk * 8;
   const uint16_t* ap[QA];
   const int KT_ALL = a.K / kBK;  // slices of the whole contraction
@@ -298,8 +302,8 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   //    consecutive outputs per lane, so E_0 is read and the output written in whole
   //    lines. E_0 add and the 1/(S+1) scale in fp32, one rounding to bf16.
   __syncthreads();                      // every wave is done with the slice buffers
-  const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0);
-  uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out);
+  const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0[layer]);
+  uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out[layer]);
   char* ep = lds + w * (32 * EP_PITCH);
   constexpr int LPR = WN / 4;           // lanes per output row
   constexpr int RPI = 64 / LPR;         // rows per wave instruction
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     const int64_t mrow = m0 + wm * WM + i * 32 + er;
     const int n = n0 + wn * WN + ec * 4;
     if constexpr (OM == kOutPartial) {
-      float* pp = static_cast<float*>(a.out) + int64_t(split) * a.nrows * a.ldo;
+      float* pp = static_cast<float*>(a.out[layer]) + int64_t(split) * a.nrows * a.ldo;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int64_t m = mrow + it * RPI;
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
       continue;
     }
     // without E_0 (dense products) every row is valid and nothing is added
-    const bool has_e0 = a.E0 != nullptr;
+    const bool has_e0 = E0 != nullptr;
     int32_t tk[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
         const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
         if constexpr (OM == kOutF32) {
           const f32x4_t res = ok ? f32x4_t{y0, y1, y2, y3} : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + om * a.ldo + n) = res;
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + om * a.ldo + n) = res;
         } else {
           u32x2_t res = {0u, 0u};
           if (ok) {
@@ -399,13 +403,14 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
   __shared__ const T* Etab[NGRAM_MAX_SUBTABLES];
   __shared__ uint32_t Vtab[NGRAM_MAX_SUBTABLES];
   const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const int layer = blockIdx.z;
   if (t < a.S) {
-    Etab[t] = static_cast<const T*>(a.E[t]);
+    Etab[t] = static_cast<const T*>(a.E[layer * a.S + t]);
     Vtab[t] = a.Vm1[t];
   }
   const int64_t m0 = int64_t(blockIdx.x) * 64;
   const int n0 = blockIdx.y * 64;
-  const T* __restrict__ W = static_cast<const T*>(a.W);
+  const T* __restrict__ W = static_cast<const T*>(a.W[layer]);
   float acc[4][4] = {};
   __syncthreads();
   for (int k0 = 0; k0 < a.K; k0 += 16) {
@@ -433,13 +438,13 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const ProjArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] += As[kk][ty + 16 * i] * Bs[kk][tx + 16 * j];
     __syncthreads();
   }
-  const T* __restrict__ E0 = static_cast<const T*>(a.E0);
-  TO* __restrict__ out = static_cast<TO*>(a.out);
+  const T* __restrict__ E0 = static_cast<const T*>(a.E0[layer]);
+  TO* __restrict__ out = static_cast<TO*>(a.out[layer]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + ty + 16 * i;
     if (m >= a.nrows) continue;
-    const bool has_e0 = a.E0 != nullptr;        // without E_0 every row is valid
+    const bool has_e0 = E0 != nullptr;          // without E_0 every row is valid
     const int32_t tk = has_e0 ? a.tok[m] : 0;
     if (tk == kSkipRow) continue;
     const int64_t om = out_row(a, m);
@@ -464,10 +469,12 @@ __global__ __launch_bounds__(256) void e0_lookup_kernel(const ProjArgs a, int32_
   const int64_t r = item / cpr, c = item - r * cpr;
   const int32_t tk = a.tok[r];
   if (tk == kSkipRow) return;
+  const int layer = blockIdx.z;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (uint32_t(tk) < uint32_t(a.V0))
-    v = reinterpret_cast<const uint4*>(static_cast<const char*>(a.E0) + int64_t(tk) * row_bytes)[c];
-  reinterpret_cast<uint4*>(static_cast<char*>(a.out) + out_row(a, r) * row_bytes)[c] = v;
+    v = reinterpret_cast<const uint4*>(static_cast<const char*>(a.E0[layer]) +
+                                       int64_t(tk) * row_bytes)[c];
+  reinterpret_cast<uint4*>(static_cast<char*>(a.out[layer]) + out_row(a, r) * row_bytes)[c] = v;
 }
 
 // Scaled (or fp32-output) rows: one element per thread, fp32 product, one rounding.
@@ -478,10 +485,12 @@ __global__ __launch_bounds__(256) void e0_scaled_kernel(const ProjArgs a) {
   const int64_t r = item / a.N;
   const int32_t tk = a.tok[r];
   if (tk == kSkipRow) return;
+  const int layer = blockIdx.z;
   float v = 0.f;
   if (uint32_t(tk) < uint32_t(a.V0))
-    v = ld<T>(static_cast<const T*>(a.E0) + int64_t(tk) * a.N + (item - r * a.N)) * a.inv;
-  st<TO>(static_cast<TO*>(a.out) + out_row(a, r) * a.N + (item - r * a.N), v);
+    v = ld<T>(static_cast<const T*>(a.E0[layer]) + int64_t(tk) * a.N + (item - r * a.N)) *
+        a.inv;
+  st<TO>(static_cast<TO*>(a.out[layer]) + out_row(a, r) * a.N + (item - r * a.N), v);
 }
 
 // out[m, n] += f * sum_s part[s, m, n]: the split partial sums added in split order (the
@@ -510,17 +519,19 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int osz, hipStream_t st) {
   if ((OM == kOutPartial || a.row_group != 0) && nrows > chunk) return hipErrorInvalidValue;
   const int32_t* idx = a.idx;
   const int32_t* tok = a.tok;
-  char* out = static_cast<char*>(a.out);
+  char* out[kMaxLaunchLayers];
+  for (int l = 0; l < a.layers; ++l) out[l] = static_cast<char*>(a.out[l]);
   for (int64_t r0 = 0; r0 < nrows; r0 += chunk) {
     const int64_t n = nrows - r0 < chunk ? nrows - r0 : chunk;
     a.idx = idx + r0 * a.S;
     a.tok = tok ? tok + r0 : nullptr;
-    a.out = out + r0 * a.ldo * osz;
+    for (int l = 0; l < a.layers; ++l) a.out[l] = out[l] + r0 * a.ldo * osz;
     a.nrows = n;
     a.tiles_m = int32_t((n + BM - 1) / BM);
     a.tiles_n = a.N / kBN;
     const int64_t blocks = int64_t(a.tiles_m) * a.tiles_n * (OM == kOutPartial ? a.splits : 1);
-    hipLaunchKernelGGL((proj_mfma_kernel<BM, OM>), dim3(unsigned(blocks)), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((proj_mfma_kernel<BM, OM>), dim3(unsigned(blocks), 1, unsigned(a.layers)),
+                       dim3(512), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -558,16 +569,15 @@ hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStre
   const unsigned gy = unsigned((a.N + 63) / 64);
   const int32_t* idx = a.idx;
   const int32_t* tok = a.tok;
-  char* out = static_cast<char*>(a.out);
   if (a.row_group != 0 && nrows > (int64_t(1) << 30)) return hipErrorInvalidValue;
   for (int64_t r0 = 0; r0 < nrows; r0 += (int64_t(1) << 30)) {
     ProjArgs b = a;
     const int64_t n = nrows - r0 < (int64_t(1) << 30) ? nrows - r0 : (int64_t(1) << 30);
     b.idx = idx + r0 * a.S;
     b.tok = tok ? tok + r0 : nullptr;
-    b.out = out + r0 * a.ldo * osz;
+    for (int l = 0; l < a.layers; ++l) b.out[l] = static_cast<char*>(a.out[l]) + r0 * a.ldo * osz;
     b.nrows = n;
-    const dim3 grid(unsigned((n + 63) / 64), gy);
+    const dim3 grid(unsigned((n + 63) / 64), gy, unsigned(a.layers));
     if (dtype == NGRAM_F32)
       hipLaunchKernelGGL((proj_generic_kernel<float, float>), grid, dim3(256), 0, st, b);
     else if (om == kOutF32)
@@ -589,9 +599,10 @@ ProjArgs dense_args(const void* A, int64_t M, const void* B, int32_t N, int32_t 
   a.Vm1[0] = uint32_t(M - 1);
   a.idx = ident;
   a.tok = nullptr;
-  a.E0 = nullptr;
-  a.W = B;
-  a.out = out;
+  a.E0[0] = nullptr;
+  a.W[0] = B;
+  a.out[0] = out;
+  a.layers = 1;
   a.nrows = M;
   a.ldb = K;
   a.ldo = ldo;
@@ -607,23 +618,22 @@ ProjArgs dense_args(const void* A, int64_t M, const void* B, int32_t N, int32_t 
 
 }  // namespace
 
-hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
-                          const void* W, const int32_t* idx, const int32_t* tok,
-                          int64_t nrows, void* out, bool f32out, const RowMap& map,
-                          hipStream_t st) {
-  if (nrows <= 0) return hipSuccess;
-  if (L.form == NGRAM_FORM_BASIC && L.S > 0)
-    return launch_basic(L, E0, E, idx, tok, nrows, out, f32out, map, st);
-  ProjArgs a{};
-  for (int s = 0; s < L.S; ++s) {
-    a.E[s] = E[s];
-    a.Vm1[s] = L.V[s] - 1u;
+hipError_t launch_project_layers(const LayerDesc& L, const LayerParams* layers, int32_t nlayers,
+                                 const int32_t* idx, const int32_t* tok, int64_t nrows,
+                                 bool f32out, const RowMap& map, hipStream_t st) {
+  if (nrows <= 0 || nlayers <= 0) return hipSuccess;
+  if (L.form == NGRAM_FORM_BASIC && L.S > 0) {
+    for (int l = 0; l < nlayers; ++l) {
+      const hipError_t e = launch_basic(L, layers[l].E0, layers[l].E, idx, tok, nrows,
+                                        layers[l].out, f32out, map, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
+  ProjArgs a{};
+  for (int s = 0; s < L.S; ++s) a.Vm1[s] = L.V[s] - 1u;
   a.idx = idx;
   a.tok = tok;
-  a.E0 = E0;
-  a.W = W;
-  a.out = out;
   a.nrows = nrows;
   a.K = L.D;
   a.N = L.D;
@@ -638,35 +648,59 @@ hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const*
   a.row_stride = map.stride;
   a.row_off = map.off;
   const int osz = f32out ? 4 : L.esz;   // bytes per output element
-  if (L.S == 0) {
-    if (!f32out && L.scale == 1.0f) {
+  // layers per launch: as many as the kernel arguments hold
+  const int per = std::min<int>(kMaxLaunchLayers, L.S > 0 ? kMaxLaunchTables / L.S
+                                                           : kMaxLaunchLayers);
+  for (int l0 = 0; l0 < nlayers; l0 += per) {
+    a.layers = std::min(per, nlayers - l0);
+    for (int l = 0; l < a.layers; ++l) {
+      const LayerParams& p = layers[l0 + l];
+      for (int s = 0; s < L.S; ++s) a.E[l * L.S + s] = p.E[s];
+      a.E0[l] = p.E0;
+      a.W[l] = p.W;
+      a.out[l] = p.out;
+    }
+    hipError_t e = hipSuccess;
+    if (L.S > 0) {
+      e = run_product(a, L.dtype, f32out ? kOutF32 : kOutBf16, nrows, st);
+    } else if (!f32out && L.scale == 1.0f) {
       const int32_t row_bytes = L.D * L.esz;
       const int64_t items = nrows * (row_bytes / 16);
-      hipLaunchKernelGGL(e0_lookup_kernel, dim3(unsigned((items + 255) / 256)), dim3(256), 0,
-                         st, a, row_bytes);
-      return hipGetLastError();
+      hipLaunchKernelGGL(e0_lookup_kernel, dim3(unsigned((items + 255) / 256), 1,
+                                                unsigned(a.layers)),
+                         dim3(256), 0, st, a, row_bytes);
+      e = hipGetLastError();
+    } else {
+      // at most 2^30 rows x D elements per launch keeps the grid in range
+      const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 38) / L.D);
+      if (map.group != 0 && nrows > rows_per) return hipErrorInvalidValue;
+      for (int64_t r0 = 0; r0 < nrows && e == hipSuccess; r0 += rows_per) {
+        ProjArgs b = a;
+        b.nrows = std::min(rows_per, nrows - r0);
+        b.tok = tok + r0;
+        for (int l = 0; l < a.layers; ++l)
+          b.out[l] = static_cast<char*>(a.out[l]) + r0 * L.D * osz;
+        const dim3 grid(unsigned((b.nrows * L.D + 255) / 256), 1, unsigned(a.layers));
+        if (L.dtype == NGRAM_F32)
+          hipLaunchKernelGGL((e0_scaled_kernel<float, float>), grid, dim3(256), 0, st, b);
+        else if (f32out)
+          hipLaunchKernelGGL((e0_scaled_kernel<uint16_t, float>), grid, dim3(256), 0, st, b);
+        else
+          hipLaunchKernelGGL((e0_scaled_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, b);
+        e = hipGetLastError();
+      }
     }
-    // at most 2^30 rows x D elements per launch keeps the grid in range
-    const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 38) / L.D);
-    if (map.group != 0 && nrows > rows_per) return hipErrorInvalidValue;
-    for (int64_t r0 = 0; r0 < nrows; r0 += rows_per) {
-      ProjArgs b = a;
-      b.nrows = std::min(rows_per, nrows - r0);
-      b.tok = tok + r0;
-      b.out = static_cast<char*>(out) + r0 * L.D * osz;
-      const dim3 grid(unsigned((b.nrows * L.D + 255) / 256));
-      if (L.dtype == NGRAM_F32)
-        hipLaunchKernelGGL((e0_scaled_kernel<float, float>), grid, dim3(256), 0, st, b);
-      else if (f32out)
-        hipLaunchKernelGGL((e0_scaled_kernel<uint16_t, float>), grid, dim3(256), 0, st, b);
-      else
-        hipLaunchKernelGGL((e0_scaled_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, b);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    if (e != hipSuccess) return e;
   }
-  return run_product(a, L.dtype, f32out ? kOutF32 : kOutBf16, nrows, st);
+  return hipSuccess;
+}
+
+hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,
+                          const void* W, const int32_t* idx, const int32_t* tok,
+                          int64_t nrows, void* out, bool f32out, const RowMap& map,
+                          hipStream_t st) {
+  const LayerParams p{E0, E, W, out};
+  return launch_project_layers(L, &p, 1, idx, tok, nrows, f32out, map, st);
 }
 
 hipError_t launch_dense_product(const LayerDesc& L, const void* A, int64_t M, const void* B,

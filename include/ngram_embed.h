@@ -254,6 +254,28 @@ int ngram_cache_commit_slots(const ngram_embed_config* cfg, ngram_cache* cache,
                              const int32_t* n_accept, int32_t tmax, int32_t* err_flags,
                              void* stream);
 
+/* ---------------------------------------------------------------- per-layer embeddings
+ * Per-layer N-gram embedding (PLNE, section 5.2 of the same page): every layer l of a model
+ * computes the layer's output with embedding tables and projections of its own, from the
+ * same token ids (the model then uses out[l] inside layer l's feed-forward block). One
+ * config serves every layer, so the hash indices are computed once and shared; the
+ * projections of up to 8 layers (at most 128 sub-table pointers in all) run in one launch,
+ * blockIdx.z selecting the layer. Each layer's output has the same bits as a single-layer
+ * call with that layer's tables.
+ * tables: host array of nlayers >= 1 tables (each as for one layer); out: host array of
+ * nlayers device pointers, out[l] [ntok, D] (prefill) or [nseq, tmax, D] (decode), 16-byte
+ * aligned. ws: as for one layer (its size does not depend on nlayers). With
+ * NGRAM_AMP_LAYERNORM the layers run one after another through the workspace. The decode
+ * cache and n_commit work as in ngram_embed_decode: the step is committed once. */
+int ngram_embed_prefill_layers(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                               int32_t nlayers, const int32_t* tokens,
+                               const int32_t* cu_seqlens, int32_t nseq, int64_t ntok,
+                               void* const* out, void* ws, size_t ws_bytes, void* stream);
+int ngram_embed_decode_layers(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                              int32_t nlayers, ngram_cache* cache, const int32_t* new_tokens,
+                              const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
+                              void* const* out, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- backward (training)
  * Gradients of the layer for one batch, given the upstream gradient dout = dL/dout
  * (device [ntok, D], config dtype, 16-byte aligned) of out = ngram_embed_prefill(tokens).

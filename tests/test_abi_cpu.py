@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "ngram_cache_commit", "ngram_embed_backward",
               "ngram_embed_backward_workspace_size"):
         assert n in names
-    assert len(names) == 17
+    assert len(names) == 19
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -125,6 +125,36 @@ def test_prefill_argument_checks(lib):
     assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE + 8, FAKE, ws_need, 0) == -3
     assert lib.ngram_embed_prefill(P(c), P(T), FAKE + 1, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
     assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+
+
+def test_layers_argument_checks(lib):
+    """Per-layer entry points: at least one layer, every layer's tables and output checked."""
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    P = ctypes.byref
+    ws_need = g.ngram_embed_workspace_size(cfg, 16)
+    good, k1 = _tables_c(4)
+    bad, k2 = _tables_c(4, sub=FAKE + 2)
+    two = (g._CTables * 2)(good, good)
+    mixed = (g._CTables * 2)(good, bad)
+    outs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    outs_bad = (ctypes.c_void_p * 2)(FAKE, FAKE + 8)
+    pf = lib.ngram_embed_prefill_layers
+    assert pf(P(c), two, 0, FAKE, FAKE, 1, 16, outs, FAKE, ws_need, 0) == -1
+    assert pf(P(c), two, 2, FAKE, FAKE, 1, 16, outs, FAKE, ws_need - 1, 0) == -4
+    assert pf(P(c), mixed, 2, FAKE, FAKE, 1, 16, outs, FAKE, ws_need, 0) == -3
+    assert pf(P(c), two, 2, FAKE, FAKE, 1, 16, outs_bad, FAKE, ws_need, 0) == -3
+    assert pf(P(c), None, 2, FAKE, FAKE, 1, 16, outs, FAKE, ws_need, 0) == -3
+    assert pf(P(c), two, 2, FAKE, FAKE, 1, 16, None, FAKE, ws_need, 0) == -3
+    assert pf(P(c), two, 2, FAKE, FAKE, 1, 0, outs, FAKE, ws_need, 0) == 0      # no tokens
+    cache = g._CCache(FAKE, FAKE, 4)
+    ws_dec = g.ngram_embed_workspace_size(cfg, 4 * 5)
+    dl = lib.ngram_embed_decode_layers
+    assert dl(P(c), two, -1, P(cache), FAKE, FAKE, 5, None, outs, FAKE, ws_dec, 0) == -1
+    assert dl(P(c), two, 2, P(cache), FAKE, FAKE, 9, None, outs, FAKE, ws_dec, 0) == -1
+    assert dl(P(c), two, 2, P(cache), FAKE, FAKE, 5, None, outs, FAKE, ws_dec - 1, 0) == -4
+    assert dl(P(c), mixed, 2, P(cache), FAKE, FAKE, 5, None, outs, FAKE, ws_dec, 0) == -3
+    assert dl(P(c), two, 2, P(cache), FAKE, FAKE, 5, None, outs_bad, FAKE, ws_dec, 0) == -3
 
 
 def test_decode_and_cache_argument_checks(lib):

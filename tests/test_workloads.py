@@ -60,6 +60,13 @@ def test_basic_tables_have_no_projection():
     assert [tuple(e.shape) for e in E] == [(5003, 64), (7001, 64)]
 
 
+def test_per_layer_workload():
+    w = W.workload("plne_8x_d2048")
+    assert w.layers == 8 and w.S == 4 and w.d == 512
+    assert W.mid_gap_primes(131072, 1000000, 4) == list(w.V)
+    assert sum(v * w.d for v in w.V) == pytest.approx(2.0e9, rel=0.01)
+
+
 def test_mid_gap_primes_rule():
     ps = W.mid_gap_primes(131072, int(9.8e6), 12)
     assert ps == list(W.workload("prefill_64k_30b").V)

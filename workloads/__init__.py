@@ -47,6 +47,7 @@ class Workload:
     decode_steps: int = 0      # decode: steps per run
     decode_new: int = 0        # decode: new tokens per sequence per step (1 + drafts)
     form: str = "final"        # "final" (projected sub-tables) or "basic" (Eq. 1)
+    layers: int = 1            # per-layer embeddings: layers with tables of their own
 
     @property
     def S(self) -> int:
@@ -78,6 +79,7 @@ _V3 = (2031671, 2031691, 2031703, 2031713, 2031749, 2031767, 2031779, 2031791,
        2031811, 2031839, 2031851, 2031863, 2031893, 2031907, 2031937, 2031961)
 _V4 = (9764873, 9764897, 9764899, 9764921, 9764939, 9764957, 9764959, 9764971,
        9764977, 9764981, 9765001, 9765017)
+_V5 = (983063, 983069, 983083, 983113)       # per-layer workload, V0 = 131072
 _VB2 = (1104017, 1104041)                 # basic form, V0 = 32000
 _VB4 = (3211279, 3211289, 3211291)        # basic form, V0 = 131072: 3 x 3.2M x 3072 = 29.6B
 
@@ -96,6 +98,9 @@ WORKLOADS = {
                          "uniform", 6, form="basic"),
     "basic_bf16_d1024": _w("basic_bf16_d1024", "bf16", 32000, 1024, 3, 1, _VB2, 8, 2048,
                            "uniform", 7, form="basic"),
+    # per-layer N-gram embedding (section 5.2): 8 layers, 2.0B n-gram parameters each
+    "plne_8x_d2048": _w("plne_8x_d2048", "bf16", 131072, 2048, 3, 2, _V5, 8, 8192, "zipf1.1", 9,
+                        layers=8),
     "prefill_64k_basic_30b": _w("prefill_64k_basic_30b", "bf16", 131072, 3072, 4, 1, _VB4, 8,
                                 8192, "zipf1.1", 8, form="basic"),
 }
