@@ -133,7 +133,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
@@ -142,6 +142,8 @@ def main():
                     help="skip the amplified (scale / layer-norm) prefill timings")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the per-layer (PLNE) batched-launch timing")
+    ap.add_argument("--no-stats", action="store_true",
+                    help="skip the hash-collision statistics timing")
     ap.add_argument("--no-basic", action="store_true",
                     help="skip the basic-form (Eq. 1) prefill timing")
     ap.add_argument("--decode-steps", type=int, default=1000)
@@ -270,6 +272,10 @@ def main():
     if not args.no_layers:
         layers = bench_layers(g, WL, dev, stream, min(args.steps, 10))
 
+    stats = None
+    if not args.no_stats:
+        stats = bench_hash_stats(g, WL, dev, stream, min(args.steps, 10))
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_batches} batches")
@@ -295,6 +301,7 @@ def main():
         "decode": decode,
         "basic_form": basic,
         "per_layer": layers,
+        "hash_stats": stats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -510,6 +517,45 @@ def bench_layers(g, WL, dev, stream, steps):
         f"{t_bat*1e6:.0f} us in one; decode {d_sep*1e6:.1f} vs {d_bat*1e6:.1f} us/step")
     del tabs, douts, dws, cache
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_hash_stats(g, WL, dev, stream, steps):
+    """Hash collisions of the 2-gram hash (section 3.2.2, Fig. 3b): 100 sequences x 8192
+    Zipf(1.1) ids, 59 table sizes between 30x and 33x V0 = 131072; rows in use per size and
+    the distinct 2-grams, exact, on the device."""
+    import numpy as np
+    import torch
+
+    V0 = 131072
+    ids, sizes = WL.collision_study(V0)
+    toks = torch.as_tensor(ids.reshape(-1)).to(dev)
+    cu = torch.as_tensor(np.arange(ids.shape[0] + 1, dtype=np.int32) * ids.shape[1]).to(dev)
+    rows = torch.empty((len(sizes),), dtype=torch.int64, device=dev)
+    distinct = torch.empty((1,), dtype=torch.int64, device=dev)
+    ws = g.ngram_hash_stats(V0, 2, toks, cu, sizes, rows, distinct, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        g.ngram_hash_stats(V0, 2, toks, cu, sizes, rows, distinct, ws=ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+        raise RuntimeError("device error flags set in the hash statistics")
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    d = int(distinct.item())
+    coll = {v: d - int(r) for v, r in zip(sizes, rows.cpu())}
+    res = {"positions": int(toks.numel()), "table_sizes": len(sizes), "n": 2,
+           "us_per_call": round(t * 1e6, 1),
+           "position_sizes_per_s": round(toks.numel() * len(sizes) / t, 1),
+           "distinct_2grams": d,
+           "collisions_at_multiples": {f"{m}xV0": coll[m * V0] for m in range(30, 34)},
+           "collisions_coprime_sizes": [min(c for v, c in coll.items() if v % 2),
+                                        max(c for v, c in coll.items() if v % 2)]}
+    log(f"hash stats: {t*1e6:.0f} us for {toks.numel()} positions x {len(sizes)} sizes; "
+        f"collisions at multiples {list(res['collisions_at_multiples'].values())}, "
+        f"coprime {res['collisions_coprime_sizes']}")
     return res
 
 

@@ -22,7 +22,8 @@ __all__ = [
     "NGRAM_FLAG_BAD_TOKEN", "NGRAM_FLAG_BAD_SEQLENS", "NGRAM_FLAG_BAD_COUNT",
     "NGRAM_FLAG_BAD_SLOT", "ngram_embed_decode_rows", "ngram_cache_init_slots",
     "ngram_cache_commit_slots", "ngram_embed_prefill_layers", "ngram_embed_decode_layers",
-    "NGRAM_FORM_FINAL", "NGRAM_FORM_BASIC", "FORMS",
+    "NGRAM_FORM_FINAL", "NGRAM_FORM_BASIC", "FORMS", "ngram_hash_stats_workspace_size",
+    "ngram_hash_stats",
     "ngram_embed_workspace_size", "ngram_embed_workspace_layout", "ngram_embed_hash",
     "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
     "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
@@ -107,6 +108,9 @@ def load():
                                                       ctypes.POINTER(P), P, SZ, P]),
         "ngram_embed_decode_layers": (ctypes.c_int, [cfgp, tabp, I32, cachep, P, P, I32, P,
                                                      ctypes.POINTER(P), P, SZ, P]),
+        "ngram_hash_stats_workspace_size": (SZ, [I64, I32, I64, ctypes.POINTER(I64), I32]),
+        "ngram_hash_stats": (ctypes.c_int, [I64, I32, P, P, I32, I64, ctypes.POINTER(I64), I32,
+                                            P, P, P, SZ, P]),
         "ngram_embed_backward_workspace_size": (SZ, [cfgp, I64]),
         "ngram_embed_backward": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, P,
                                                 ctypes.POINTER(P), P, P, SZ, P]),
@@ -366,6 +370,35 @@ def ngram_embed_decode_layers(cfg: Config, tables, cache: Cache, new_tokens, n_n
         ctypes.byref(c), tarr, len(tables), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
         int(new_tokens.shape[1]), _ptr(n_commit), oarr, _ptr(ws),
         int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def _vocab_arr(vocab):
+    return (ctypes.c_int64 * max(1, len(vocab)))(*[int(v) for v in vocab])
+
+
+def ngram_hash_stats_workspace_size(V0: int, n: int, ntok: int, vocab) -> int:
+    arr = _vocab_arr(vocab)
+    return int(load().ngram_hash_stats_workspace_size(int(V0), int(n), int(ntok), arr,
+                                                      len(vocab)))
+
+
+def ngram_hash_stats(V0: int, n: int, tokens, cu_seqlens, vocab, rows, distinct=None,
+                     ws=None, stream=None):
+    """rows[v] (device int64 [len(vocab)]) = distinct table rows of size vocab[v] that the
+    order-n hash of every position uses; distinct (device int64 [1], optional) = distinct
+    n-grams. ws: None allocates a zero-filled workspace."""
+    import torch
+    arr = _vocab_arr(vocab)
+    if ws is None:
+        nbytes = ngram_hash_stats_workspace_size(V0, n, tokens.numel(), vocab)
+        if nbytes == 0:
+            raise NgramError("ngram_hash_stats_workspace_size", -1)
+        ws = torch.zeros((nbytes,), dtype=torch.uint8, device=tokens.device)
+    _check("ngram_hash_stats", load().ngram_hash_stats(
+        int(V0), int(n), _ptr(tokens), _ptr(cu_seqlens), int(cu_seqlens.numel()) - 1,
+        int(tokens.numel()), arr, len(vocab), _ptr(rows), _ptr(distinct), _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream(stream)))
+    return ws
 
 
 def ngram_embed_decode_rows(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_new, out,

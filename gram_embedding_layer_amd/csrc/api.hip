@@ -452,6 +452,52 @@ int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables
   return hip_status(ngram::launch_backward(L, b, st));
 }
 
+size_t ngram_hash_stats_workspace_size(int64_t V0, int32_t n, int64_t ntok,
+                                       const int64_t* vocab, int32_t nvocab) {
+  ngram::StatsLayout lay;
+  if (ngram::stats_layout(V0, n, ntok, vocab, nvocab, &lay) != NGRAM_OK) return 0;
+  return lay.total;
+}
+
+int ngram_hash_stats(int64_t V0, int32_t n, const int32_t* tokens, const int32_t* cu_seqlens,
+                     int32_t nseq, int64_t ntok, const int64_t* vocab, int32_t nvocab,
+                     int64_t* rows, int64_t* distinct, void* ws, size_t ws_bytes,
+                     void* stream) {
+  ngram::StatsLayout lay;
+  int rc = ngram::stats_layout(V0, n, ntok, vocab, nvocab, &lay);
+  if (rc != NGRAM_OK) return rc;
+  if (nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
+  if (distinct != nullptr && !lay.exact) return NGRAM_EOVERFLOW;
+  if (!ngram::aligned(ws, 256) || ws_bytes < lay.total) return NGRAM_EWORKSPACE;
+  if (nvocab == 0 && distinct == nullptr) return NGRAM_OK;
+  if ((nvocab > 0 && !ngram::aligned(rows, 8)) ||
+      (distinct != nullptr && !ngram::aligned(distinct, 8)))
+    return NGRAM_EALIGN;
+  if (ntok > 0 && (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4)))
+    return NGRAM_EALIGN;
+  char* w = static_cast<char*>(ws);
+  ngram::StatsArgs a{};
+  a.tokens = tokens;
+  a.cu = cu_seqlens;
+  a.nseq = nseq;
+  a.ntok = ntok;
+  a.V0 = V0;
+  a.n = n;
+  a.vocab = vocab;
+  a.nvocab = nvocab;
+  a.rows = rows;
+  a.distinct = distinct;
+  a.bits = reinterpret_cast<uint32_t*>(w + lay.bits_off);
+  a.keys0 = reinterpret_cast<uint64_t*>(w + lay.keys0_off);
+  a.keys1 = reinterpret_cast<uint64_t*>(w + lay.keys1_off);
+  a.vals0 = reinterpret_cast<uint32_t*>(w + lay.vals0_off);
+  a.vals1 = reinterpret_cast<uint32_t*>(w + lay.vals1_off);
+  a.hist = reinterpret_cast<uint32_t*>(w + lay.hist_off);
+  a.key_bits = lay.key_bits;
+  a.flags = ws_flags(ws);
+  return hip_status(ngram::launch_hash_stats(a, static_cast<hipStream_t>(stream)));
+}
+
 int ngram_embed_read_error_flag(const void* ws, int32_t* flags, void* stream) {
   if (!ngram::aligned(ws, 256) || flags == nullptr) return NGRAM_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -581,6 +581,11 @@ int32_t ceil_log2(int64_t x) {
 
 }  // namespace
 
+hipError_t launch_radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1,
+                             uint32_t* hist, int64_t n, int bits, hipStream_t st) {
+  return radix_sort(k0, v0, k1, v1, hist, n, bits, st);
+}
+
 hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_t st) {
   const int64_t T = b.rows;
   const int64_t Tp = (T + 63) / 64 * 64;

@@ -43,19 +43,22 @@ __device__ __forceinline__ void hash_position(const LayerDesc& L, const uint32_t
   }
 }
 
+// Thread i of a prefill-shaped launch: checks entry i of cu_seqlens (0 = c_0 <= c_1 <= ...
+// <= c_nseq = ntok), then, for a position i < ntok, its id, and fills c[j] = t_{i-j} for
+// j < nord (pad id 0 before the start of the position's sequence). False past the batch.
 template <int NMAX>
-__global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
-    const LayerDesc L, const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu,
-    int32_t nseq, int64_t ntok, int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+__device__ __forceinline__ bool position_context(const int32_t* __restrict__ tokens,
+                                                 const int32_t* __restrict__ cu, int32_t nseq,
+                                                 int64_t ntok, int64_t V0, int nord, int64_t i,
+                                                 int32_t* __restrict__ flags,
+                                                 uint32_t (&c)[NMAX]) {
   if (flags != nullptr && i <= nseq) {
-    // cu_seqlens must run 0 = c_0 <= c_1 <= ... <= c_nseq = ntok
     const int64_t ci = cu[i];
     const bool bad = (i == 0 && ci != 0) || (i == nseq && ci != ntok) ||
                      (i < nseq && ci > cu[i + 1]);
     if (bad) atomicOr(flags, NGRAM_FLAG_BAD_SEQLENS);
   }
-  if (i >= ntok) return;
+  if (i >= ntok) return false;
   // sequence of position i: the last b with cu[b] <= i
   int lo = 0, hi = nseq - 1;
   while (lo < hi) {
@@ -65,12 +68,21 @@ __global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
   int64_t start = cu[lo];
   start = start < 0 ? 0 : (start > i ? i : start);   // never read outside [0, i]
   const int32_t t = tokens[i];
-  if (flags != nullptr && uint32_t(t) >= uint32_t(L.V0)) atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
-  uint32_t c[NMAX];
+  if (flags != nullptr && uint32_t(t) >= uint32_t(V0)) atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
 #pragma unroll
   for (int j = 0; j < NMAX; ++j)
-    c[j] = (j < L.N && i - j >= start) ? uint32_t(tokens[i - j]) : 0u;
-  hash_position<NMAX>(L, c, idx + i * L.S);
+    c[j] = (j < nord && i - j >= start) ? uint32_t(tokens[i - j]) : 0u;
+  return true;
+}
+
+template <int NMAX>
+__global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
+    const LayerDesc L, const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu,
+    int32_t nseq, int64_t ntok, int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t c[NMAX];
+  if (position_context<NMAX>(tokens, cu, nseq, ntok, L.V0, L.N, i, flags, c))
+    hash_position<NMAX>(L, c, idx + i * L.S);
 }
 
 // One decode step: every thread hashes one (batch entry, row) of the window from the
@@ -205,6 +217,142 @@ __global__ __launch_bounds__(kThreads) void cache_commit_kernel(
 
 __global__ void clear_flags_kernel(int32_t* flags) { flags[0] = 0; }
 
+// ------------------------------------------------------------------ hash statistics
+// Collisions and table hit counts of one order n (section 3.2.2 and Fig. 3 of the same
+// page), exact integers throughout. Rows in use: one bit per table row for each table size,
+// set by every position whose n-gram lands on it (a plain load first, so the repeats of
+// frequent n-grams do not queue atomics on one word), then the set bits are counted.
+// Distinct n-grams: the exact n-gram values (V0^n <= 2^63) are sorted and the boundaries
+// counted.
+
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* __restrict__ w,
+                                                              int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) w[i] = 0u;
+}
+
+__global__ void zero_counts_kernel(int64_t* __restrict__ rows, int32_t nvocab,
+                                   int64_t* __restrict__ distinct) {
+  for (int v = threadIdx.x; v < nvocab; v += blockDim.x) rows[v] = 0;
+  if (threadIdx.x == 0 && distinct != nullptr) *distinct = 0;
+}
+
+template <int NMAX>
+__global__ __launch_bounds__(kThreads) void hash_slots_kernel(
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu, int32_t nseq,
+    int64_t ntok, int64_t V0, int32_t n, const SlotArgs a, uint32_t* __restrict__ bits,
+    int32_t* __restrict__ flags) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t c[NMAX];
+  if (!position_context<NMAX>(tokens, cu, nseq, ntok, V0, n, i, flags, c)) return;
+  for (int v = 0; v < a.nv; ++v) {
+    const uint64_t V = a.V[v], m = a.Vinv[v];
+    uint64_t x = 0;
+#pragma unroll
+    for (int j = NMAX - 1; j >= 0; --j)
+      if (j < n) x = horner_step(x, uint64_t(V0), c[j], V, m);
+    uint32_t* word = bits + a.word_off[v] + (x >> 5);
+    const uint32_t mask = 1u << (x & 31u);
+    if ((*word & mask) == 0u) atomicOr(word, mask);
+  }
+}
+
+// Exact n-gram values (Horner's rule without reduction; exact when V0^n <= 2^63) and the
+// positions, for the sort.
+template <int NMAX>
+__global__ __launch_bounds__(kThreads) void ngram_values_kernel(
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu, int32_t nseq,
+    int64_t ntok, int64_t V0, int32_t n, uint64_t* __restrict__ keys,
+    uint32_t* __restrict__ vals) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t c[NMAX];
+  if (!position_context<NMAX>(tokens, cu, nseq, ntok, V0, n, i, nullptr, c)) return;
+  uint64_t x = 0;
+#pragma unroll
+  for (int j = NMAX - 1; j >= 0; --j)
+    if (j < n) x = x * uint64_t(V0) + c[j];
+  keys[i] = x;
+  vals[i] = uint32_t(i);
+}
+
+// Block sum of one value per thread (kThreads threads), returned to thread 0.
+__device__ __forceinline__ uint64_t block_sum(uint64_t v) {
+  __shared__ uint64_t part[kThreads / 64];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t t = 0;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < kThreads / 64; ++w) t += part[w];
+  return t;
+}
+
+// Sorted values: 1 for each first occurrence.
+__global__ __launch_bounds__(kThreads) void count_distinct_kernel(
+    const uint64_t* __restrict__ keys, int64_t n, int64_t* __restrict__ distinct) {
+  uint64_t c = 0;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * kThreads)
+    c += (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+  const uint64_t t = block_sum(c);
+  if (threadIdx.x == 0 && t != 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(distinct), (unsigned long long)t);
+}
+
+// Set bits of each table size's bitmap (blockIdx.y: size v of the launch).
+__global__ __launch_bounds__(kThreads) void count_rows_kernel(const uint32_t* __restrict__ bits,
+                                                              const SlotArgs a,
+                                                              int64_t* __restrict__ rows) {
+  const int v = blockIdx.y;
+  const int64_t lo = a.word_off[v], hi = a.word_off[v + 1];
+  uint64_t c = 0;
+  for (int64_t w = lo + int64_t(blockIdx.x) * kThreads + threadIdx.x; w < hi;
+       w += int64_t(gridDim.x) * kThreads)
+    c += __popc(bits[w]);
+  const uint64_t t = block_sum(c);
+  if (threadIdx.x == 0 && t != 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(rows + v), (unsigned long long)t);
+}
+
+template <int NMAX>
+hipError_t hash_stats_n(const StatsArgs& s, hipStream_t st) {
+  const int64_t work = s.ntok > int64_t(s.nseq) + 1 ? s.ntok : int64_t(s.nseq) + 1;
+  const unsigned blocks = unsigned((work + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kThreads), 0, st, s.rows, s.nvocab,
+                     s.distinct);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // table sizes in groups of kStatsGroup per launch
+  for (int32_t v0 = 0; v0 < s.nvocab; v0 += kStatsGroup) {
+    SlotArgs a{};
+    a.nv = s.nvocab - v0 < kStatsGroup ? s.nvocab - v0 : kStatsGroup;
+    uint64_t words = 0;
+    for (int v = 0; v < a.nv; ++v) {
+      a.V[v] = uint64_t(s.vocab[v0 + v]);
+      a.Vinv[v] = ~uint64_t(0) / a.V[v];
+      a.word_off[v] = words;
+      words += (a.V[v] + 31) / 32;
+    }
+    a.word_off[a.nv] = words;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(unsigned((words + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, st, s.bits, int64_t(words));
+    hipLaunchKernelGGL(hash_slots_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, s.tokens,
+                       s.cu, s.nseq, s.ntok, s.V0, s.n, a, s.bits, v0 == 0 ? s.flags : nullptr);
+    hipLaunchKernelGGL(count_rows_kernel, dim3(256, unsigned(a.nv)), dim3(kThreads), 0, st,
+                       s.bits, a, s.rows + v0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (s.distinct == nullptr || s.ntok == 0) return hipSuccess;
+  hipLaunchKernelGGL(ngram_values_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, s.tokens,
+                     s.cu, s.nseq, s.ntok, s.V0, s.n, s.keys0, s.vals0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_radix_sort(s.keys0, s.vals0, s.keys1, s.vals1, s.hist, s.ntok, s.key_bits, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(count_distinct_kernel, dim3(1024), dim3(kThreads), 0, st, s.keys0, s.ntok,
+                     s.distinct);
+  return hipGetLastError();
+}
+
 template <int NMAX>
 hipError_t hash_prefill_n(const LayerDesc& L, const int32_t* tokens, const int32_t* cu,
                           int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
@@ -234,6 +382,13 @@ hipError_t launch_hash_prefill(const LayerDesc& L, const int32_t* tokens, const 
   if (L.N <= 4) return hash_prefill_n<4>(L, tokens, cu, nseq, ntok, idx, flags, st);
   if (L.N <= 8) return hash_prefill_n<8>(L, tokens, cu, nseq, ntok, idx, flags, st);
   return hash_prefill_n<NGRAM_MAX_ORDER>(L, tokens, cu, nseq, ntok, idx, flags, st);
+}
+
+hipError_t launch_hash_stats(const StatsArgs& s, hipStream_t st) {
+  if (s.n <= 2) return hash_stats_n<2>(s, st);
+  if (s.n <= 4) return hash_stats_n<4>(s, st);
+  if (s.n <= 8) return hash_stats_n<8>(s, st);
+  return hash_stats_n<NGRAM_MAX_ORDER>(s, st);
 }
 
 hipError_t launch_hash_decode(const LayerDesc& L, const DecodeArgs& a, hipStream_t st) {

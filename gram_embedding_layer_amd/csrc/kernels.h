@@ -44,6 +44,42 @@ hipError_t launch_cache_commit(const LayerDesc& L, int32_t* ring, int64_t* len,
                                const int32_t* n_accept, int32_t nbatch, int32_t tmax,
                                int32_t* flags, hipStream_t st);
 
+// hash statistics of order n over packed sequences (collisions, table hit counts): rows[v]
+// = distinct rows (n-gram value mod vocab[v]) in use; distinct (if not null) = distinct
+// n-grams, from exact values (V0^n <= 2^63, key_bits their width) sorted in keys/vals
+struct SlotArgs {
+  uint64_t V[kStatsGroup];
+  uint64_t Vinv[kStatsGroup];          // floor((2^64 - 1) / V): Barrett multipliers
+  uint64_t word_off[kStatsGroup + 1];  // bitmap of size v: words [word_off[v], word_off[v+1])
+  int32_t nv;
+};
+struct StatsArgs {
+  const int32_t* tokens;
+  const int32_t* cu;
+  int32_t nseq;
+  int64_t ntok;
+  int64_t V0;
+  int32_t n;
+  const int64_t* vocab;   // host [nvocab]
+  int32_t nvocab;
+  int64_t* rows;          // device [nvocab]
+  int64_t* distinct;      // device [1] or null
+  uint32_t* bits;         // bitmaps of kStatsGroup sizes at a time
+  uint64_t* keys0;
+  uint64_t* keys1;
+  uint32_t* vals0;
+  uint32_t* vals1;
+  uint32_t* hist;
+  int32_t key_bits;
+  int32_t* flags;
+};
+hipError_t launch_hash_stats(const StatsArgs& s, hipStream_t st);
+
+// stable LSD radix sort of n (key, value) pairs by the low `bits` key bits, 8 per pass;
+// result in k0/v0, k1/v1 scratch, hist [m + ceil(m / 1024)] with m = 256 * ceil(n / 4096)
+hipError_t launch_radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1,
+                             uint32_t* hist, int64_t n, int bits, hipStream_t st);
+
 // Where the final output rows go: compact row m is written to row
 // (m / group) * stride + off + m % group of `out` (group 0: row m). Rows whose token is
 // kSkipRow are not written.

@@ -53,6 +53,19 @@ struct BwLayout {
 int32_t backward_splits(const LayerDesc& L, int64_t rows);
 bool bw_layout(const LayerDesc& L, int64_t rows, BwLayout* out);
 
+// Hash statistics (collisions and table hit counts of one order n) over ntok positions:
+// bitmaps of the table sizes (one group of kStatsGroup sizes at a time), and, when the exact
+// n-gram values fit (V0^n <= 2^63: `exact`, `key_bits` their width), the sort buffers.
+constexpr int kStatsGroup = 32;
+struct StatsLayout {
+  size_t bits_off, keys0_off, keys1_off, vals0_off, vals1_off, hist_off, total;
+  bool exact;
+  int32_t key_bits;
+};
+// NGRAM_OK, or NGRAM_EINVAL for out-of-range arguments (vocab: host [nvocab]).
+int stats_layout(int64_t V0, int32_t n, int64_t ntok, const int64_t* vocab, int32_t nvocab,
+                 StatsLayout* out);
+
 inline bool aligned(const void* p, size_t a) {
   return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }

@@ -125,4 +125,45 @@ bool bw_layout(const LayerDesc& L, int64_t rows, BwLayout* out) {
   return true;
 }
 
+int stats_layout(int64_t V0, int32_t n, int64_t ntok, const int64_t* vocab, int32_t nvocab,
+                 StatsLayout* out) {
+  if (V0 < 1 || V0 >= (int64_t(1) << 31) || n < 1 || n > NGRAM_MAX_ORDER || ntok < 0 ||
+      nvocab < 0 || (nvocab > 0 && vocab == nullptr) || out == nullptr)
+    return NGRAM_EINVAL;
+  // one group of table sizes at a time: the largest group's bitmaps
+  size_t words = 0;
+  for (int32_t g = 0; g < nvocab; g += kStatsGroup) {
+    size_t w = 0;
+    for (int32_t v = g; v < nvocab && v < g + kStatsGroup; ++v) {
+      if (vocab[v] < 1 || vocab[v] >= (int64_t(1) << 31)) return NGRAM_EINVAL;
+      w += size_t((vocab[v] + 31) / 32);
+    }
+    if (w > words) words = w;
+  }
+  // exact values: the largest is V0^n - 1, so V0^n <= 2^63 keeps them in 63 bits
+  StatsLayout L{};
+  uint64_t p = 1;
+  L.exact = true;
+  for (int j = 0; j < n && L.exact; ++j) {
+    if (p > (uint64_t(1) << 63) / uint64_t(V0)) L.exact = false;
+    else p *= uint64_t(V0);
+  }
+  L.key_bits = 0;
+  if (L.exact)
+    while (L.key_bits < 64 && (uint64_t(1) << L.key_bits) < p) ++L.key_bits;
+  const size_t T = L.exact ? size_t(ntok) : 0;
+  size_t o = 256;                                    // error flags
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.bits_off = take(words * 4);
+  L.keys0_off = take(T * 8);
+  L.keys1_off = take(T * 8);
+  L.vals0_off = take(T * 4);
+  L.vals1_off = take(T * 4);
+  const size_t m = 256 * ((T + kSortTile - 1) / kSortTile > 0 ? (T + kSortTile - 1) / kSortTile : 1);
+  L.hist_off = take(L.exact ? (m + (m + 1023) / 1024) * 4 : 0);
+  L.total = o;
+  *out = L;
+  return NGRAM_OK;
+}
+
 }  // namespace ngram

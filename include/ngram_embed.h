@@ -302,6 +302,28 @@ int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables
                          int64_t ntok, const void* dout, float* dE0, float* const* dE,
                          float* dW, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- hash statistics
+ * Hash collisions and table hit counts of order n (section 3.2.2 and Fig. 3 of the same
+ * page), over every position of ntok packed tokens (the n-grams a layer hashes: pad id 0
+ * before a sequence's start; tokens/cu_seqlens/nseq as in ngram_embed_hash):
+ *   rows[v]   = number of distinct table rows H_n = (n-gram value) mod vocab[v] in use,
+ *   *distinct = number of distinct n-grams (if distinct is not NULL).
+ * The pages count as collisions the unique n-grams lost to the modulo, distinct - rows[v];
+ * the hit rate is rows[v] / vocab[v]. Exact integers: H_n by the same Horner reduction as
+ * ngram_embed_hash; distinct from the exact n-gram values, which needs V0^n <= 2^63 (else
+ * NGRAM_EOVERFLOW; rows alone work for any n). vocab: host array of nvocab >= 0 table sizes,
+ * 1 <= vocab[v] < 2^31; 1 <= n <= NGRAM_MAX_ORDER; 1 <= V0 < 2^31. rows: device int64
+ * [nvocab]; distinct: device int64 [1]; both overwritten. ws: at least
+ * ngram_hash_stats_workspace_size(...) bytes (0 on bad arguments), 256-byte aligned, error
+ * flags at offset 0 (NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS; counts then unspecified).
+ * Intermediate buffers are filled by kernels, so the workspace needs no clearing. */
+size_t ngram_hash_stats_workspace_size(int64_t V0, int32_t n, int64_t ntok,
+                                       const int64_t* vocab, int32_t nvocab);
+int ngram_hash_stats(int64_t V0, int32_t n, const int32_t* tokens, const int32_t* cu_seqlens,
+                     int32_t nseq, int64_t ntok, const int64_t* vocab, int32_t nvocab,
+                     int64_t* rows, int64_t* distinct, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* ---------------------------------------------------------------- errors
  * Wait for `stream`, then copy the workspace's error flags to *flags (host). */
 int ngram_embed_read_error_flag(const void* ws, int32_t* flags, void* stream);

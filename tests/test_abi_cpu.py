@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "ngram_cache_commit", "ngram_embed_backward",
               "ngram_embed_backward_workspace_size"):
         assert n in names
-    assert len(names) == 19
+    assert len(names) == 21
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -155,6 +155,35 @@ def test_layers_argument_checks(lib):
     assert dl(P(c), two, 2, P(cache), FAKE, FAKE, 5, None, outs, FAKE, ws_dec - 1, 0) == -4
     assert dl(P(c), mixed, 2, P(cache), FAKE, FAKE, 5, None, outs, FAKE, ws_dec, 0) == -3
     assert dl(P(c), two, 2, P(cache), FAKE, FAKE, 5, None, outs_bad, FAKE, ws_dec, 0) == -3
+
+
+def test_hash_stats_checks(lib):
+    """Hash statistics: workspace sizes, exact-value limit, argument checks."""
+    P = ctypes.byref
+    vocab = [5003, 32, 1, 2 ** 31 - 1]
+    n1 = g.ngram_hash_stats_workspace_size(1000, 2, 100, vocab)
+    n2 = g.ngram_hash_stats_workspace_size(1000, 2, 10000, vocab)
+    assert 0 < n1 < n2 and n1 % 256 == 0
+    # the bitmaps of one group of sizes: 2^31 - 1 rows need 2^26 words
+    assert n1 >= (5003 + 31) // 32 * 4 + 32 // 32 * 4 + 4 + (2 ** 26) * 4
+    assert g.ngram_hash_stats_workspace_size(1000, 2, 100, [0]) == 0
+    assert g.ngram_hash_stats_workspace_size(1000, 2, 100, [2 ** 31]) == 0
+    assert g.ngram_hash_stats_workspace_size(0, 2, 100, vocab) == 0
+    assert g.ngram_hash_stats_workspace_size(1000, 0, 100, vocab) == 0
+    assert g.ngram_hash_stats_workspace_size(1000, 17, 100, vocab) == 0
+    # no sort buffers once the exact values do not fit: V0 = 2^17, n = 4 is 2^68
+    big = g.ngram_hash_stats_workspace_size(131072, 4, 10 ** 6, [7])
+    small = g.ngram_hash_stats_workspace_size(131072, 3, 10 ** 6, [7])
+    assert big < small
+    hs = lib.ngram_hash_stats
+    arr = (ctypes.c_int64 * 1)(7)
+    ws = g.ngram_hash_stats_workspace_size(131072, 4, 16, [7])
+    assert hs(131072, 4, FAKE, FAKE, 1, 16, arr, 1, FAKE, FAKE, FAKE, ws, 0) == -5
+    assert hs(131072, 4, FAKE, FAKE, 1, 16, arr, 1, FAKE + 4, None, FAKE, ws, 0) == -3
+    assert hs(131072, 4, FAKE, FAKE, 1, 16, arr, 1, FAKE, None, FAKE, ws - 1, 0) == -4
+    assert hs(131072, 4, FAKE, FAKE, 0, 16, arr, 1, FAKE, None, FAKE, ws, 0) == -1
+    assert hs(131072, 4, FAKE, FAKE, 1, 16, None, 1, FAKE, None, FAKE, ws, 0) == -1
+    assert hs(131072, 4, FAKE, FAKE, 1, 16, arr, 0, None, None, FAKE, ws, 0) == 0
 
 
 def test_decode_and_cache_argument_checks(lib):

@@ -110,6 +110,20 @@ int main() {
   basic.K = 1;
   basic.form = 2;
   EXPECT(ngram::describe(&basic, &Lb) == NGRAM_EINVAL);
+  // hash statistics: exact n-gram values while V0^n <= 2^63, their width for the sort
+  ngram::StatsLayout sl;
+  const int64_t sizes[3] = {7, 64, 33};
+  EXPECT(ngram::stats_layout(10, 2, 100, sizes, 3, &sl) == NGRAM_OK && sl.exact &&
+         sl.key_bits == 7 && sl.bits_off == 256);
+  EXPECT(ngram::stats_layout(131072, 3, 100, sizes, 3, &sl) == NGRAM_OK && sl.key_bits == 51);
+  EXPECT(ngram::stats_layout(int64_t(1) << 21, 3, 100, sizes, 3, &sl) == NGRAM_OK &&
+         sl.exact && sl.key_bits == 63);
+  EXPECT(ngram::stats_layout((int64_t(1) << 21) + 1, 3, 100, sizes, 3, &sl) == NGRAM_OK &&
+         !sl.exact && sl.keys0_off == sl.keys1_off);
+  const int64_t bad_sizes[1] = {0};
+  EXPECT(ngram::stats_layout(10, 2, 100, bad_sizes, 1, &sl) == NGRAM_EINVAL);
+  EXPECT(ngram::stats_layout(10, 0, 100, sizes, 3, &sl) == NGRAM_EINVAL);
+  EXPECT(ngram::stats_layout(10, 2, -1, sizes, 3, &sl) == NGRAM_EINVAL);
   EXPECT(ngram::aligned(reinterpret_cast<void*>(0x1000), 256));
   EXPECT(!ngram::aligned(reinterpret_cast<void*>(0x1004), 16));
   EXPECT(!ngram::aligned(nullptr, 4));

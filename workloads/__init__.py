@@ -25,7 +25,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "mid_gap_primes",
     "uniform_ids", "zipf_ids", "token_batch", "cu_seqlens_from_lengths",
-    "host_tables", "device_tables", "split_stacked_w",
+    "host_tables", "device_tables", "split_stacked_w", "collision_study",
 ]
 
 
@@ -229,3 +229,25 @@ def split_stacked_w(W_stack, S: int):
     """The S blocks W_{n,k} [D, d] of a stacked [D, S*d] projection (a view per block)."""
     d = W_stack.shape[1] // S
     return [W_stack[:, s * d:(s + 1) * d] for s in range(S)]
+
+
+# ---------------------------------------------------------------- hash-collision study
+
+def collision_study(V0: int = 131072, nseq: int = 100, seqlen: int = 8192, seed: int = 10,
+                    lo: int = 30, hi: int = 33):
+    """Inputs of the collision measurement of section 3.2.2 (Fig. 3b): 100 sequences of
+    Zipf(1.1) ids over a 128K base vocabulary stand in for the pretraining sequences, and
+    table sizes between 30x and 33x the base vocabulary, sampled densely around the integer
+    multiples of V0 (offsets 0, +-1, +-8, +-64, +-1024) and every 3*V0/32 elsewhere.
+    Returns (ids int32 [nseq, seqlen], sorted table sizes)."""
+    rng = _rng(seed, 0)
+    ids = zipf_ids(rng, V0, (nseq, seqlen))
+    sizes = set()
+    for m in range(lo, hi + 1):
+        for off in (-1024, -64, -8, -1, 0, 1, 8, 64, 1024):
+            v = m * V0 + off
+            if lo * V0 <= v <= hi * V0:
+                sizes.add(v)
+    for k in range(0, 32 * (hi - lo) // 3 + 1):
+        sizes.add(lo * V0 + k * 3 * V0 // 32)
+    return ids, sorted(sizes)
