@@ -80,13 +80,22 @@ enum OutMode {
 // ------------------------------------------------------------------ bf16 matrix-core path
 
 constexpr int kBN = 256;          // outputs per tile
-constexpr int kBK = 64;           // contraction depth of one slice: 128 bytes of a row, one
-                                  // full L2 line per row per load
-constexpr int kIdxBytes = 16384;  // LDS for the tile's hash indices (BM * S int32)
+constexpr int kBK = 64;           // slice depths divide this (the routing checks d % kBK)
 
-// LDS slice buffers per tile height (160 KB of LDS per CU, 16 KB of it for indices):
-// 256-row tiles double-buffer, shorter tiles keep two slices in flight.
-template <int BM> struct Stages { static constexpr int value = BM >= 256 ? 2 : 3; };
+// LDS for a tile's hash indices (BM * S int32) and, at its end, the rows' E_0 tokens (BM
+// int32): S <= 16 fits 256-row tiles, S <= 31 128-row tiles, S <= 64 64-row tiles.
+template <int BM> struct IdxLds {
+  static constexpr int bytes = BM >= 256 ? 17408 : BM >= 128 ? 16384 : 16640;
+};
+
+// Contraction depth of one slice (BK = 64: a full 128-byte L2 line of each row per load)
+// and LDS slice buffers (NST; 160 KB of LDS per CU): 256-row tiles double-buffer, shorter
+// tiles keep two slices in flight. Measured on the 64K-token batch and not adopted: 32-deep
+// slices with four buffers (twice the barriers, half-line loads): 1365 vs 1251 us.
+template <int BM> struct Tile {
+  static constexpr int BK = 64;
+  static constexpr int NST = BM >= 256 ? 2 : 3;
+};
 
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -117,26 +126,34 @@ template <int BM> struct WaveGrid { static constexpr int WGM = BM >= 128 ? 4 : 2
 
 template <int BM, int OM>
 __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
-  constexpr int NST = Stages<BM>::value;
+  constexpr int NST = Tile<BM>::NST;
+  constexpr int BK = Tile<BM>::BK;
+  constexpr int RB = BK * 2;             // bytes of one row per slice
+  constexpr int CPR = RB / 16;           // 16-byte chunks per row per slice
+  constexpr int RPL = 1024 / RB;         // rows per wave load (64 lanes x 16 bytes)
+  constexpr int KS = BK / 16;            // 16-deep k-steps per slice
   constexpr int WGM = WaveGrid<BM>::WGM;
   constexpr int WGN = 8 / WGM;
   constexpr int WM = BM / WGM;           // rows per wave
   constexpr int WN = kBN / WGN;          // outputs per wave
   constexpr int TI = WM / 32;            // 32-row MFMA blocks per wave
   constexpr int TJ = WN / 32;            // 32-output MFMA blocks per wave
-  constexpr int A_BYTES = BM * kBK * 2;  // rows of 128 bytes, XOR-swizzled 16-byte chunks
-  constexpr int B_BYTES = kBN * kBK * 2;
+  constexpr int A_BYTES = BM * RB;       // rows of RB bytes, XOR-swizzled 16-byte chunks
+  constexpr int B_BYTES = kBN * RB;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int QA = BM / 64;            // A loads per wave per slice (8 rows each)
-  constexpr int QB = kBN / 64;           // W loads per wave per slice
+  constexpr int QA = A_BYTES / 8192;     // A loads per wave per slice (RPL rows each)
+  constexpr int QB = B_BYTES / 8192;     // W loads per wave per slice
   constexpr int PER_SLICE = QA + QB;
   // One LDS pool: NST slice stages + the tile's hash indices during the main loop; the
   // epilogue then reuses it to turn each wave's results into row-major order.
   constexpr int EP_PITCH = WN * 4 + 32;  // bytes per staged fp32 row (conflict-free pitch)
-  constexpr int POOL = NST * STAGE + kIdxBytes;
-  static_assert(8 * 32 * EP_PITCH <= POOL, "epilogue staging must fit the LDS pool");
+  constexpr int IDXB = IdxLds<BM>::bytes;
+  constexpr int POOL = NST * STAGE + IDXB;
+  static_assert(8 * 32 * EP_PITCH <= POOL - BM * 4,
+                "epilogue staging must fit the LDS pool, short of the tokens");
   __shared__ __attribute__((aligned(1024))) char lds[POOL];
   int32_t* sidx = reinterpret_cast<int32_t*>(lds + NST * STAGE);
+  int32_t* stok = reinterpret_cast<int32_t*>(lds + NST * STAGE + IDXB - BM * 4);
 
   // -- XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous range
   //    of virtual tiles and walk a range GM row tiles at a time, outputs slowest, so the
@@ -164,30 +181,38 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WGN, wn = w % WGN;
 
-  // -- hash indices of the tile's rows (rows past the batch repeat the last row)
+  // -- hash indices of the tile's rows (rows past the batch repeat the last row), and the
+  //    rows' E_0 tokens for the epilogue (-1 past the batch; 0 without E_0)
   for (int e = t; e < BM * a.S; e += 512) {
     const int r = e / a.S, s = e - r * a.S;
     const int64_t m = m0 + r < a.nrows ? m0 + r : a.nrows - 1;
     sidx[e] = a.idx[m * a.S + s];
   }
+  if (OM != kOutPartial && t < BM) {
+    const int64_t m = m0 + t;
+    stok[t] = m < a.nrows ? (a.E0[blockIdx.z] != nullptr ? a.tok[m] : 0) : -1;
+  }
   __syncthreads();
 
-  // -- loads: lane p fills LDS chunk (row p/8, chunk p%8) of an 8-row group with logical
-  //    16-byte chunk c = (p%8) ^ (row%8), so that fragment reads (8 lanes = 8 rows, one
-  //    logical chunk) hit 8 different bank groups; 8 lanes read one 128-byte row piece.
-  const int prow = lane >> 3;
-  const int pchunk = (lane & 7) ^ prow;
+  // -- loads: lane p fills LDS chunk (row p/CPR, chunk p%CPR) of an RPL-row group with
+  //    logical 16-byte chunk c = (p%CPR) ^ swz(row), so that fragment reads (8 lanes = 8
+  //    rows, one logical chunk) hit 8 different 16-byte bank groups; CPR lanes read one
+  //    row piece. swz(r) = r mod 8 for 128-byte pieces, (r/2) mod 4 for 64-byte ones (two
+  //    rows per 128 bytes of banks).
+  auto swz = [](int r) __attribute__((always_inline)) { return (r / (8 / CPR)) % CPR; };
+  const int prow = lane / CPR;
+  const int pchunk = (lane % CPR) ^ swz(prow);
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)lds));
   const int layer = blockIdx.z;
   const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E) + layer * a.S;
   const uint16_t* W = static_cast<const uint16_t*>(a.W[layer]);
   const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.ldb + pchunk * 8;
   const uint16_t* ap[QA];
-  const int KT_ALL = a.K / kBK;  // slices of the whole contraction
+  const int KT_ALL = a.K / BK;   // slices of the whole contraction
   // this block's slice range (all of it unless the contraction is split)
   const int kt_lo = OM == kOutPartial ? int(int64_t(split) * KT_ALL / a.splits) : 0;
   const int kt_hi = OM == kOutPartial ? int(int64_t(split + 1) * KT_ALL / a.splits) : KT_ALL;
-  const int kps = a.d / kBK;     // slices per sub-table
+  const int kps = a.d / BK;      // slices per sub-table
   int s_cur = -1;
 
   // The slice being fetched: its LDS stage, its offset within the current sub-table.
@@ -198,22 +223,22 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
       s_cur = kt / kps;
 #pragma unroll
       for (int q = 0; q < QA; ++q) {
-        const int r = w * (BM / 8) + q * 8 + prow;
+        const int r = w * (BM / 8) + q * RPL + prow;
         const uint32_t id = min(uint32_t(sidx[r * a.S + s_cur]), a.Vm1[s_cur]);
         ap[q] = E[s_cur] + int64_t(id) * a.d + pchunk * 8;
       }
     }
     f_sb = lds0 + uint32_t((kt - kt_lo) % NST) * STAGE;
-    f_koff = (kt - s_cur * kps) * kBK;
+    f_koff = (kt - s_cur * kps) * BK;
     f_kt = kt;
   };
   // load q of this wave's PER_SLICE loads of the slice (A rows first, then W rows)
   auto dma = [&](int q) __attribute__((always_inline)) {
     if (q < QA)
-      dma16(ap[q] + f_koff, f_sb + w * (BM * 16) + q * 1024);
+      dma16(ap[q] + f_koff, f_sb + w * (BM / 8) * RB + q * 1024);
     else
-      dma16(bp + int64_t((q - QA) * 8) * a.ldb + f_kt * kBK,
-            f_sb + A_BYTES + w * 4096 + (q - QA) * 1024);
+      dma16(bp + int64_t((q - QA) * RPL) * a.ldb + f_kt * BK,
+            f_sb + A_BYTES + w * 32 * RB + (q - QA) * 1024);
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
     prep(kt);
@@ -231,20 +256,20 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
 
   // fragment lane (fr, fk): 8 consecutive k (logical chunk 2*kk + fk) of row fr
   const int fr = lane & 31, fk = lane >> 5;
-  const int arow0 = (wm * WM + fr) * 128;          // byte offset of the lane's first A row
-  const int brow0 = A_BYTES + (wn * WN + fr) * 128;
-  int pcs[4];                                      // physical chunk byte offset per k-step
+  const int arow0 = (wm * WM + fr) * RB;           // byte offset of the lane's first A row
+  const int brow0 = A_BYTES + (wn * WN + fr) * RB;
+  int pcs[KS];                                     // physical chunk byte offset per k-step
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) pcs[kk] = ((2 * kk + fk) ^ (fr & 7)) * 16;
+  for (int kk = 0; kk < KS; ++kk) pcs[kk] = ((2 * kk + fk) ^ swz(fr)) * 16;
 
   bf16x8_t wf[2][TJ], xf[2][TI];
   auto frags = [&](const char* sp, int kk, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
-      wf[buf][j] = *reinterpret_cast<const bf16x8_t*>(sp + brow0 + j * 32 * 128 + pcs[kk]);
+      wf[buf][j] = *reinterpret_cast<const bf16x8_t*>(sp + brow0 + j * 32 * RB + pcs[kk]);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
-      xf[buf][i] = *reinterpret_cast<const bf16x8_t*>(sp + arow0 + i * 32 * 128 + pcs[kk]);
+      xf[buf][i] = *reinterpret_cast<const bf16x8_t*>(sp + arow0 + i * 32 * RB + pcs[kk]);
   };
   // One 16-deep k-step: TI x TJ matrix-core ops. W block as the first operand: each lane's
   // results are 4 consecutive outputs of one row, which makes the epilogue's E_0 reads and
@@ -254,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   // stages, so the loads must land within the slice) place them in the first three of the
   // four k-steps, which measured ~2% faster than all four; shorter tiles use all four.
   constexpr int NM = TI * TJ;
-  constexpr int LOAD_STEPS = BM >= 256 ? 3 : 4;
+  constexpr int LOAD_STEPS = NST == 2 && KS == 4 ? 3 : KS;
   constexpr int DPP = (PER_SLICE + LOAD_STEPS - 1) / LOAD_STEPS;
   constexpr int EVERY = NM / DPP > 0 ? NM / DPP : 1;
   // every load of the slice gets a slot (NM / EVERY slots per k-step, at most DPP used)
@@ -278,22 +303,23 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   const int NK = kt_hi - kt_lo;  // slices of this block
   for (int p = 0; p < NST - 1 && p < NK; ++p) issue(kt_lo + p);
   for (int k = 0; k < NK; ++k) {
-    // own loads of slice k done (later slices may stay in flight), then all waves meet:
-    // slice k is complete in LDS and every wave is past slice k-1, whose buffer the
-    // load of slice k+NST-1 reuses.
-    if (NST == 3 && k + 1 < NK) wait_loads_and_meet<PER_SLICE>();
+    // own loads of slice k done (the later slices already issued stay in flight), then all
+    // waves meet: slice k is complete in LDS and every wave is past slice k-1, whose buffer
+    // the load of slice k+NST-1 reuses.
+    const int ahead = NST - 2 < NK - 1 - k ? NST - 2 : NK - 1 - k;
+    if (NST >= 4 && ahead >= 2) wait_loads_and_meet<(NST >= 4 ? 2 : 0) * PER_SLICE>();
+    else if (NST >= 3 && ahead >= 1) wait_loads_and_meet<(NST >= 3 ? 1 : 0) * PER_SLICE>();
     else wait_loads_and_meet<0>();
     const bool loads = k + NST - 1 < NK;
     if (loads) prep(kt_lo + k + NST - 1);
     const char* sp = lds + (k % NST) * STAGE;
     frags(sp, 0, 0);
-    frags(sp, 1, 1);
-    mma(0, loads, 0);
-    frags(sp, 2, 0);
-    mma(1, loads, 1);
-    frags(sp, 3, 1);
-    mma(0, loads, 2);
-    mma(1, loads, 3);
+    if (KS > 1) frags(sp, 1, 1);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      mma(kk & 1, loads, kk);
+      if (kk + 2 < KS) frags(sp, kk + 2, kk & 1);
+    }
   }
 
   // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*WN + 32j + 8g + 4fk + q of row
@@ -307,7 +333,24 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   char* ep = lds + w * (32 * EP_PITCH);
   constexpr int LPR = WN / 4;           // lanes per output row
   constexpr int RPI = 64 / LPR;         // rows per wave instruction
+  constexpr int NIT = 32 / RPI;
   const int er = lane / LPR, ec = lane % LPR;
+  // the E_0 pieces of all of the wave's output rows are requested before any is used
+  // (tokens from LDS), so the tile waits for one round trip to memory instead of two (the
+  // token, then its row) per 32-row group: 12-20 us less per 64K-token launch
+  u32x2_t ev_all[OM != kOutPartial ? TI : 1][NIT];
+  if constexpr (OM != kOutPartial) {
+    const int n = n0 + wn * WN + ec * 4;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int32_t tk = stok[wm * WM + i * 32 + it * RPI + er];
+        ev_all[i][it] = u32x2_t{0u, 0u};
+        if (E0 != nullptr && uint32_t(tk) < uint32_t(a.V0))
+          ev_all[i][it] = *reinterpret_cast<const u32x2_t*>(E0 + int64_t(tk) * a.N + n);
+      }
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -322,7 +365,6 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // all loads of the 32 rows first (tok, then E_0), then the stores: a load placed after
     // a store would wait for it, since the compiler cannot rule out aliasing
-    constexpr int NIT = 32 / RPI;
     const int64_t mrow = m0 + wm * WM + i * 32 + er;
     const int n = n0 + wn * WN + ec * 4;
     if constexpr (OM == kOutPartial) {
@@ -340,17 +382,11 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     // without E_0 (dense products) every row is valid and nothing is added
     const bool has_e0 = E0 != nullptr;
     int32_t tk[NIT];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int64_t m = mrow + it * RPI;
-      tk[it] = m < a.nrows ? (has_e0 ? a.tok[m] : 0) : -1;
-    }
     u32x2_t ev[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      ev[it] = u32x2_t{0u, 0u};
-      if (has_e0 && uint32_t(tk[it]) < uint32_t(a.V0))
-        ev[it] = *reinterpret_cast<const u32x2_t*>(E0 + int64_t(tk[it]) * a.N + n);
+      tk[it] = stok[wm * WM + i * 32 + it * RPI + er];
+      ev[it] = ev_all[i][it];
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -545,25 +581,33 @@ hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStre
   if (dtype == NGRAM_BF16 && a.N % kBN == 0 && a.d % kBK == 0 && a.K % kBK == 0) {
     // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
     // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
-    // rows' hash indices in LDS, BM * S <= kIdxBytes / 4.
+    // rows' hash indices (and E_0 tokens) in LDS.
     const int64_t tiles_n = a.N / kBN;
-    const int64_t idx_cap = kIdxBytes / 4;
     const int64_t sp = om == kOutPartial ? a.splits : 1;
-    const bool big = ((nrows + 255) / 256) * tiles_n * sp >= 512 && 256 * a.S <= idx_cap;
-    const bool mid = ((nrows + 127) / 128) * tiles_n * sp >= 256 && 128 * a.S <= idx_cap;
+    const int per_row = a.S + (om != kOutPartial ? 1 : 0);   // int32 per row
+    const bool f256 = 256 * per_row * 4 <= IdxLds<256>::bytes;
+    const bool f128 = 128 * per_row * 4 <= IdxLds<128>::bytes;
+    const bool f64 = 64 * per_row * 4 <= IdxLds<64>::bytes;
+    const bool big = ((nrows + 255) / 256) * tiles_n * sp >= 512;
+    const bool mid = ((nrows + 127) / 128) * tiles_n * sp >= 256;
+    const int bm = big && f256 ? 256 : (big || mid) && f128 ? 128 : f64 ? 64 : f128 ? 128
+                 : f256 ? 256 : 0;
     if (om == kOutPartial) {
-      if (big || 128 * a.S > idx_cap) return run_mfma<256, kOutPartial>(a, nrows, osz, st);
-      if (mid) return run_mfma<128, kOutPartial>(a, nrows, osz, st);
-      return run_mfma<64, kOutPartial>(a, nrows, osz, st);
+      if (bm == 256) return run_mfma<256, kOutPartial>(a, nrows, osz, st);
+      if (bm == 128) return run_mfma<128, kOutPartial>(a, nrows, osz, st);
+      if (bm == 64) return run_mfma<64, kOutPartial>(a, nrows, osz, st);
+      return hipErrorInvalidValue;
     }
     if (om == kOutF32) {
-      if (big) return run_mfma<256, kOutF32>(a, nrows, osz, st);
-      if (mid) return run_mfma<128, kOutF32>(a, nrows, osz, st);
-      return run_mfma<64, kOutF32>(a, nrows, osz, st);
+      if (bm == 256) return run_mfma<256, kOutF32>(a, nrows, osz, st);
+      if (bm == 128) return run_mfma<128, kOutF32>(a, nrows, osz, st);
+      if (bm == 64) return run_mfma<64, kOutF32>(a, nrows, osz, st);
+    } else {
+      if (bm == 256) return run_mfma<256, kOutBf16>(a, nrows, osz, st);
+      if (bm == 128) return run_mfma<128, kOutBf16>(a, nrows, osz, st);
+      if (bm == 64) return run_mfma<64, kOutBf16>(a, nrows, osz, st);
     }
-    if (big) return run_mfma<256, kOutBf16>(a, nrows, osz, st);
-    if (mid) return run_mfma<128, kOutBf16>(a, nrows, osz, st);
-    return run_mfma<64, kOutBf16>(a, nrows, osz, st);
+    // no tile keeps this many indices: the generic path below
   }
   if (om == kOutPartial) return hipErrorInvalidValue;   // callers use kOutF32 here
   const unsigned gy = unsigned((a.N + 63) / 64);
