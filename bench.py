@@ -417,8 +417,8 @@ def bench_layers(g, WL, dev, stream, steps):
     N = 3, K = 2, 2.0B n-gram parameters each, 38 GB in all). Each layer's embeddings in one
     call per layer, against all 8 layers in one call (hash once, the projections of the 8
     layers in one launch): 64K-token prefill batches, and speculative-verify decode steps
-    (256 sequences x 5 ids, no commit so every step does the same work) in HIP graphs of
-    200 steps."""
+    (256 sequences x 5 ids, no commit so every step does the same work), each captured in
+    HIP graphs so that host launch gaps do not count."""
     import numpy as np
     import torch
 
@@ -443,24 +443,29 @@ def bench_layers(g, WL, dev, stream, steps):
     def batched(cs):
         g.ngram_embed_prefill_layers(cfg, tabs, toks, cu, outs, ws, stream=cs)
 
-    def timed(fn, n):
-        for _ in range(2):
-            fn(stream)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        for a, b in ev:
-            a.record(stream)
-            fn(stream)
-            b.record(stream)
+    def graph_us(body, reps):
+        """GPU time of `reps` calls captured in one HIP graph (no host gaps), per call."""
+        body(stream)
         torch.cuda.synchronize(dev)
-        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream()
+            for _ in range(reps):
+                body(cs)
+        ts = []
+        for _ in range(3):
+            torch.cuda.synchronize(dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize(dev)
+            ts.append(a.elapsed_time(b) * 1e-3 / reps)
+        del gr
+        return float(np.median(ts))
 
-    # interleave the two forms so that clocks and caches treat them alike
-    t_sep, t_bat = [], []
-    for _ in range(steps):
-        t_sep.append(timed(separate, 1))
-        t_bat.append(timed(batched, 1))
-    t_sep, t_bat = float(np.mean(t_sep)), float(np.mean(t_bat))
+    t_sep = graph_us(separate, steps)
+    t_bat = graph_us(batched, steps)
     flops = 2.0 * T * w.D * w.D * w.layers
     res = {"workload": w.name, "layers": w.layers,
            "prefill": {"tokens": T, "us_separate_calls": round(t_sep * 1e6, 1),
