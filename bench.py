@@ -250,7 +250,24 @@ def main():
               "bytes_read": read_b, "bytes_written": read_b,
               "traffic": counter_traffic("gather", "gather.hip")}
     log(f"gather {t_g*1e6:.1f} us: {2*read_b/t_g/1e9:.0f} GB/s read+write")
-    del G
+    # control: uniform ids (no Zipf repeats, so no reuse of rows within a batch)
+    uni = [torch.as_tensor(WL.uniform_ids(np.random.default_rng([7, p]), w.V0, (T,))).to(dev)
+           for p in range(nrot)]
+    for r in range(nrot):
+        g.ngram_embed_hash(cfg, uni[r], cu, idx_rot[r], None, stream=stream)
+    for k in range(3):
+        g.ngram_embed_gather(cfg, tables, idx_rot[k % nrot], G, stream=stream)
+    for k in range(args.steps):
+        gev[k][0].record(stream)
+        g.ngram_embed_gather(cfg, tables, idx_rot[k % nrot], G, stream=stream)
+        gev[k][1].record(stream)
+    torch.cuda.synchronize(dev)
+    t_u = float(np.mean([a.elapsed_time(b) for a, b in gev])) * 1e-3
+    gather["uniform_ids_control"] = {
+        "kernel_us": round(t_u * 1e6, 1), "read_write_GBps": round(2 * read_b / t_u / 1e9, 1),
+        "frac_of_hbm_peak": round(2 * read_b / t_u / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"gather, uniform ids: {t_u*1e6:.1f} us: {2*read_b/t_u/1e9:.0f} GB/s read+write")
+    del G, uni
 
     amp = None
     if not args.no_amp:

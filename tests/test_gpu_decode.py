@@ -185,6 +185,61 @@ def test_decode_30b_spec_verify_shape(lib, tables_30b):
     check_cache(cfg, cache, orc.hist)
 
 
+def test_decode_30b_1000_steps(lib, tables_30b):
+    """The speculative-verify workload end to end: 1000 steps of 256 x 5 ids, all committed,
+    on the 30B-parameter tables (the ids the benchmark times). Every index of every step
+    (15.36M) bit for bit against the oracle's hash of the sequences (history followed by all
+    committed ids: a decode step's rows are the prefill rows of those positions), and
+    the embeddings of 34 steps (first, last, 32 seeded) against the oracle."""
+    wd = WL.workload("decode_spec5_30b")
+    cfg = cfg_of(wd)
+    E0, E, W = tables_30b
+    tables = g.Tables(E0, E, W)
+    nseq, tmax, nsteps, L = wd.batch, wd.decode_new, wd.decode_steps, wd.seqlen
+    hist = WL.token_batch(wd, purpose=0)                                   # [256, 8192]
+    ids = WL.token_batch(wd, purpose=1, batch=nsteps * nseq, seqlen=tmax).reshape(
+        nsteps, nseq, tmax)
+    cache = g.Cache.empty(cfg, nseq)
+    cu_h = np.arange(nseq + 1, dtype=np.int32) * L
+    g.ngram_cache_init(cfg, cache, dev(hist.reshape(-1)), dev(cu_h))
+    ws = g.alloc_workspace(cfg, nseq * tmax)
+    _, idx_off = g.ngram_embed_workspace_layout(cfg, nseq * tmax)
+    idx_ws = ws[idx_off:idx_off + nseq * tmax * wd.S * 4].view(torch.int32)
+    rng = np.random.default_rng(8)
+    check = sorted({0, nsteps - 1} | set(int(x) for x in rng.choice(nsteps, 32, replace=False)))
+    all_idx = torch.empty((nsteps, nseq * tmax * wd.S), dtype=torch.int32, device="cuda")
+    outs = {}
+    n_new = dev(np.full(nseq, tmax, np.int32))
+    ids_dev = dev(ids)
+    out = torch.empty((nseq, tmax, wd.D), dtype=torch.bfloat16, device="cuda")
+    for step in range(nsteps):
+        g.ngram_embed_decode(cfg, tables, cache, ids_dev[step], n_new, out, ws, n_commit=n_new)
+        all_idx[step].copy_(idx_ws)
+        if step in check:
+            outs[step] = out.clone()
+    torch.cuda.synchronize()
+    assert g.ngram_embed_read_error_flag(ws) == 0
+    assert bool((cache.len == L + nsteps * tmax).all())
+    # the oracle: every sequence = history + the 5000 committed ids, hashed once. Only the
+    # last N-1 history ids reach a decode position's context, so each sequence is cut to
+    # them plus the committed ids (the cut's own first N-1 positions are not compared)
+    h = wd.N - 1
+    full = np.concatenate([hist[:, L - h:], ids.transpose(1, 0, 2).reshape(nseq, nsteps * tmax)],
+                          axis=1)
+    cu = np.arange(nseq + 1, dtype=np.int64) * full.shape[1]
+    want = oracle.hash_indices(wd.V0, wd.N, wd.K, wd.V, full.reshape(-1), cu)
+    want = want.reshape(nseq, full.shape[1], wd.S)[:, h:, :]               # decode positions
+    want = want.reshape(nseq, nsteps, tmax, wd.S).transpose(1, 0, 2, 3)   # [step, b, j, s]
+    got = all_idx.cpu().numpy().reshape(nsteps, nseq, tmax, wd.S)
+    np.testing.assert_array_equal(got, want)
+    fetch, Wb = device_fetch(E0, E), w_blocks(W, wd.S)
+    for step in check:
+        e = oracle.embed_from_indices(wd.D, wd.N, wd.K, ids[step].reshape(-1),
+                                      want[step].reshape(-1, wd.S), fetch, Wb)
+        assert_close(to_f64(outs[step]).reshape(nseq * tmax, wd.D), e, "bf16", f"step {step}")
+    del outs, all_idx
+
+
 def test_decode_graph_replays(lib):
     """Four decode+commit steps captured in one HIP graph, replayed three times from the
     same cache snapshot with eager work in between; every replay equals the eager run."""
