@@ -101,9 +101,14 @@ __global__ __launch_bounds__(kThreads) void hash_decode_kernel(const LayerDesc L
   const int j = a.row_begin + jj;
   const bool active = threadIdx.x < spb * a.width && b < a.nbatch;
   const int nm1 = L.N - 1;
-  int nn = 0, slot = 0;
+  int nn = 0, slot = 0, acc = 0;
   bool slot_ok = false;
   int64_t committed = 0;
+  // Every value a row needs is loaded up front, none through another: the entry's counts,
+  // its whole ring row (the last N-1 committed ids, N-1 <= NMAX-1, picked by position in
+  // registers) and its new ids; after the barrier the commit only stores.
+  uint32_t ringv[NMAX > 1 ? NMAX - 1 : 1];
+  uint32_t newv[NGRAM_MAX_DECODE_TOKENS];
   if (active) {
     slot = a.slots != nullptr ? a.slots[b] : b;
     slot_ok = slot >= 0 && slot < a.nslots;
@@ -113,31 +118,48 @@ __global__ __launch_bounds__(kThreads) void hash_decode_kernel(const LayerDesc L
       if (a.flags != nullptr && jj == 0) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
       nn = nn < 0 ? 0 : a.tmax;
     }
+    if (a.n_commit != nullptr && jj == 0) acc = a.n_commit[b];
+#pragma unroll
+    for (int q = 0; q < (NMAX > 1 ? NMAX - 1 : 1); ++q)
+      ringv[q] = slot_ok && q < nm1 ? uint32_t(a.ring[int64_t(slot) * nm1 + q]) : 0u;
     if (slot_ok) {
       committed = a.len[slot];
       if (committed < 0) committed = 0;
     }
+    const int32_t* nt = a.newtok + int64_t(b) * a.tmax;
+    // the ids this thread reads: its row's context (<= j) and, for the commit, all of them
+#pragma unroll
+    for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)
+      newv[q] = q < a.tmax && (q <= j || jj == 0) ? uint32_t(nt[q]) : 0u;
     const int64_t r = int64_t(b) * a.width + jj;
     int32_t* out = a.idx + r * L.S;
-    const int32_t* nt = a.newtok + int64_t(b) * a.tmax;
     if (j >= nn || !slot_ok) {
       a.tok[r] = a.unused_tok;
       for (int s = 0; s < L.S; ++s) out[s] = 0;
     } else {
-      const int32_t t = nt[j];
-      if (a.flags != nullptr && uint32_t(t) >= uint32_t(L.V0))
-        atomicOr(a.flags, NGRAM_FLAG_BAD_TOKEN);
-      a.tok[r] = t;
+      uint32_t t = 0;
+#pragma unroll
+      for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)
+        if (q == j) t = newv[q];
+      if (a.flags != nullptr && t >= uint32_t(L.V0)) atomicOr(a.flags, NGRAM_FLAG_BAD_TOKEN);
+      a.tok[r] = int32_t(t);
       uint32_t c[NMAX];
 #pragma unroll
       for (int i = 0; i < NMAX; ++i) {
         uint32_t v = 0;
         if (i < L.N) {
           if (j - i >= 0) {
-            v = uint32_t(nt[j - i]);                 // a new id of this step
+#pragma unroll
+            for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)   // a new id of this step
+              if (q == j - i) v = newv[q];
           } else {
-            const int64_t q = committed + (j - i);   // committed position, from the cache
-            if (q >= 0) v = uint32_t(a.ring[int64_t(slot) * nm1 + q % nm1]);
+            const int64_t p = committed + (j - i);             // committed position
+            if (p >= 0) {
+              const int u = int(p % nm1);
+#pragma unroll
+              for (int q = 0; q < (NMAX > 1 ? NMAX - 1 : 1); ++q)
+                if (q == u) v = ringv[q];
+            }
           }
         }
         c[i] = v;
@@ -149,15 +171,15 @@ __global__ __launch_bounds__(kThreads) void hash_decode_kernel(const LayerDesc L
   __syncthreads();
   if (!active || jj != 0 || !slot_ok) return;
   // commit the first n_commit[b] (<= n_new[b]) new ids
-  int acc = a.n_commit[b];
   if (acc < 0 || acc > nn) {
     if (a.flags != nullptr) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
     acc = acc < 0 ? 0 : nn;
   }
   if (nm1 > 0) {
     int32_t* rb = a.ring + int64_t(slot) * nm1;
-    const int32_t* nt = a.newtok + int64_t(b) * a.tmax;
-    for (int q = (acc > nm1 ? acc - nm1 : 0); q < acc; ++q) rb[(committed + q) % nm1] = nt[q];
+#pragma unroll
+    for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)
+      if (q < acc && q >= acc - nm1) rb[(committed + q) % nm1] = int32_t(newv[q]);
   }
   a.len[slot] = committed + acc;
 }
