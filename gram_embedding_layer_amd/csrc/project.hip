@@ -146,7 +146,9 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   constexpr int PER_SLICE = QA + QB;
   // One LDS pool: NST slice stages + the tile's hash indices during the main loop; the
   // epilogue then reuses it to turn each wave's results into row-major order.
-  constexpr int EP_PITCH = WN * 4 + 32;  // bytes per staged fp32 row (conflict-free pitch)
+  // bytes per staged fp32 row: 16 bytes past a multiple of 256, so the 16 rows one write
+  // instruction's lane group covers fall in 16 different 16-byte bank groups
+  constexpr int EP_PITCH = WN * 4 + 16;
   constexpr int IDXB = IdxLds<BM>::bytes;
   constexpr int POOL = NST * STAGE + IDXB;
   static_assert(8 * 32 * EP_PITCH <= POOL - BM * 4,
@@ -195,18 +197,28 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
   __syncthreads();
 
   // -- loads: lane p fills LDS chunk (row p/CPR, chunk p%CPR) of an RPL-row group with
-  //    logical 16-byte chunk c = (p%CPR) ^ swz(row), so that fragment reads (8 lanes = 8
-  //    rows, one logical chunk) hit 8 different 16-byte bank groups; CPR lanes read one
-  //    row piece. swz(r) = r mod 8 for 128-byte pieces, (r/2) mod 4 for 64-byte ones (two
-  //    rows per 128 bytes of banks).
-  auto swz = [](int r) __attribute__((always_inline)) { return (r / (8 / CPR)) % CPR; };
+  //    logical 16-byte chunk c = (p%CPR) ^ swz(row), CPR lanes per row piece. LDS has 64
+  //    banks of 4 bytes: a 16-byte read serves 16 lanes per cycle, and a fragment read's 16
+  //    lanes are 16 consecutive rows, one logical chunk. With 128-byte rows two rows span
+  //    the 256 bytes of banks, so swz(r) = (r/2) mod 8 puts the 16 rows in 16 different
+  //    16-byte bank groups (r mod 8 left rows r and r+8 colliding: 1.9% slower). 64-byte
+  //    rows: (r/2) mod 4.
+  auto swz = [](int r) __attribute__((always_inline)) {
+    return CPR == 8 ? (r >> 1) & 7 : (r / (8 / CPR)) % CPR;
+  };
   const int prow = lane / CPR;
-  const int pchunk = (lane % CPR) ^ swz(prow);
+  // physical chunk of load q's row (A rows of this wave, then W rows)
+  auto pchunk_a = [&](int q) __attribute__((always_inline)) {
+    return (lane % CPR) ^ swz(w * (BM / 8) + q * RPL + prow);
+  };
+  auto pchunk_b = [&](int q) __attribute__((always_inline)) {
+    return (lane % CPR) ^ swz(w * 32 + q * RPL + prow);
+  };
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)lds));
   const int layer = blockIdx.z;
   const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E) + layer * a.S;
   const uint16_t* W = static_cast<const uint16_t*>(a.W[layer]);
-  const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.ldb + pchunk * 8;
+  const uint16_t* bp = W + int64_t(n0 + w * 32 + prow) * a.ldb;
   const uint16_t* ap[QA];
   const int KT_ALL = a.K / BK;   // slices of the whole contraction
   // this block's slice range (all of it unless the contraction is split)
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
       for (int q = 0; q < QA; ++q) {
         const int r = w * (BM / 8) + q * RPL + prow;
         const uint32_t id = min(uint32_t(sidx[r * a.S + s_cur]), a.Vm1[s_cur]);
-        ap[q] = E[s_cur] + int64_t(id) * a.d + pchunk * 8;
+        ap[q] = E[s_cur] + int64_t(id) * a.d + pchunk_a(q) * 8;
       }
     }
     f_sb = lds0 + uint32_t((kt - kt_lo) % NST) * STAGE;
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void proj_mfma_kernel(const ProjArgs a) {
     if (q < QA)
       dma16(ap[q] + f_koff, f_sb + w * (BM / 8) * RB + q * 1024);
     else
-      dma16(bp + int64_t((q - QA) * RPL) * a.ldb + f_kt * BK,
+      dma16(bp + int64_t((q - QA) * RPL) * a.ldb + pchunk_b(q - QA) * 8 + f_kt * BK,
             f_sb + A_BYTES + w * 32 * RB + (q - QA) * 1024);
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
