@@ -97,8 +97,15 @@ def cpu_baseline(w, E0, E, W, batches):
         t_embed += time.perf_counter() - t1
         n += len(tokens)
         del rows
-    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                        if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    blas_threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(n / (t_hash + t_embed), 1),
         "unit": "tokens/s",
@@ -109,6 +116,10 @@ def cpu_baseline(w, E0, E, W, batches):
                    f"{t_embed:.2f} s on {blas_threads} BLAS threads; host copy of the named "
                    f"table rows {t_copy:.2f} s not timed"),
         "host_cpus": len(os.sched_getaffinity(0)),
+        "host_cpu_model": cpu_model,
+        "blas": ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in blas})),
+        "seconds": {"hash_python_int": round(t_hash, 3), "contraction_float64": round(t_embed, 3),
+                    "row_copy_not_timed": round(t_copy, 3)},
     }
 
 
