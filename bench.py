@@ -233,7 +233,7 @@ def main():
     traffic = counter_traffic("project", "project.hip")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "proj_mfma_kernel<256, 0>",
+                "traffic": traffic, "kernel": "proj_mfma_kernel<256, 0, 256>",
                 "kernel_us": round(t_proj * 1e6, 1),
                 "algorithmic_hbm_GBps": round(alg_bytes_proj / t_proj / 1e9, 1)}
     log(f"step {ms_per_step:.3f} ms: hash {t_hash*1e6:.1f} us, project {t_proj*1e6:.1f} us "
