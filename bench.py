@@ -52,8 +52,9 @@ def counter_traffic(kernel, source):
         return None
     kv = {}
     for ln in open(TRAFFIC_FILE):
-        if ":" in ln and not ln.lstrip().startswith(("#", "|", "-")):
-            k, v = ln.split(":", 1)
+        # "key: value" lines; keys may hold a colon themselves ("project.hip sha256[:16]")
+        if ": " in ln and not ln.lstrip().startswith(("#", "|", "-")):
+            k, v = ln.rsplit(": ", 1)
             kv[k.strip()] = v.strip()
     if kv.get(f"{source} sha256[:16]") != source_digest(source):
         return None
