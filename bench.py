@@ -746,10 +746,22 @@ def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
              "us_verify_path_commit_only": round(t_commit * 1e6, 2)}
     log(f"draft-phase rows: {t_rows*1e6:.1f} us/step in {tmax} calls, verify path "
         f"{t_commit*1e6:.1f} us (one-shot decode {t/nsteps*1e6:.1f} us)")
+    # both rooflines of a step: algorithmic bytes (the rows' sub-table pieces, E_0 rows and
+    # outputs, ids, W once, the ring read and written) and the product's flops
+    rows = nseq * tmax
+    step_bytes = (rows * (wd.S * wd.d * 2 + wd.D * 2 + wd.D * 2 + wd.S * 4 + 8)
+                  + wd.D * wd.D * 2 + nseq * (2 * (wd.N - 1) * 4 + 16))
+    step_flops = 2.0 * rows * wd.D * wd.D
+    t_step = t / nsteps
+    fractions = {"bytes_per_step": step_bytes, "flops_per_step": step_flops,
+                 "hbm_GBps": round(step_bytes / t_step / 1e9, 1),
+                 "hbm_frac": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_TFLOPs": round(step_flops / t_step / 1e12, 1),
+                 "mfma_frac": round(step_flops / t_step / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     return {"workload": DECODE_WORKLOAD, "steps": nsteps, "seqs": nseq, "ids_per_step": tmax,
-            "tokens_per_s": round(toks / t, 1), "us_per_step_graph": round(t / nsteps * 1e6, 2),
+            "tokens_per_s": round(toks / t, 1), "us_per_step_graph": round(t_step * 1e6, 2),
             "us_per_step_eager": round(eager_us, 2), "replays": len(times),
-            "draft_phase": draft}
+            "roofline_fractions": fractions, "draft_phase": draft}
 
 
 if __name__ == "__main__":
