@@ -9,8 +9,9 @@
 // Layout on MI355X: lane i of the grid owns 16-byte chunk i % cpr of output row i / cpr, so
 // consecutive lanes cover consecutive chunks of one row and each of the N table rows is read
 // as one contiguous piece (a 3072-wide bf16 row is 6 KB: 384 lanes, 6 waves). Every lane
-// issues its N loads before it adds, keeps the sum in fp32 (E_0 first, then the tables in
-// order), scales once and rounds once. Table loads stay cached (Zipf-distributed ids repeat
+// requests the row's token and ids together, then its N table pieces, before it adds (two
+// memory round trips), keeps the sum in fp32 (E_0 first, then the tables in order), scales
+// once and rounds once. Table loads stay cached (Zipf-distributed ids repeat
 // within a batch); output stores are non-temporal, since nothing here reads them again.
 // Rows whose token is outside [0, V0) are written as zeros, rows marked kSkipRow not at all,
 // and the output row map places decode windows, as in the final form's epilogue.
@@ -55,28 +56,37 @@ template <> __device__ __forceinline__ void add_chunk<uint16_t>(float* acc, cons
   }
 }
 
-template <typename T, typename TO>
+// SB: a bound on S (the orders after the first), so the row's ids sit in registers.
+template <typename T, typename TO, int SB>
 __global__ __launch_bounds__(kThreads) void basic_sum_kernel(const SumArgs a) {
   constexpr int kVec = 16 / sizeof(T);                  // elements per chunk
   const int64_t item = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (item >= a.nrows * a.cpr) return;
   const int64_t r = item / a.cpr;
   const int32_t c = int32_t(item - r * a.cpr);
+  // the token and the ids first, all at once (the ids do not depend on the token), then
+  // every table piece: two round trips to memory instead of three
   const int32_t tk = a.tok[r];
+  const int32_t* id = a.idx + r * a.S;
+  uint32_t ids[SB];
+#pragma unroll
+  for (int s = 0; s < SB; ++s) ids[s] = s < a.S ? uint32_t(id[s]) : 0u;
   if (tk == kSkipRow) return;
   float acc[kVec];
 #pragma unroll
   for (int i = 0; i < kVec; ++i) acc[i] = 0.f;
   if (uint32_t(tk) < uint32_t(a.V0)) {
-    const int32_t* id = a.idx + r * a.S;
     const int64_t off = int64_t(c) * 16;
-    add_chunk<T>(acc, *reinterpret_cast<const u32x4_t*>(a.E0 + int64_t(tk) * a.row_bytes + off));
-#pragma unroll 4
-    for (int s = 0; s < a.S; ++s) {
-      uint32_t x = uint32_t(id[s]);
-      x = x > a.Vm1[s] ? a.Vm1[s] : x;
-      add_chunk<T>(acc, *reinterpret_cast<const u32x4_t*>(a.E[s] + int64_t(x) * a.row_bytes + off));
+    u32x4_t piece[SB];
+#pragma unroll
+    for (int s = 0; s < SB; ++s) {
+      const uint32_t x = ids[s] > a.Vm1[s] ? a.Vm1[s] : ids[s];
+      if (s < a.S) piece[s] = *reinterpret_cast<const u32x4_t*>(a.E[s] + int64_t(x) * a.row_bytes + off);
     }
+    add_chunk<T>(acc, *reinterpret_cast<const u32x4_t*>(a.E0 + int64_t(tk) * a.row_bytes + off));
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+      if (s < a.S) add_chunk<T>(acc, piece[s]);
 #pragma unroll
     for (int i = 0; i < kVec; ++i) acc[i] *= a.inv;
   }
@@ -97,6 +107,23 @@ __global__ __launch_bounds__(kThreads) void basic_sum_kernel(const SumArgs a) {
           f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]},
           reinterpret_cast<f32x4_t*>(o) + q);
   }
+}
+
+// The basic form has K = 1: S = N - 1 <= NGRAM_MAX_ORDER - 1 orders after the first.
+constexpr int kMaxBasicS = NGRAM_MAX_ORDER;
+
+template <int SB>
+hipError_t launch_sum(const LayerDesc& L, const SumArgs& a, dim3 grid, bool f32out,
+                      hipStream_t st) {
+  if (L.S > SB) return hipErrorInvalidValue;
+  if (L.dtype == NGRAM_F32)
+    hipLaunchKernelGGL((basic_sum_kernel<float, float, SB>), grid, dim3(kThreads), 0, st, a);
+  else if (f32out)
+    hipLaunchKernelGGL((basic_sum_kernel<uint16_t, float, SB>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((basic_sum_kernel<uint16_t, uint16_t, SB>), grid, dim3(kThreads), 0, st,
+                       a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -127,13 +154,8 @@ hipError_t launch_basic(const LayerDesc& L, const void* E0, const void* const* E
   const int64_t blocks = (nrows * a.cpr + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid{unsigned(blocks)};
-  if (L.dtype == NGRAM_F32)
-    hipLaunchKernelGGL((basic_sum_kernel<float, float>), grid, dim3(kThreads), 0, st, a);
-  else if (f32out)
-    hipLaunchKernelGGL((basic_sum_kernel<uint16_t, float>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((basic_sum_kernel<uint16_t, uint16_t>), grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  if (L.S <= 4) return launch_sum<4>(L, a, grid, f32out, st);
+  return launch_sum<kMaxBasicS>(L, a, grid, f32out, st);
 }
 
 }  // namespace ngram
