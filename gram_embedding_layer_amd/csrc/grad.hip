@@ -73,24 +73,35 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict_
 
 // 16-bit elements, 16-byte vectors: the same transposes with each thread moving 8 elements
 // per access (64 x 64 tiles; the LDS pitch of 72 elements keeps the column reads spread
-// over the banks). `src_row(r)` points at the tile's first column in source row r (null =
-// a zero row).
+// over the banks). `src_row(r)` gives the tile's first column in source row r (null past
+// the last row) and whether the row is kept (else it reads as zeros). A thread asks for both
+// of its rows' index data first, then loads both rows, then drops the rows not kept: one or
+// two memory round trips instead of up to three per row.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPitch = kTile + 8;
+
+struct SrcRow {
+  const uint16_t* p;   // the tile's first column in the source row; null past the last row
+  bool keep;           // false: the row reads as zeros
+};
 
 template <typename RowFn>
 __device__ __forceinline__ void transpose_tile16(uint16_t (*tile)[kPitch], RowFn src_row,
                                                  int c0, uint16_t* XT, int64_t ldt, int cols,
                                                  int64_t r0) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, q = t % 8;
+  SrcRow sr[2];                                  // 512 vectors of 8 elements per tile
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {                  // 512 vectors of 8 elements per tile
-    const int r = t / 8 + 32 * k, q = t % 8;
-    const uint16_t* row = src_row(r);
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row != nullptr) v = *reinterpret_cast<const u32x4_t*>(row + q * 8);
-    *reinterpret_cast<u32x4_t*>(&tile[r][q * 8]) = v;
-  }
+  for (int k = 0; k < 2; ++k) sr[k] = src_row(t / 8 + 32 * k);
+  u32x4_t v[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    v[k] = sr[k].p != nullptr ? *reinterpret_cast<const u32x4_t*>(sr[k].p + q * 8)
+                              : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    *reinterpret_cast<u32x4_t*>(&tile[t / 8 + 32 * k][q * 8]) =
+        sr[k].keep ? v[k] : u32x4_t{0u, 0u, 0u, 0u};
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -115,10 +126,11 @@ __global__ __launch_bounds__(256) void transpose_pad16_kernel(const uint16_t* __
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][kPitch];
   const int64_t r0 = int64_t(blockIdx.x) * kTile;
   const int c0 = blockIdx.y * kTile;
-  auto src_row = [&](int r) -> const uint16_t* {
+  auto src_row = [&](int r) -> SrcRow {
     const int64_t rr = r0 + r;
-    if (rr >= rows || (tok != nullptr && uint32_t(tok[rr]) >= uint32_t(V0))) return nullptr;
-    return X + rr * cols + c0;
+    if (rr >= rows) return SrcRow{nullptr, false};
+    // the row's address does not depend on its token: both loads fly together
+    return SrcRow{X + rr * cols + c0, tok == nullptr || uint32_t(tok[rr]) < uint32_t(V0)};
   };
   transpose_tile16(tile, src_row, c0, XT, ldt, cols, r0);
 }
@@ -168,11 +180,14 @@ __global__ __launch_bounds__(256) void gather_transpose16_kernel(const GatherTAr
   const int c0 = blockIdx.y * kTile;
   const int s = c0 / a.d;
   const uint16_t* E = static_cast<const uint16_t*>(a.E[s]);
-  auto src_row = [&](int r) -> const uint16_t* {
+  auto src_row = [&](int r) -> SrcRow {
     const int64_t rr = r0 + r;
-    if (rr >= a.rows || uint32_t(a.tok[rr]) >= uint32_t(a.V0)) return nullptr;
+    if (rr >= a.rows) return SrcRow{nullptr, false};
+    // token and index together (the index is clamped into the table, so the row load is in
+    // bounds whatever the token)
+    const int32_t tk = a.tok[rr];
     const uint32_t id = min(uint32_t(a.idx[rr * a.S + s]), a.Vm1[s]);
-    return E + int64_t(id) * a.d + (c0 - s * a.d);
+    return SrcRow{E + int64_t(id) * a.d + (c0 - s * a.d), uint32_t(tk) < uint32_t(a.V0)};
   };
   transpose_tile16(tile, src_row, c0, static_cast<uint16_t*>(a.GT), a.ldt, a.D, r0);
 }
