@@ -55,9 +55,12 @@ def decode_step(cfg, tables, cache, new, n_new, n_commit, ws, dtype):
     return out
 
 
-@pytest.mark.parametrize("N,K,D,dtype", [(4, 2, 1536, "bf16"), (3, 2, 64, "f32"),
-                                         (2, 1, 256, "bf16"), (6, 1, 320, "bf16")])
-def test_decode_matches_oracle(lib, N, K, D, dtype):
+# (5, 16, 512) with 8-id windows: 8 x 64 (row, sub-table) hashes per entry, exactly one entry
+# per block of the decode hash; N = 1: no sub-tables, the rows are E_0 rows
+@pytest.mark.parametrize("N,K,D,dtype,tmax", [(4, 2, 1536, "bf16", 5), (3, 2, 64, "f32", 5),
+                                              (2, 1, 256, "bf16", 5), (6, 1, 320, "bf16", 5),
+                                              (5, 16, 512, "bf16", 8), (1, 1, 256, "bf16", 8)])
+def test_decode_matches_oracle(lib, N, K, D, dtype, tmax):
     w = decode_workload(N=N, K=K, D=D, dtype=dtype)
     cfg = cfg_of(w)
     E0, E, W = WL.host_tables(w) if dtype == "f32" else WL.device_tables(w)
@@ -66,7 +69,7 @@ def test_decode_matches_oracle(lib, N, K, D, dtype):
     tdt = E0.dtype
     rng = np.random.default_rng([N, K, D])
     hist = [list(rng.integers(0, w.V0, size=L)) for L in (0, 1, 2, 3, 10, 100, N - 1, 5)]
-    nseq, tmax = len(hist), 5
+    nseq = len(hist)
     cache = init_cache(cfg, hist)
     check_cache(cfg, cache, hist)
     orc = oracle.DecodeOracle(w.V0, w.D, w.N, w.K, w.V, hist)
