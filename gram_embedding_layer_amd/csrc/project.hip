@@ -620,6 +620,14 @@ hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStre
                       ((nrows + 127) / 128) * (a.N / 128) * sp >= 192;
     if (n128 && om == kOutF32) return run_mfma<128, kOutF32, 128>(a, nrows, osz, st);
     if (n128 && om == kOutBf16) return run_mfma<128, kOutBf16, 128>(a, nrows, osz, st);
+    // fewer rows still (a draft-phase call: one row per sequence): 64 x 128 tiles when 64 x 256
+    // tiles would leave the chip short of blocks. Each block's 48 slices then move 24 KB
+    // instead of 40 KB and twice as many CUs work: 256 rows of the 30B layer, 33.4 vs 43.4 us
+    // per call (64 x 64 tiles with 4 waves: 32.5 us, not worth another wave grid).
+    const bool s128 = !big && !mid && bm == 64 && a.N % 128 == 0 &&
+                      ((nrows + 63) / 64) * (a.N / 256) * sp < 192;
+    if (s128 && om == kOutF32) return run_mfma<64, kOutF32, 128>(a, nrows, osz, st);
+    if (s128 && om == kOutBf16) return run_mfma<64, kOutBf16, 128>(a, nrows, osz, st);
     if (om == kOutPartial) {
       if (bm == 256) return run_mfma<256, kOutPartial>(a, nrows, osz, st);
       if (bm == 128) return run_mfma<128, kOutPartial>(a, nrows, osz, st);
