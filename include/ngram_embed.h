@@ -315,8 +315,9 @@ int ngram_embed_backward(const ngram_embed_config* cfg, const ngram_embed_tables
  * 1 <= vocab[v] < 2^31; 1 <= n <= NGRAM_MAX_ORDER; 1 <= V0 < 2^31. rows: device int64
  * [nvocab]; distinct: device int64 [1]; both overwritten. ws: at least
  * ngram_hash_stats_workspace_size(...) bytes (0 on bad arguments), 256-byte aligned, error
- * flags at offset 0 (NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS; counts then unspecified).
- * Intermediate buffers are filled by kernels, so the workspace needs no clearing. */
+ * flags at offset 0 as in the forward workspace: zero-filled once before first use, sticky
+ * until cleared (NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS; counts then unspecified). The
+ * rest of the workspace is written by the call before it is read, so it needs no clearing. */
 size_t ngram_hash_stats_workspace_size(int64_t V0, int32_t n, int64_t ntok,
                                        const int64_t* vocab, int32_t nvocab);
 int ngram_hash_stats(int64_t V0, int32_t n, const int32_t* tokens, const int32_t* cu_seqlens,
