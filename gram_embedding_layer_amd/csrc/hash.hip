@@ -7,25 +7,12 @@
 // evaluated by Horner's rule from the oldest id to the newest, reducing modulo V_{n,k} after
 // every step: x <- (x*V0 + t) mod V. With x < V < 2^31 and t < 2^32 every intermediate is
 // below 2^63, and the step's residue is taken exactly by Barrett reduction (below).
-#include "kernels.h"
+#include "decode_step.h"
 
 namespace ngram {
 namespace {
 
 constexpr int kThreads = 256;
-
-// One Horner step, exactly: (x*V0 + t) mod V for x < V < 2^31, V0 < 2^31, t < 2^32, so
-// y = x*V0 + t < 2^63. With m = floor((2^64 - 1) / V), q = floor(y*m / 2^64) satisfies
-// floor(y/V) - 1 <= q <= floor(y/V) (y*m/2^64 > y/V - y/2^64 - y/(V 2^64) > y/V - 1), so
-// r = y - q*V lies in [0, 2V) and one conditional subtraction leaves y mod V.
-__device__ __forceinline__ uint64_t horner_step(uint64_t x, uint64_t V0, uint32_t t, uint64_t V,
-                                                uint64_t m) {
-  const uint64_t y = x * V0 + t;
-  const uint64_t q = __umul64hi(y, m);
-  uint64_t r = y - q * V;
-  if (r >= V) r -= V;
-  return r;
-}
 
 // Hash one position. c[j] = t_{i-j} (pad 0 before the sequence start), j < NMAX.
 template <int NMAX>
@@ -109,97 +96,35 @@ __global__ __launch_bounds__(kDecThreads) void hash_decode_kernel(const LayerDes
   const int j = a.row_begin + jj;
   const bool active = int(threadIdx.x) < epb * tpe && b < a.nbatch;
   const bool lead = within == 0;                   // the entry's flags and commit
-  const int nm1 = L.N - 1;
-  int nn = 0, slot = 0, acc = 0;
-  bool slot_ok = false;
-  int64_t committed = 0;
-  // Every value a row needs is loaded up front, none through another: the entry's counts,
-  // its whole ring row (the last N-1 committed ids, N-1 <= NMAX-1, picked by position in
-  // registers) and its new ids; after the barrier the commit only stores.
-  uint32_t ringv[NMAX > 1 ? NMAX - 1 : 1];
-  uint32_t newv[NGRAM_MAX_DECODE_TOKENS];
+  DecodeEntry<NMAX> e{};
+  int acc = 0;
   if (active) {
-    slot = a.slots != nullptr ? a.slots[b] : b;
-    slot_ok = slot >= 0 && slot < a.nslots;
-    if (!slot_ok && a.flags != nullptr && lead) atomicOr(a.flags, NGRAM_FLAG_BAD_SLOT);
-    nn = a.n_new[b];
-    if (nn < 0 || nn > a.tmax) {
-      if (a.flags != nullptr && lead) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
-      nn = nn < 0 ? 0 : a.tmax;
-    }
+    // the row's context (ids up to j) and, for the entry's commit, every new id
+    e = load_entry<NMAX>(L, a, b, lead ? NGRAM_MAX_DECODE_TOKENS - 1 : j);
     if (a.n_commit != nullptr && lead) acc = a.n_commit[b];
-#pragma unroll
-    for (int q = 0; q < (NMAX > 1 ? NMAX - 1 : 1); ++q)
-      ringv[q] = slot_ok && q < nm1 ? uint32_t(a.ring[int64_t(slot) * nm1 + q]) : 0u;
-    if (slot_ok) {
-      committed = a.len[slot];
-      if (committed < 0) committed = 0;
+    if (lead && a.flags != nullptr) {
+      if (!e.slot_ok) atomicOr(a.flags, NGRAM_FLAG_BAD_SLOT);
+      if (e.bad_count) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
     }
-    const int32_t* nt = a.newtok + int64_t(b) * a.tmax;
-    // the ids this thread reads: its row's context (<= j) and, for the commit, all of them
-#pragma unroll
-    for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)
-      newv[q] = q < a.tmax && (q <= j || lead) ? uint32_t(nt[q]) : 0u;
     const int64_t r = int64_t(b) * a.width + jj;
-    if (j >= nn || !slot_ok) {
+    uint32_t id;
+    if (!entry_row(e, j, &id)) {
       if (s == 0) a.tok[r] = a.unused_tok;
       if (s < L.S) a.idx[r * L.S + s] = 0;
     } else {
-      uint32_t t = 0;
-#pragma unroll
-      for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)
-        if (q == j) t = newv[q];
       if (s == 0) {
-        if (a.flags != nullptr && t >= uint32_t(L.V0)) atomicOr(a.flags, NGRAM_FLAG_BAD_TOKEN);
-        a.tok[r] = int32_t(t);
+        if (a.flags != nullptr && id >= uint32_t(L.V0)) atomicOr(a.flags, NGRAM_FLAG_BAD_TOKEN);
+        a.tok[r] = int32_t(id);
       }
-      if (s < L.S) {
-        const int n = 2 + s / L.K;                 // order of sub-table s = (n-2)K + (k-1)
-        uint32_t c[NMAX];                          // c[i] = t_{j-i}, pad 0 before the start
-#pragma unroll
-        for (int i = 0; i < NMAX; ++i) {
-          uint32_t v = 0;
-          if (i < n) {
-            if (j - i >= 0) {
-#pragma unroll
-              for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)   // a new id of this step
-                if (q == j - i) v = newv[q];
-            } else {
-              const int64_t p = committed + (j - i);             // committed position
-              if (p >= 0) {
-                const int u = int(p % nm1);
-#pragma unroll
-                for (int q = 0; q < (NMAX > 1 ? NMAX - 1 : 1); ++q)
-                  if (q == u) v = ringv[q];
-              }
-            }
-          }
-          c[i] = v;
-        }
-        const uint64_t V = L.V[s], m = L.Vinv[s];
-        uint64_t x = 0;
-#pragma unroll
-        for (int i = NMAX - 1; i >= 0; --i)          // oldest id first
-          if (i < n) x = horner_step(x, uint64_t(L.V0), c[i], V, m);
-        a.idx[r * L.S + s] = int32_t(x);
-      }
+      if (s < L.S) a.idx[r * L.S + s] = entry_index<NMAX>(L, e, j, s);
     }
   }
   if (a.n_commit == nullptr) return;
   __syncthreads();
-  if (!active || !lead || !slot_ok) return;
+  if (!active || !lead || !e.slot_ok) return;
   // commit the first n_commit[b] (<= n_new[b]) new ids
-  if (acc < 0 || acc > nn) {
-    if (a.flags != nullptr) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
-    acc = acc < 0 ? 0 : nn;
-  }
-  if (nm1 > 0) {
-    int32_t* rb = a.ring + int64_t(slot) * nm1;
-#pragma unroll
-    for (int q = 0; q < NGRAM_MAX_DECODE_TOKENS; ++q)
-      if (q < acc && q >= acc - nm1) rb[(committed + q) % nm1] = int32_t(newv[q]);
-  }
-  a.len[slot] = committed + acc;
+  if (commit_entry<NMAX>(L, a, e, acc) && a.flags != nullptr)
+    atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
 }
 
 // Batch entry b (sequence b of the packed tokens) fills cache slot slots[b] (or b).

@@ -594,57 +594,69 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int osz, hipStream_t st) {
   return hipSuccess;
 }
 
-// Runs the product `a` describes (E/idx/S/d, K, N, ldb, ldo, E0/tok, inv) over nrows rows.
-// om: kOutBf16 (config dtype), kOutF32, or kOutPartial (a.splits ranges, matrix cores only).
-hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStream_t st) {
-  const int osz = om == kOutBf16 ? (dtype == NGRAM_F32 ? 4 : 2) : 4;
-  if (dtype == NGRAM_BF16 && a.N % kBN == 0 && a.d % kBK == 0 && a.K % kBK == 0) {
-    // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
-    // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
-    // rows' hash indices (and E_0 tokens) in LDS.
-    const int64_t tiles_n = a.N / kBN;
-    const int64_t sp = om == kOutPartial ? a.splits : 1;
-    const int per_row = a.S + (om != kOutPartial ? 1 : 0);   // int32 per row
-    const bool f256 = 256 * per_row * 4 <= IdxLds<256>::bytes;
-    const bool f128 = 128 * per_row * 4 <= IdxLds<128>::bytes;
-    const bool f64 = 64 * per_row * 4 <= IdxLds<64>::bytes;
-    const bool big = ((nrows + 255) / 256) * tiles_n * sp >= 512;
-    const bool mid = ((nrows + 127) / 128) * tiles_n * sp >= 256;
-    const int bm = big && f256 ? 256 : (big || mid) && f128 ? 128 : f64 ? 64 : f128 ? 128
-                 : f256 ? 256 : 0;
+// Tile shape of the matrix-core kernel for the product `a` over nrows rows with output mode
+// om, or bm = 0: the generic path (or, for partial sums, no path).
+struct Route {
+  int bm, bn;
+};
+Route mfma_route(const ProjArgs& a, int32_t dtype, int om, int64_t nrows) {
+  if (!(dtype == NGRAM_BF16 && a.N % kBN == 0 && a.d % kBK == 0 && a.K % kBK == 0))
+    return {0, 0};
+  // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
+  // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
+  // rows' hash indices (and E_0 tokens) in LDS.
+  const int64_t tiles_n = a.N / kBN;
+  const int64_t sp = om == kOutPartial ? a.splits : 1;
+  const int per_row = a.S + (om != kOutPartial ? 1 : 0);   // int32 per row
+  const bool f256 = 256 * per_row * 4 <= IdxLds<256>::bytes;
+  const bool f128 = 128 * per_row * 4 <= IdxLds<128>::bytes;
+  const bool f64 = 64 * per_row * 4 <= IdxLds<64>::bytes;
+  const bool big = ((nrows + 255) / 256) * tiles_n * sp >= 512;
+  const bool mid = ((nrows + 127) / 128) * tiles_n * sp >= 256;
+  const int bm = big && f256 ? 256 : (big || mid) && f128 ? 128 : f64 ? 64 : f128 ? 128
+               : f256 ? 256 : 0;
+  if (om != kOutPartial) {
     // a batch too small for 128 x 256 tiles to fill the chip (a decode step) takes 128 x 128
     // tiles when those are enough blocks, rather than 64 x 256: the same blocks move less
     // through L2 (each W panel is read by half as many row tiles, each gathered row by
     // twice as many output tiles). 1280 rows of the 30B layer: 46.1 vs 48.7 us per step.
-    const bool n128 = !big && !mid && f128 && a.N % 128 == 0 &&
-                      ((nrows + 127) / 128) * (a.N / 128) * sp >= 192;
-    if (n128 && om == kOutF32) return run_mfma<128, kOutF32, 128>(a, nrows, osz, st);
-    if (n128 && om == kOutBf16) return run_mfma<128, kOutBf16, 128>(a, nrows, osz, st);
-    // fewer rows still (a draft-phase call: one row per sequence): 64 x 128 tiles when 64 x 256
-    // tiles would leave the chip short of blocks. Each block's 48 slices then move 24 KB
-    // instead of 40 KB and twice as many CUs work: 256 rows of the 30B layer, 33.4 vs 43.4 us
-    // per call (64 x 64 tiles with 4 waves: 32.5 us, not worth another wave grid).
-    const bool s128 = !big && !mid && bm == 64 && a.N % 128 == 0 &&
-                      ((nrows + 63) / 64) * (a.N / 256) * sp < 192;
-    if (s128 && om == kOutF32) return run_mfma<64, kOutF32, 128>(a, nrows, osz, st);
-    if (s128 && om == kOutBf16) return run_mfma<64, kOutBf16, 128>(a, nrows, osz, st);
-    if (om == kOutPartial) {
-      if (bm == 256) return run_mfma<256, kOutPartial>(a, nrows, osz, st);
-      if (bm == 128) return run_mfma<128, kOutPartial>(a, nrows, osz, st);
-      if (bm == 64) return run_mfma<64, kOutPartial>(a, nrows, osz, st);
-      return hipErrorInvalidValue;
-    }
-    if (om == kOutF32) {
-      if (bm == 256) return run_mfma<256, kOutF32>(a, nrows, osz, st);
-      if (bm == 128) return run_mfma<128, kOutF32>(a, nrows, osz, st);
-      if (bm == 64) return run_mfma<64, kOutF32>(a, nrows, osz, st);
-    } else {
-      if (bm == 256) return run_mfma<256, kOutBf16>(a, nrows, osz, st);
-      if (bm == 128) return run_mfma<128, kOutBf16>(a, nrows, osz, st);
-      if (bm == 64) return run_mfma<64, kOutBf16>(a, nrows, osz, st);
-    }
-    // no tile keeps this many indices: the generic path below
+    if (!big && !mid && f128 && a.N % 128 == 0 &&
+        ((nrows + 127) / 128) * (a.N / 128) * sp >= 192)
+      return {128, 128};
+    // fewer rows still (a draft-phase call: one row per sequence): 64 x 128 tiles when
+    // 64 x 256 tiles would leave the chip short of blocks. Each block's 48 slices then move
+    // 24 KB instead of 40 KB and twice as many CUs work: 256 rows of the 30B layer, 33.4 vs
+    // 43.4 us per call (64 x 64 tiles with 4 waves: 32.5 us, not worth another wave grid).
+    if (!big && !mid && bm == 64 && a.N % 128 == 0 &&
+        ((nrows + 63) / 64) * (a.N / 256) * sp < 192)
+      return {64, 128};
   }
+  return {bm, kBN};
+}
+
+template <int OM>
+hipError_t dispatch(Route r, const ProjArgs& a, int64_t nrows, int osz, hipStream_t st) {
+  if (r.bm == 256) return run_mfma<256, OM>(a, nrows, osz, st);
+  if (r.bm == 128 && r.bn == kBN) return run_mfma<128, OM>(a, nrows, osz, st);
+  if (r.bm == 64 && r.bn == kBN) return run_mfma<64, OM>(a, nrows, osz, st);
+  if constexpr (OM != kOutPartial) {
+    if (r.bm == 128 && r.bn == 128) return run_mfma<128, OM, 128>(a, nrows, osz, st);
+    if (r.bm == 64 && r.bn == 128) return run_mfma<64, OM, 128>(a, nrows, osz, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Runs the product `a` describes (E/idx/S/d, K, N, ldb, ldo, E0/tok, inv) over nrows rows.
+// om: kOutBf16 (config dtype), kOutF32, or kOutPartial (a.splits ranges, matrix cores only).
+hipError_t run_product(ProjArgs a, int32_t dtype, int om, int64_t nrows, hipStream_t st) {
+  const int osz = om == kOutBf16 ? (dtype == NGRAM_F32 ? 4 : 2) : 4;
+  const Route r = mfma_route(a, dtype, om, nrows);
+  if (r.bm != 0) {
+    if (om == kOutPartial) return dispatch<kOutPartial>(r, a, nrows, osz, st);
+    if (om == kOutF32) return dispatch<kOutF32>(r, a, nrows, osz, st);
+    return dispatch<kOutBf16>(r, a, nrows, osz, st);
+  }
+  // no tile keeps this many indices, or not a matrix-core shape: the generic path below
   if (om == kOutPartial) return hipErrorInvalidValue;   // callers use kOutF32 here
   const unsigned gy = unsigned((a.N + 63) / 64);
   const int32_t* idx = a.idx;
