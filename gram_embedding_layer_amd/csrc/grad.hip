@@ -193,7 +193,9 @@ __global__ __launch_bounds__(256) void gather_transpose16_kernel(const GatherTAr
 }
 
 // Sort inputs. E_0: key = token, value = position. Sub-tables: pair p = i*S + s has key
-// (s << 31) | idx[i, s] and value i. Invalid positions get the key `sentinel` (sorted last).
+// (s << row_bits) | idx[i, s] and value i (row_bits: enough for the largest table's rows, so
+// the keys take as few sort passes as they can). Invalid positions get the key `sentinel`
+// (sorted last).
 __global__ __launch_bounds__(256) void keys_tokens_kernel(const int32_t* __restrict__ tok,
                                                           int64_t n, int32_t V0,
                                                           uint64_t sentinel,
@@ -209,12 +211,13 @@ __global__ __launch_bounds__(256) void keys_tokens_kernel(const int32_t* __restr
 // (the indices come from the hash kernel, so they lie in [0, V_s))
 __global__ __launch_bounds__(256) void keys_subtables_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ tok, int64_t rows, int32_t S,
-    int32_t V0, uint64_t sentinel, uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+    int32_t V0, int32_t row_bits, uint64_t sentinel, uint64_t* __restrict__ keys,
+    uint32_t* __restrict__ vals) {
   const int64_t p = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (p >= rows * S) return;
   const int64_t i = p / S;
   const int s = int(p - i * S);
-  keys[p] = uint32_t(tok[i]) < uint32_t(V0) ? (uint64_t(s) << 31) | uint32_t(idx[p])
+  keys[p] = uint32_t(tok[i]) < uint32_t(V0) ? (uint64_t(s) << row_bits) | uint32_t(idx[p])
                                             : sentinel;
   vals[p] = uint32_t(i);
 }
@@ -358,13 +361,15 @@ struct SegArgs {
   uint64_t sentinel;
   int32_t width;                     // gradient row width (D for E_0, d for sub-tables)
   int32_t chunk;                     // sorted entries per chunk
-  int32_t by_table;                  // 1: key = (s << 31) | r, source columns s*col_step...
+  int32_t by_table;                  // 1: key = (s << row_bits) | r, source columns s*col_step...
+  int32_t row_bits;
   int32_t col_step;                  // source columns per key class (0: all read column 0)
   float factor;                      // applied to source rows (c for dout, 1 for dG)
 };
 
 __device__ __forceinline__ float* dst_row(const SegArgs& a, uint64_t key) {
-  if (a.by_table) return a.dst[key >> 31] + int64_t(key & 0x7fffffffu) * a.width;
+  if (a.by_table)
+    return a.dst[key >> a.row_bits] + int64_t(key & ((uint64_t(1) << a.row_bits) - 1)) * a.width;
   return a.dst[0] + int64_t(key) * a.width;
 }
 
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(THREADS) void segsum_level1_kernel(const SegArgs a)
       const int j = b0 + u;
       const bool live = j < cnt && skey[j + 1] != a.sentinel;
       const uint64_t key = live ? skey[j + 1] : 0;
-      const int s = a.by_table ? int(key >> 31) : 0;
+      const int s = a.by_table ? int(key >> a.row_bits) : 0;
       const T* row = static_cast<const T*>(a.src) + int64_t(live ? sval[j] : 0) * a.ld_src +
                      s * a.col_step;
       const bool last = j + 1 == cnt;
@@ -676,9 +681,13 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
   if (need_dg) {
     // dE_s: sort (s, row) keys of all T*S pairs, sum the dG blocks of each run
     const int64_t n = T * L.S;
-    const uint64_t sentinel = uint64_t(1) << (31 + ceil_log2(L.S));
+    // key = (s << row_bits) | row: 24 + 4 bits for the 30B layer, 4 sort passes (not 5)
+    uint32_t vmax = 1;
+    for (int s = 0; s < L.S; ++s) vmax = std::max(vmax, L.V[s]);
+    const int32_t row_bits = std::max<int32_t>(1, ceil_log2(int64_t(vmax)));
+    const uint64_t sentinel = uint64_t(1) << (row_bits + ceil_log2(L.S));
     hipLaunchKernelGGL(keys_subtables_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st,
-                       b.idx, b.tokens, T, L.S, L.V0, sentinel, b.keys0, b.vals0);
+                       b.idx, b.tokens, T, L.S, L.V0, row_bits, sentinel, b.keys0, b.vals0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = radix_sort(b.keys0, b.vals0, b.keys1, b.vals1, b.hist, n, key_bits(sentinel), st);
     if (e != hipSuccess) return e;
@@ -695,6 +704,7 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     a.sentinel = sentinel;
     a.width = L.d;
     a.by_table = 1;
+    a.row_bits = row_bits;
     a.col_step = basic ? 0 : L.d;
     a.factor = basic ? c : 1.0f;
     if ((e = segsum(a, basic ? f32 : true, st)) != hipSuccess) return e;
