@@ -90,11 +90,16 @@ template <int BM> struct IdxLds {
 
 // Contraction depth of one slice (BK = 64: a full 128-byte L2 line of each row per load)
 // and LDS slice buffers (NST; 160 KB of LDS per CU): 256-row tiles double-buffer, shorter
-// tiles keep two slices in flight. Measured on the 64K-token batch and not adopted: 32-deep
-// slices with four buffers (twice the barriers, half-line loads): 1365 vs 1251 us.
-template <int BM> struct Tile {
+// tiles keep two slices in flight, 64 x 128 tiles (the smallest batches) three: 256 rows of
+// the 30B layer, 29.8 vs 33.1 us per call (four in flight: 31.3 us; 128 x 128 decode tiles
+// gain nothing from a third: 43.4 vs 43.2 us per step). Measured on the 64K-token batch and
+// not adopted: 32-deep slices with four buffers (twice the barriers, half-line loads): 1365
+// vs 1251 us; for small batches, 128-deep slices (two buffers): slower by 12-14%.
+template <int BM, int BN> struct Tile {
   static constexpr int BK = 64;
-  static constexpr int NST = BM >= 256 ? 2 : 3;
+  static constexpr int NST = BM >= 256 ? 2 : (BM == 64 && BN == 128) ? 4 : 3;
+  static_assert(NST * (BM + BN) * BK * 2 + IdxLds<BM>::bytes <= 163840,
+                "the slice buffers and the tile's indices must fit the LDS");
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -130,8 +135,8 @@ template <int BM> struct WaveGrid {
 
 template <int BM, int OM, int BN>
 __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(const ProjArgs a) {
-  constexpr int NST = Tile<BM>::NST;
-  constexpr int BK = Tile<BM>::BK;
+  constexpr int NST = Tile<BM, BN>::NST;
+  constexpr int BK = Tile<BM, BN>::BK;
   constexpr int RB = BK * 2;             // bytes of one row per slice
   constexpr int CPR = RB / 16;           // 16-byte chunks per row per slice
   constexpr int RPL = 1024 / RB;         // rows per wave load (64 lanes x 16 bytes)
