@@ -81,6 +81,10 @@ CASES = [
      (16384, 16384, 999)),
     ("f32_n1", small_workload("f32", D=64, N=1, K=1), (40, 9)),
     ("bf16_n1", small_workload("bf16", D=256, N=1, K=1), (40, 9)),
+    # rows wider than the normalisation pass keeps its parameters in registers for (bf16 past
+    # D = 3072, fp32 past D = 1024): the parameters are loaded where they are used
+    ("bf16_wide_d4096", small_workload("bf16", D=4096, N=3, K=2), (300, 7)),
+    ("f32_wide_d2048", small_workload("f32", D=2048, N=2, K=1), (90, 3)),
 ]
 MODES = [("scale", None, False), ("scale", -0.75, False), ("layernorm", None, False),
          ("layernorm", None, True)]
