@@ -58,6 +58,9 @@ CASES = [
     ("bf16_n5_d512", basic_workload("bf16", D=512, N=5, V0=5000), (600, 3)),
     ("f32_n2", basic_workload("f32", D=64, N=2), (50, 9)),
     ("bf16_n1", basic_workload("bf16", D=128, N=1), (40, 9)),
+    # more than 4 orders after the first (the kernel's id registers sized for up to 16)
+    ("bf16_n9", basic_workload("bf16", D=256, N=9), (200, 5)),
+    ("bf16_n16_max", basic_workload("bf16", D=128, N=16), (100, 2)),
 ]
 
 
