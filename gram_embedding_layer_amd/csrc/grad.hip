@@ -527,9 +527,10 @@ int key_bits(uint64_t max_key) {
   return b;
 }
 
-// Sorts n (key, value) pairs in place (result in k0/v0); keys below 2^bits.
-hipError_t radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1, uint32_t* hist,
-                      int64_t n, int bits, hipStream_t st) {
+// Sorts n (key, value) pairs with keys below 2^bits, ping-ponging between the two buffers;
+// on return k0/v0 name the buffers that hold the result.
+hipError_t radix_sort_pp(uint64_t*& k0, uint32_t*& v0, uint64_t*& k1, uint32_t*& v1,
+                         uint32_t* hist, int64_t n, int bits, hipStream_t st) {
   const int64_t nblocks = (n + kSortTile - 1) / kSortTile;
   for (int shift = 0; shift < bits; shift += 8) {
     hipLaunchKernelGGL(radix_hist_kernel, dim3(unsigned(nblocks)), dim3(kSortThreads), 0, st, k0,
@@ -546,14 +547,20 @@ hipError_t radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1, ui
     std::swap(k0, k1);
     std::swap(v0, v1);
   }
-  // an odd number of passes leaves the result in the second buffer: copy it back
-  if (((bits + 7) / 8) % 2 == 1) {
-    hipError_t e = hipMemcpyAsync(k1, k0, size_t(n) * 8, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(v1, v0, size_t(n) * 4, hipMemcpyDeviceToDevice, st);
-    return e;
-  }
   return hipSuccess;
+}
+
+// The same with the result in the first buffers (an odd number of passes copies it back).
+hipError_t radix_sort(uint64_t* k0, uint32_t* v0, uint64_t* k1, uint32_t* v1, uint32_t* hist,
+                      int64_t n, int bits, hipStream_t st) {
+  uint64_t* ka = k0;
+  uint32_t* va = v0;
+  hipError_t e = radix_sort_pp(ka, va, k1, v1, hist, n, bits, st);
+  if (e == hipSuccess && ka != k0) {
+    e = hipMemcpyAsync(k0, ka, size_t(n) * 8, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(v0, va, size_t(n) * 4, hipMemcpyDeviceToDevice, st);
+  }
+  return e;
 }
 
 __global__ void clear_count_kernel(uint32_t* c) { *c = 0u; }
@@ -689,12 +696,14 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     hipLaunchKernelGGL(keys_subtables_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st,
                        b.idx, b.tokens, T, L.S, L.V0, row_bits, sentinel, b.keys0, b.vals0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = radix_sort(b.keys0, b.vals0, b.keys1, b.vals1, b.hist, n, key_bits(sentinel), st);
+    uint64_t *ks = b.keys0, *kt = b.keys1;
+    uint32_t *vs = b.vals0, *vt = b.vals1;
+    e = radix_sort_pp(ks, vs, kt, vt, b.hist, n, key_bits(sentinel), st);
     if (e != hipSuccess) return e;
     SegArgs a{};
     for (int s = 0; s < L.S; ++s) a.dst[s] = b.dE[s];
-    a.keys = b.keys0;
-    a.vals = b.vals0;
+    a.keys = ks;
+    a.vals = vs;
     a.src = basic ? b.dout : static_cast<const void*>(b.dG);
     a.head = b.head;
     a.tail = b.tail;
@@ -715,12 +724,14 @@ hipError_t launch_backward(const LayerDesc& L, const BackwardArgs& b, hipStream_
     hipLaunchKernelGGL(keys_tokens_kernel, dim3(unsigned((T + 255) / 256)), dim3(256), 0, st,
                        b.tokens, T, L.V0, sentinel, b.keys0, b.vals0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = radix_sort(b.keys0, b.vals0, b.keys1, b.vals1, b.hist, T, key_bits(sentinel), st);
+    uint64_t *ks = b.keys0, *kt = b.keys1;
+    uint32_t *vs = b.vals0, *vt = b.vals1;
+    e = radix_sort_pp(ks, vs, kt, vt, b.hist, T, key_bits(sentinel), st);
     if (e != hipSuccess) return e;
     SegArgs a{};
     a.dst[0] = b.dE0;
-    a.keys = b.keys0;
-    a.vals = b.vals0;
+    a.keys = ks;
+    a.vals = vs;
     a.src = b.dout;
     a.head = b.head;
     a.tail = b.tail;
