@@ -38,6 +38,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte vector
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// E_0 piece of VO consecutive bf16 outputs: 16 bytes for 8, 8 bytes for 4
+template <int VO> struct EVec;
+template <> struct EVec<8> { typedef u32x4_t type; };
+template <> struct EVec<4> { typedef u32x2_t type; };
 
 // One product out[m, n] = inv * (E0[tok[m], n] + sum_k A[m, k] B[n, k]) over nrows rows m and
 // N outputs n, with A's row m the concatenation of the S gathered rows E[s][idx[m, s]] (K
@@ -349,31 +353,44 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
 
   // -- epilogue: acc[j][i][4g + q] is output n = n0 + wn*WN + 32j + 8g + 4fk + q of row
   //    m = m0 + wm*WM + 32i + fr. Each wave stages 32 rows at a time (fp32) in its own
-  //    part of the LDS pool, then reads them back row-major: WN/4 lanes per row, 4
-  //    consecutive outputs per lane, so E_0 is read and the output written in whole
-  //    lines. E_0 add and the 1/(S+1) scale in fp32, one rounding to bf16.
+  //    part of the LDS pool, then reads them back row-major, VO consecutive outputs per
+  //    lane (WN/VO lanes per row), so E_0 is read and the output written in whole lines.
+  //    bf16 rows take 8 outputs per lane (16-byte E_0 loads and stores: half the memory
+  //    instructions of 4 per lane; 1204 -> 1163 us on the 64K-token batch). fp32 rows and
+  //    partial sums take 4 (16-byte stores already; 8 measured no faster with E_0 and 1%
+  //    slower without). E_0 add and the 1/(S+1) scale in fp32, one rounding to bf16.
   __syncthreads();                      // every wave is done with the slice buffers
   const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0[layer]);
   uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out[layer]);
   char* ep = lds + w * (32 * EP_PITCH);
-  constexpr int LPR = WN / 4;           // lanes per output row
+  constexpr int VO = OM == kOutBf16 ? 8 : 4;   // outputs per lane in the read-back
+  constexpr int LPR = WN / VO;          // lanes per output row
   constexpr int RPI = 64 / LPR;         // rows per wave instruction
   constexpr int NIT = 32 / RPI;
+  static_assert(64 % LPR == 0 && RPI <= 32, "a wave instruction covers whole rows");
+  typedef typename EVec<VO>::type ev_t;
+  // Byte offset, in a staged row, of outputs n .. n+3 (n % 4 == 0). With 8 per lane, the
+  // first 4 of every group of 8 sit in the row's first half and the other 4 in its second,
+  // so the read-back's 16 lanes of one LDS cycle read 256 contiguous bytes (no conflicts)
+  // and each staging write stays one 16-byte piece.
+  auto spos = [](int n) __attribute__((always_inline)) {
+    return VO == 8 ? ((n >> 2) & 1) * (WN * 2) + (n >> 3) * 16 : n * 4;
+  };
   const int er = lane / LPR, ec = lane % LPR;
   // the E_0 pieces of all of the wave's output rows are requested before any is used
   // (tokens from LDS), so the tile waits for one round trip to memory instead of two (the
   // token, then its row) per 32-row group: 12-20 us less per 64K-token launch
-  u32x2_t ev_all[OM != kOutPartial ? TI : 1][NIT];
+  ev_t ev_all[OM != kOutPartial ? TI : 1][NIT];
   if constexpr (OM != kOutPartial) {
-    const int n = n0 + wn * WN + ec * 4;
+    const int n = n0 + wn * WN + ec * VO;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int32_t tk = stok[wm * WM + i * 32 + it * RPI + er];
-        ev_all[i][it] = u32x2_t{0u, 0u};
+        ev_all[i][it] = ev_t{};
         if (E0 != nullptr && uint32_t(tk) < uint32_t(a.V0))
-          ev_all[i][it] = *reinterpret_cast<const u32x2_t*>(E0 + int64_t(tk) * a.N + n);
+          ev_all[i][it] = *reinterpret_cast<const ev_t*>(E0 + int64_t(tk) * a.N + n);
       }
   }
 #pragma unroll
@@ -384,21 +401,21 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
       for (int g = 0; g < 4; ++g) {
         f32x4_t v = {acc[j][i][4 * g + 0], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
                      acc[j][i][4 * g + 3]};
-        *reinterpret_cast<f32x4_t*>(ep + fr * EP_PITCH + (j * 32 + g * 8 + fk * 4) * 4) = v;
+        *reinterpret_cast<f32x4_t*>(ep + fr * EP_PITCH + spos(j * 32 + g * 8 + fk * 4)) = v;
       }
     // the wave reads back what its own lanes wrote: wait for the writes, keep the order
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // all loads of the 32 rows first (tok, then E_0), then the stores: a load placed after
     // a store would wait for it, since the compiler cannot rule out aliasing
     const int64_t mrow = m0 + wm * WM + i * 32 + er;
-    const int n = n0 + wn * WN + ec * 4;
+    const int n = n0 + wn * WN + ec * VO;
     if constexpr (OM == kOutPartial) {
       float* pp = static_cast<float*>(a.out[layer]) + int64_t(split) * a.nrows * a.ldo;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int64_t m = mrow + it * RPI;
         const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
-                                                             ec * 16);
+                                                             spos(ec * 4));
         if (m < a.nrows) *reinterpret_cast<f32x4_t*>(pp + m * a.ldo + n) = y;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -407,7 +424,7 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
     // without E_0 (dense products) every row is valid and nothing is added
     const bool has_e0 = E0 != nullptr;
     int32_t tk[NIT];
-    u32x2_t ev[NIT];
+    ev_t ev[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       tk[it] = stok[wm * WM + i * 32 + it * RPI + er];
@@ -416,25 +433,33 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int64_t m = mrow + it * RPI;
-      const f32x4_t y = *reinterpret_cast<const f32x4_t*>(ep + (it * RPI + er) * EP_PITCH +
-                                                           ec * 16);
+      const char* row = ep + (it * RPI + er) * EP_PITCH;
       if (m < a.nrows && tk[it] != kSkipRow) {
         const int64_t om = out_row(a, m);
         const bool ok = !has_e0 || uint32_t(tk[it]) < uint32_t(a.V0);
-        const float y0 = (y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv;
-        const float y1 = (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv;
-        const float y2 = (y[2] + bf16_to_f32(ev[it].y & 0xffffu)) * a.inv;
-        const float y3 = (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv;
         if constexpr (OM == kOutF32) {
-          const f32x4_t res = ok ? f32x4_t{y0, y1, y2, y3} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const f32x4_t y = *reinterpret_cast<const f32x4_t*>(row + spos(ec * 4));
+          const f32x4_t res = ok ? f32x4_t{(y[0] + bf16_to_f32(ev[it].x & 0xffffu)) * a.inv,
+                                           (y[1] + bf16_to_f32(ev[it].x >> 16)) * a.inv,
+                                           (y[2] + bf16_to_f32(ev[it].y & 0xffffu)) * a.inv,
+                                           (y[3] + bf16_to_f32(ev[it].y >> 16)) * a.inv}
+                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
           *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + om * a.ldo + n) = res;
         } else {
-          u32x2_t res = {0u, 0u};
+          const f32x4_t ya = *reinterpret_cast<const f32x4_t*>(row + spos(ec * 8));
+          const f32x4_t yb = *reinterpret_cast<const f32x4_t*>(row + spos(ec * 8 + 4));
+          u32x4_t res = {0u, 0u, 0u, 0u};
           if (ok) {
-            res.x = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
-            res.y = f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const f32x4_t& y = h < 2 ? ya : yb;
+              const uint32_t e = ev[it][h];
+              const float lo = (y[(h & 1) * 2] + bf16_to_f32(e & 0xffffu)) * a.inv;
+              const float hi = (y[(h & 1) * 2 + 1] + bf16_to_f32(e >> 16)) * a.inv;
+              res[h] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+            }
           }
-          __builtin_nontemporal_store(res, reinterpret_cast<u32x2_t*>(out + om * a.ldo + n));
+          __builtin_nontemporal_store(res, reinterpret_cast<u32x4_t*>(out + om * a.ldo + n));
         }
       }
     }
