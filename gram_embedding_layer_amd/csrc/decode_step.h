@@ -1,8 +1,8 @@
-// Device code shared by the decode hash kernel and the decode prologue of the projection:
-// the exact Horner step of the rolling hash (section A2 of the deep-notes page on "Scaling
-// Embeddings Outperforms Scaling Experts in Language Models") and what one batch entry of a
-// decode step reads from and appends to the N-gram cache (section 4.2: the last N-1
-// committed ids of every sequence kept on the device).
+// Device code of the decode step's hash kernel and the exact Horner step it shares with the
+// prefill hash (the rolling hash of section A2 of the deep-notes page on "Scaling Embeddings
+// Outperforms Scaling Experts in Language Models"): what one batch entry of a decode step
+// reads from and appends to the N-gram cache (section 4.2: the last N-1 committed ids of
+// every sequence kept on the device).
 #pragma once
 
 #include "kernels.h"
@@ -98,20 +98,16 @@ __device__ __forceinline__ void entry_context(const LayerDesc& L, const DecodeEn
 }
 
 // H_{n,k} for sub-table s (n = 2 + s / K) of a row with context c: its last n ids reduced
-// by Horner's rule from the oldest id to the newest. c in registers (an array, so the loop is
-// unrolled over NMAX) or in LDS (a pointer: exactly n steps).
-template <int NMAX, typename C>
-__device__ __forceinline__ int32_t context_hash(const LayerDesc& L, const C& c, int s) {
+// by Horner's rule from the oldest id to the newest.
+template <int NMAX>
+__device__ __forceinline__ int32_t context_hash(const LayerDesc& L, const uint32_t (&c)[NMAX],
+                                                int s) {
   const int n = 2 + s / L.K;
   const uint64_t V = L.V[s], m = L.Vinv[s];
   uint64_t x = 0;
-  if constexpr (__is_pointer(C)) {
-    for (int i = n - 1; i >= 0; --i) x = horner_step(x, uint64_t(L.V0), c[i], V, m);
-  } else {
 #pragma unroll
-    for (int i = NMAX - 1; i >= 0; --i)
-      if (i < n) x = horner_step(x, uint64_t(L.V0), c[i], V, m);
-  }
+  for (int i = NMAX - 1; i >= 0; --i)
+    if (i < n) x = horner_step(x, uint64_t(L.V0), c[i], V, m);
   return int32_t(x);
 }
 
