@@ -316,12 +316,37 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
   // every load of the slice gets a slot (NM / EVERY slots per k-step, at most DPP used)
   static_assert((NM / EVERY < DPP ? NM / EVERY : DPP) * LOAD_STEPS >= PER_SLICE,
                 "the load slots of a slice must cover its loads");
-  auto mma = [&](int buf, bool loads, int part) __attribute__((always_inline)) {
+  // When a k-step has at least as many matrix-core ops as fragment reads (256 x 256 tiles: 8
+  // ops, 6 reads), the next k-step's fragments are read one after each op, into the other
+  // fragment buffer, in the order that k-step's ops use them; otherwise (shorter tiles) a
+  // k-step's reads go out together, two k-steps ahead. 64K-token batch: 1154 vs 1176 us and
+  // 1177 vs 1208 us in two same-box A/Bs, outputs bitwise equal (the same reads and ops in
+  // another order). With one wave per SIMD (4 waves of 128 x 128) it gained nothing: 1250 us.
+  constexpr bool kInterleave = NM >= TI + TJ;
+  // r-th fragment read of k-step kk: wf[0], xf[0 .. TI-1], then wf[1 .. TJ-1]
+  auto frag1 = [&](const char* sp, int kk, int buf, int r) __attribute__((always_inline)) {
+    if (r == 0)
+      wf[buf][0] = *reinterpret_cast<const bf16x8_t*>(sp + brow0 + pcs[kk]);
+    else if (r <= TI)
+      xf[buf][r - 1] =
+          *reinterpret_cast<const bf16x8_t*>(sp + arow0 + (r - 1) * 32 * RB + pcs[kk]);
+    else
+      wf[buf][r - TI] =
+          *reinterpret_cast<const bf16x8_t*>(sp + brow0 + (r - TI) * 32 * RB + pcs[kk]);
+  };
+  auto mma = [&](int buf, bool loads, int part, const char* sp) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
       const int j = x / TI, i = x % TI;
       acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], xf[buf][i], acc[j][i],
                                                           0, 0, 0);
+      if constexpr (kInterleave) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (part + 1 < KS && x < TI + TJ) {
+          frag1(sp, part + 1, buf ^ 1, x);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       const int q = part * DPP + (x + 1) / EVERY - 1;
       if (loads && (x + 1) % EVERY == 0 && (x + 1) / EVERY <= DPP && q < PER_SLICE) {
         __builtin_amdgcn_sched_barrier(0);
@@ -345,11 +370,16 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
     if (loads) prep(kt_lo + k + NST - 1);
     const char* sp = lds + (k % NST) * STAGE;
     frags(sp, 0, 0);
-    if (KS > 1) frags(sp, 1, 1);
+    if constexpr (kInterleave) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      mma(kk & 1, loads, kk);
-      if (kk + 2 < KS) frags(sp, kk + 2, kk & 1);
+      for (int kk = 0; kk < KS; ++kk) mma(kk & 1, loads, kk, sp);
+    } else {
+      if (KS > 1) frags(sp, 1, 1);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        mma(kk & 1, loads, kk, sp);
+        if (kk + 2 < KS) frags(sp, kk + 2, kk & 1);
+      }
     }
   }
 
