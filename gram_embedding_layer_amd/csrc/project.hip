@@ -373,11 +373,15 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
     else if (NST >= 3 && ahead >= 1) wait_loads_and_meet<(NST >= 3 ? 1 : 0) * PER_SLICE>();
     else wait_loads_and_meet<0>();
     const char* sp = lds + (k % NST) * STAGE;
-    frags(sp, 0, 0);
     if constexpr (kInterleave) {
+      // the first k-step's fragments in the order its ops use them, so the first op waits
+      // for two reads rather than five (1131-1132 vs 1137-1146 us, bitwise equal)
+#pragma unroll
+      for (int r = 0; r < TI + TJ; ++r) frag1(sp, 0, 0, r);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) mma(kk & 1, loads, kk, sp);
     } else {
+      frags(sp, 0, 0);
       if (KS > 1) frags(sp, 1, 1);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
@@ -395,7 +399,6 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
   //    instructions of 4 per lane; 1204 -> 1163 us on the 64K-token batch). fp32 rows and
   //    partial sums take 4 (16-byte stores already; 8 measured no faster with E_0 and 1%
   //    slower without). E_0 add and the 1/(S+1) scale in fp32, one rounding to bf16.
-  __syncthreads();                      // every wave is done with the slice buffers
   const uint16_t* __restrict__ E0 = static_cast<const uint16_t*>(a.E0[layer]);
   uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out[layer]);
   char* ep = lds + w * (32 * EP_PITCH);
@@ -414,21 +417,38 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
   };
   const int er = lane / LPR, ec = lane % LPR;
   // the E_0 pieces of all of the wave's output rows are requested before any is used
-  // (tokens from LDS), so the tile waits for one round trip to memory instead of two (the
-  // token, then its row) per 32-row group: 12-20 us less per 64K-token launch
+  // (tokens from LDS, all read first; loads not behind a branch each), so the tile waits for
+  // one round trip to memory instead of two (the token, then its row) per 32-row group:
+  // 12-20 us less per 64K-token launch; issued before the barrier below, they fly while the
+  // waves meet (1094-1101 vs 1102-1107 us, bitwise equal)
   ev_t ev_all[OM != kOutPartial ? TI : 1][NIT];
   if constexpr (OM != kOutPartial) {
     const int n = n0 + wn * WN + ec * VO;
+    int32_t tka[TI][NIT];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int32_t tk = stok[wm * WM + i * 32 + it * RPI + er];
-        ev_all[i][it] = ev_t{};
-        if (E0 != nullptr && uint32_t(tk) < uint32_t(a.V0))
+      for (int it = 0; it < NIT; ++it) tka[i][it] = stok[wm * WM + i * 32 + it * RPI + er];
+    if (E0 != nullptr) {
+      // rows with an invalid token read row 0 (their outputs are zeros or not written)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int32_t tk = uint32_t(tka[i][it]) < uint32_t(a.V0) ? tka[i][it] : 0;
           ev_all[i][it] = *reinterpret_cast<const ev_t*>(E0 + int64_t(tk) * a.N + n);
-      }
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) ev_all[i][it] = ev_t{};
+    }
   }
+  // Every wave is done with the slice buffers before any stages its results there. No slice
+  // load is in flight (the last slice waited for all of them), so the waves meet after their
+  // LDS reads only; a __syncthreads would also wait for the E_0 requests above.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
