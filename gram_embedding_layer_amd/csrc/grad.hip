@@ -479,36 +479,60 @@ __global__ __launch_bounds__(THREADS) void segsum_level1_kernel(const SegArgs a)
 
 // Level 2: each chunk listed by level 1 (its last run starts in it and continues) adds its
 // tail and the head sums of the following chunks that the run covers, in order. The run's
-// end is found by binary search first, so the sum's loads do not wait on each other. Blocks
-// stride over the list; its order does not matter (each run has one owner).
+// end is found first, so the sum's loads do not wait on each other: each lane of a wave
+// checks whether the run reaches one of the next 64 chunks (the chunk's first entry holds
+// the run's key; keys are sorted, so the run covers every chunk before it), and only a
+// longer run takes a binary search past them.
+// Blocks stride over the list; its order does not matter (each run has one owner).
 template <int THREADS, int NV>
 __global__ __launch_bounds__(THREADS) void segsum_level2_kernel(const SegArgs a) {
   using C = Cols<THREADS, NV>;
   const uint32_t n_owners = a.owners[0];
+  const int lane = threadIdx.x & 63;
   for (uint32_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
     const int64_t chunk = a.owners[1 + o];
     const int64_t hi = std::min<int64_t>(a.n, chunk * a.chunk + a.chunk);
     const uint64_t key = a.keys[hi - 1];
-    int64_t l = hi, r = a.n;                       // first index past the run in [hi, n)
-    while (l < r) {
-      const int64_t m = (l + r) / 2;
-      if (a.keys[m] == key) l = m + 1; else r = m;
+    const int64_t pc = chunk + 1 + lane;           // chunk whose first entry this lane checks
+    const bool reaches = pc < a.nchunks && a.keys[pc * a.chunk] == key;
+    const uint64_t stop = __ballot(!reaches);      // lane 0 reaches (the run continues)
+    int64_t last_chunk;                            // chunks chunk+1 .. last_chunk hold a head
+    if (stop != 0) {
+      last_chunk = chunk + __builtin_ctzll(stop);
+    } else {
+      // A 64-way search for the first index past the run in [l, r] (keys[l - 1] holds the
+      // run's key; keys[r] is past it, or r = n). Each round lane i checks the last entry of
+      // the i-th of 64 equal segments of [l, r); the first segment whose last entry is past
+      // the run holds the answer, and if none is, the run fills [l, r).
+      int64_t l = std::min<int64_t>(a.n, (chunk + 64) * a.chunk + 1), r = a.n;
+      while (l < r) {
+        const int64_t step = (r - l + 63) / 64;
+        const int64_t p = std::min<int64_t>(r, l + (lane + 1) * step) - 1;
+        const uint64_t past = __ballot(l + lane * step < r && a.keys[p] != key);
+        if (past == 0) {
+          l = r;
+        } else {
+          const int i = __builtin_ctzll(past);
+          r = std::min<int64_t>(r, l + (i + 1) * step) - 1;   // that segment's last entry
+          l += i * step;                                     // that segment's first entry
+        }
+      }
+      last_chunk = (l - 1) / a.chunk;
     }
-    const int64_t last_chunk = (l - 1) / a.chunk;  // chunks chunk+1 .. last_chunk hold a head
+    // the tail, then the heads in chunk order; each lane's columns are fixed, so the loads
+    // of one column range do not sit behind a branch and go out several at a time
     f32x4_t acc[NV];
     const float* tl = a.tail + chunk * a.width;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int c = C::col(v);
-      acc[v] = c < a.width ? *reinterpret_cast<const f32x4_t*>(tl + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll 8
-    for (int64_t ch = chunk + 1; ch <= last_chunk; ++ch) {
-      const float* hd = a.head + ch * a.width;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int c = C::col(v);
-        if (c < a.width) acc[v] += *reinterpret_cast<const f32x4_t*>(hd + c);
+      acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (c < a.width) {
+        f32x4_t sum = *reinterpret_cast<const f32x4_t*>(tl + c);
+#pragma unroll 16
+        for (int64_t ch = chunk + 1; ch <= last_chunk; ++ch)
+          sum += *reinterpret_cast<const f32x4_t*>(a.head + ch * a.width + c);
+        acc[v] = sum;
       }
     }
     float* dst = dst_row(a, key);

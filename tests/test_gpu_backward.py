@@ -90,6 +90,33 @@ def test_backward_matches_oracle(lib, name, w, lengths, amp):
         check(f"{name} dW", dW, dW_ref, 1e-5)
 
 
+def test_backward_runs_ending_on_chunk_boundaries(lib):
+    """Repeated ids are summed in chunks of sorted entries (64 for E_0, 32 for sub-tables);
+    a run that crosses chunks is finished by the chunk it starts in. Token counts are chosen so
+    that E_0 runs end exactly at chunk ends (32 + 96 entries, then 64, then 66 whole chunks,
+    which is also longer than the 64 chunks probed at once), and a tiny vocabulary gives long
+    sub-table runs that cross many chunks."""
+    w = small_workload("bf16", D=256, N=3, K=2, V0=8)
+    E0, E, W = host_to_dev_tables(w)
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    counts = {1: 32, 2: 96, 3: 64, 4: 64 * 66, 5: 100, 6: 7}
+    multiset = np.concatenate([np.full(c, t, dtype=np.int32) for t, c in counts.items()])
+    rng = np.random.default_rng(21)
+    rng.shuffle(multiset)
+    half = len(multiset) // 2
+    tokens, cu = packed([multiset[:half], multiset[half:]])
+    dout = upstream(w, len(tokens), 23)
+    bufs = grad_buffers(w)
+    run_backward(cfg, g.Tables(E0, E, W), tokens, cu, dout, bufs)
+    idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
+    dE0_r, dE_r, dW_r = oracle.backward(w.D, w.N, w.K, tokens, idx, to_f64(dout),
+                                         device_fetch(E0, E), w_blocks(W, w.S), w.V0, w.V, 1.0)
+    dE0, dE, dW = bufs
+    check("aligned dE0", dE0, dE0_r, 1e-5)
+    for s in range(w.S):
+        check(f"aligned dE[{s}]", dE[s], dE_r[s], 1e-5)
+
+
 def test_backward_is_repeatable_and_accumulates(lib):
     w = small_workload("bf16", D=256, N=3, K=2, V0=50)
     E0, E, W = host_to_dev_tables(w)
