@@ -20,9 +20,10 @@
 // 1/(S+1) (times the output factor of the scale amplification, section 3.2.4) in fp32 and
 // rounds once to bf16, or, for the layer-normalisation amplification, stores the unrounded
 // fp32 rows that the normalisation pass reads.
-// Measured on MI355X (64K rows, D = 3072): the loads, not the matrix cores, bound this
-// kernel; each CU keeps about 48 L2 lines in flight, so its load rate is set by L2 hit
-// latency, and the tile order below is chosen for L2 reuse.
+// Measured on MI355X (64K rows, D = 3072): the loads into LDS, not the matrix cores, bound
+// this kernel. Dropping either operand's slice loads saves less than their sum, and running
+// one operand's loads two slices ahead gains nothing, so the bytes each CU moves into LDS per
+// slice set the pace; the tile order below is chosen for L2 reuse.
 // Blocks are numbered so that the 32 blocks resident on one XCD at a time cover 4 row
 // tiles x 8 output tiles, which keeps their A rows and W panels in that XCD's L2.
 #include <algorithm>
