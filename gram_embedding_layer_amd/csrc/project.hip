@@ -321,7 +321,7 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
   // ops, 6 reads), the next k-step's fragments are read one after each op, into the other
   // fragment buffer, in the order that k-step's ops use them; otherwise (shorter tiles) a
   // k-step's reads go out together, two k-steps ahead. 64K-token batch: 1154 vs 1176 us and
-  // 1177 vs 1208 us in two same-box A/Bs, outputs bitwise equal (the same reads and ops in
+  // 1177 vs 1208 us in two same-GPU A/Bs, outputs bitwise equal (the same reads and ops in
   // another order). With one wave per SIMD (4 waves of 128 x 128) it gained nothing: 1250 us.
   constexpr bool kInterleave = NM >= TI + TJ;
   // r-th fragment read of k-step kk: wf[0], xf[0 .. TI-1], then wf[1 .. TJ-1]
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
     // The next loads' addresses first: they read only the tile's indices (fixed since the
     // tile start), so their LDS round trip at a sub-table's first slice overlaps the wait
     // below instead of delaying the first matrix-core op (64K-token batch: 1138 vs 1154 us
-    // and 1197 vs 1210 us in two same-box A/Bs, outputs bitwise equal).
+    // and 1197 vs 1210 us in two same-GPU A/Bs, outputs bitwise equal).
     const bool loads = k + NST - 1 < NK;
     if (loads) prep(kt_lo + k + NST - 1);
     // own loads of slice k done (the later slices already issued stay in flight), then all
