@@ -14,22 +14,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Hash one position. c[j] = t_{i-j} (pad 0 before the sequence start), j < NMAX.
-template <int NMAX>
-__device__ __forceinline__ void hash_position(const LayerDesc& L, const uint32_t (&c)[NMAX],
-                                              int32_t* __restrict__ out) {
-  const uint64_t V0 = uint64_t(L.V0);
-  for (int s = 0; s < L.S; ++s) {
-    const int n = 2 + s / L.K;             // order of sub-table s = (n-2)K + (k-1)
-    const uint64_t V = L.V[s], m = L.Vinv[s];
-    uint64_t x = 0;
-#pragma unroll
-    for (int j = NMAX - 1; j >= 0; --j)
-      if (j < n) x = horner_step(x, V0, c[j], V, m);
-    out[s] = int32_t(x);
-  }
-}
-
 // Thread i of a prefill-shaped launch: checks entry i of cu_seqlens (0 = c_0 <= c_1 <= ...
 // <= c_nseq = ntok), then, for a position i < ntok, its id, and fills c[j] = t_{i-j} for
 // j < nord (pad id 0 before the start of the position's sequence). False past the batch.
@@ -62,14 +46,28 @@ __device__ __forceinline__ bool position_context(const int32_t* __restrict__ tok
   return true;
 }
 
+// One thread per (position, sub-table): thread g hashes sub-table g % S of position g / S, so
+// a position's S hashes run side by side (a thread per position left one wave per SIMD
+// working through ~36 dependent 64-bit Horner steps) and the index writes are contiguous.
+// The position's first thread checks cu_seqlens and the id.
 template <int NMAX>
 __global__ __launch_bounds__(kThreads) void hash_prefill_kernel(
     const LayerDesc L, const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu,
     int32_t nseq, int64_t ntok, int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t i = g / L.S;
+  const int s = int(g - i * L.S);
   uint32_t c[NMAX];
-  if (position_context<NMAX>(tokens, cu, nseq, ntok, L.V0, L.N, i, flags, c))
-    hash_position<NMAX>(L, c, idx + i * L.S);
+  if (!position_context<NMAX>(tokens, cu, nseq, ntok, L.V0, L.N, i, s == 0 ? flags : nullptr,
+                              c))
+    return;
+  const int n = 2 + s / L.K;               // order of sub-table s = (n-2)K + (k-1)
+  const uint64_t V = L.V[s], m = L.Vinv[s];
+  uint64_t x = 0;
+#pragma unroll
+  for (int j = NMAX - 1; j >= 0; --j)
+    if (j < n) x = horner_step(x, uint64_t(L.V0), c[j], V, m);
+  idx[g] = int32_t(x);
 }
 
 // One decode step: every thread hashes one (batch entry, row, sub-table) of the window
@@ -322,7 +320,7 @@ template <int NMAX>
 hipError_t hash_prefill_n(const LayerDesc& L, const int32_t* tokens, const int32_t* cu,
                           int32_t nseq, int64_t ntok, int32_t* idx, int32_t* flags,
                           hipStream_t st) {
-  const int64_t work = ntok > int64_t(nseq) + 1 ? ntok : int64_t(nseq) + 1;
+  const int64_t work = (ntok > int64_t(nseq) + 1 ? ntok : int64_t(nseq) + 1) * L.S;
   const unsigned blocks = unsigned((work + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(hash_prefill_kernel<NMAX>, dim3(blocks), dim3(kThreads), 0, st, L, tokens,
                      cu, nseq, ntok, idx, flags);
