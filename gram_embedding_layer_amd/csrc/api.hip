@@ -88,8 +88,8 @@ int check_layers(const LayerDesc& L, const ngram_embed_tables* T, int32_t nlayer
 
 int prefill_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                  int32_t nlayers, const int32_t* tokens, const int32_t* cu_seqlens,
-                 int32_t nseq, int64_t ntok, void* const* outs, void* ws, size_t ws_bytes,
-                 void* stream);
+                 int32_t nseq, int64_t ntok, void* const* outs, ngram_cache* cache, void* ws,
+                 size_t ws_bytes, void* stream);
 int decode_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                 int32_t nlayers, ngram_cache* cache, const int32_t* new_tokens,
                 const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
@@ -106,18 +106,32 @@ int32_t* ws_flags(void* ws) { return static_cast<int32_t*>(ws); }
 
 int prefill_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                  int32_t nlayers, const int32_t* tokens, const int32_t* cu_seqlens,
-                 int32_t nseq, int64_t ntok, void* const* outs, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 int32_t nseq, int64_t ntok, void* const* outs, ngram_cache* cache, void* ws,
+                 size_t ws_bytes, void* stream) {
   LayerDesc L;
   int rc = ngram::describe(cfg, &L);
   if (rc != NGRAM_OK) return rc;
   if (ntok < 0 || nseq < 0 || (ntok > 0 && nseq < 1)) return NGRAM_EINVAL;
+  if (cache != nullptr && cache->nseq != nseq) return NGRAM_EINVAL;
   ngram::WsLayout lay;
   if ((rc = check_ws(L, ws, ws_bytes, ntok, &lay)) != NGRAM_OK) return rc;
-  if (ntok == 0) return NGRAM_OK;
-  if ((rc = check_layers(L, tables, nlayers, outs)) != NGRAM_OK) return rc;
-  if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+  if (cache != nullptr && nseq > 0) {
+    if (!ngram::aligned(cache->len, 8) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+    if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  }
+  if (ntok > 0) {
+    if ((rc = check_layers(L, tables, nlayers, outs)) != NGRAM_OK) return rc;
+    if (!ngram::aligned(tokens, 4) || !ngram::aligned(cu_seqlens, 4)) return NGRAM_EALIGN;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // the cache of the prompts (section 4.2): their lengths and last N-1 ids, as
+  // ngram_cache_init fills it (empty sequences included, so also when ntok = 0)
+  if (cache != nullptr && nseq > 0) {
+    rc = hip_status(ngram::launch_cache_init(L, cache->ring, cache->len, nullptr, cache->nseq,
+                                             tokens, cu_seqlens, nseq, ntok, ws_flags(ws), st));
+    if (rc != NGRAM_OK) return rc;
+  }
+  if (ntok == 0) return NGRAM_OK;
   int32_t* idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.idx_off);
   if (L.S > 0) {
     rc = hip_status(ngram::launch_hash_prefill(L, tokens, cu_seqlens, nseq, ntok, idx,
@@ -232,10 +246,11 @@ int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables*
 
 int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                         const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
-                        int64_t ntok, void* out, void* ws, size_t ws_bytes, void* stream) {
+                        int64_t ntok, void* out, ngram_cache* cache_or_null, void* ws,
+                        size_t ws_bytes, void* stream) {
   void* outs[1] = {out};
-  return prefill_impl(cfg, tables, 1, tokens, cu_seqlens, nseq, ntok, outs, ws, ws_bytes,
-                      stream);
+  return prefill_impl(cfg, tables, 1, tokens, cu_seqlens, nseq, ntok, outs, cache_or_null, ws,
+                      ws_bytes, stream);
 }
 
 int ngram_embed_prefill_layers(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
@@ -243,8 +258,8 @@ int ngram_embed_prefill_layers(const ngram_embed_config* cfg, const ngram_embed_
                                const int32_t* cu_seqlens, int32_t nseq, int64_t ntok,
                                void* const* out, void* ws, size_t ws_bytes, void* stream) {
   if (nlayers < 1) return NGRAM_EINVAL;
-  return prefill_impl(cfg, tables, nlayers, tokens, cu_seqlens, nseq, ntok, out, ws, ws_bytes,
-                      stream);
+  return prefill_impl(cfg, tables, nlayers, tokens, cu_seqlens, nseq, ntok, out, nullptr, ws,
+                      ws_bytes, stream);
 }
 
 int ngram_cache_init(const ngram_embed_config* cfg, ngram_cache* cache, const int32_t* tokens,

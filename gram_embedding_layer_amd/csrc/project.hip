@@ -112,14 +112,14 @@ typedef __attribute__((address_space(3))) char lds_char;
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
 // (global_load_lds_dwordx4). Written as asm so that its completion is waited for only by
 // the explicit vmcnt waits below (the compiler would otherwise drain every load in flight
-// before each LDS read); it has no register result. m0 is set here and declared clobbered
-// (hipcc warns that m0 is reserved): the compiler keeps nothing in m0 in these kernels (in
-// their generated code every m0 write is one of these), so no value of its own is lost.
+// before each LDS read); it has no register result. The LDS address is an input operand
+// bound to m0 ("{m0}"), so the compiler itself writes m0 before the instruction and knows
+// that m0 holds this value: nothing of its own can be lost. The s_nop covers the one wait
+// state an LDS DMA needs after an m0 write.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\t"
-               "s_nop 0\n\t"
+  asm volatile("s_nop 0\n\t"
                "global_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+               :: "v"(gptr), "{m0}"(lds_addr) : "memory");
 }
 
 // Wait until at most N of this wave's global loads are in flight (they complete in issue

@@ -51,7 +51,9 @@ int describe(const ngram_embed_config* cfg, LayerDesc* out) {
   L.ln_eps = 0.0f;
   if (cfg->amp == NGRAM_AMP_SCALE) {
     if (!std::isfinite(cfg->amp_scale)) return NGRAM_EINVAL;
-    L.scale = cfg->amp_scale;
+    // the sentinel selects the pages' factor sqrt(D) (section 3.2.4)
+    L.scale = cfg->amp_scale == NGRAM_AMP_SCALE_SQRT_D ? std::sqrt(float(cfg->D))
+                                                       : cfg->amp_scale;
   } else if (cfg->amp == NGRAM_AMP_LAYERNORM) {
     if (!std::isfinite(cfg->ln_eps) || !(cfg->ln_eps > 0.0f)) return NGRAM_EINVAL;
     if (cfg->D > kMaxNormD) return NGRAM_EINVAL;

@@ -79,7 +79,8 @@ enum {
  * computed in fp32 from the unrounded e and rounded once. */
 enum {
   NGRAM_AMP_NONE = 0,      /* out = e_i: the final form as is */
-  NGRAM_AMP_SCALE = 1,     /* out = amp_scale * e_i (the pages use sqrt(D)), one rounding */
+  NGRAM_AMP_SCALE = 1,     /* out = amp_scale * e_i, one rounding; amp_scale =
+                              NGRAM_AMP_SCALE_SQRT_D selects the pages' factor sqrt(D) */
   NGRAM_AMP_LAYERNORM = 2  /* out = LayerNorm(e_i) as above; needs the workspace (prefill,
                               decode), so ngram_embed_project rejects it */
 };
@@ -93,6 +94,10 @@ enum {
   NGRAM_FORM_FINAL = 0,  /* the final (Over-Encoding) form, with projections */
   NGRAM_FORM_BASIC = 1   /* the basic form (Eq. 1): K must be 1 */
 };
+
+/* amp_scale value that selects sqrt(D), the factor the pages use (section 3.2.4; the
+ * popular article prints the radical); the library computes it as sqrtf(D) */
+#define NGRAM_AMP_SCALE_SQRT_D 0.0f
 
 #define NGRAM_MAX_ORDER 16         /* largest accepted N */
 #define NGRAM_MAX_SUBTABLES 64     /* largest accepted (N-1)K */
@@ -110,7 +115,8 @@ typedef struct ngram_embed_config {
   const int64_t* V;  /* host, S entries: V_{n,k} in sub-table order, 1 <= V < 2^31,
                         and V0 * max V < 2^63 (else NGRAM_EOVERFLOW) */
   int32_t amp;       /* NGRAM_AMP_*; 0 (a zero-filled config) is the final form as is */
-  float amp_scale;   /* NGRAM_AMP_SCALE: the factor, finite (ignored otherwise) */
+  float amp_scale;   /* NGRAM_AMP_SCALE: the factor, finite; NGRAM_AMP_SCALE_SQRT_D (0)
+                        for sqrt(D) (ignored otherwise) */
   float ln_eps;      /* NGRAM_AMP_LAYERNORM: variance epsilon, finite and > 0; the layer
                         normalisation also needs D <= 8192 (ignored otherwise) */
   int32_t form;      /* NGRAM_FORM_*; 0 is the final form */
@@ -185,10 +191,15 @@ int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables*
  * ngram_embed_project with tok = tokens, then the amplification the config selects (the
  * layer normalisation as a second pass over the unrounded rows kept in the workspace; rows
  * of ids outside [0, V0) stay zero). out: device [ntok, D]. ws: workspace of at least
- * ngram_embed_workspace_size(cfg, ntok) bytes; bad ids set NGRAM_FLAG_BAD_TOKEN there. */
+ * ngram_embed_workspace_size(cfg, ntok) bytes; bad ids set NGRAM_FLAG_BAD_TOKEN there.
+ * cache_or_null: NULL, or an N-gram cache with cache->nseq == nseq that the same call fills
+ * for decoding on after the prompts (section 4.2), exactly as ngram_cache_init would: slot b
+ * gets sequence b's length and its last N-1 ids (pad id 0 before its start); bad cu_seqlens
+ * set NGRAM_FLAG_BAD_SEQLENS in the workspace. A cache with another nseq is NGRAM_EINVAL. */
 int ngram_embed_prefill(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                         const int32_t* tokens, const int32_t* cu_seqlens, int32_t nseq,
-                        int64_t ntok, void* out, void* ws, size_t ws_bytes, void* stream);
+                        int64_t ntok, void* out, ngram_cache* cache_or_null, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- kernel 4: decode
  * Fill a cache from prefilled sequences: len[b] = sequence length, ring = its last N-1 ids

@@ -95,7 +95,7 @@ def test_workspace_size_and_layout(lib):
 def test_config_validation(lib, kw, status):
     cfg = tiny_cfg(**kw)
     c, keep = cfg._c()
-    rc = lib.ngram_embed_prefill(ctypes.byref(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, 1 << 20, 0)
+    rc = lib.ngram_embed_prefill(ctypes.byref(c), None, FAKE, FAKE, 1, 16, FAKE, None, FAKE, 1 << 20, 0)
     assert rc == status
     assert lib.ngram_embed_workspace_size(ctypes.byref(c), 16) == 0
 
@@ -112,19 +112,19 @@ def test_prefill_argument_checks(lib):
     ws_need = g.ngram_embed_workspace_size(cfg, 16)
     P = ctypes.byref
     # workspace too small / misaligned
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need - 1, 0) == -4
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, FAKE + 64, ws_need, 0) == -4
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, None, FAKE, ws_need - 1, 0) == -4
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE, None, FAKE + 64, ws_need, 0) == -4
     # negative sizes, no sequences for tokens
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, -1, FAKE, FAKE, ws_need, 0) == -1
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 0, 16, FAKE, FAKE, ws_need, 0) == -1
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, -1, FAKE, None, FAKE, ws_need, 0) == -1
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 0, 16, FAKE, None, FAKE, ws_need, 0) == -1
     # misaligned table / output / token pointers
     Tb, k3 = _tables_c(4, e0=FAKE + 8)
-    assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, None, FAKE, ws_need, 0) == -3
     Tb, k4 = _tables_c(4, sub=FAKE + 2)
-    assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE + 8, FAKE, ws_need, 0) == -3
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE + 1, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
-    assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, None, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 1, 16, FAKE + 8, None, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE + 1, FAKE, 1, 16, FAKE, None, FAKE, ws_need, 0) == -3
+    assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, None, FAKE, ws_need, 0) == -3
 
 
 def test_layers_argument_checks(lib):
@@ -246,7 +246,7 @@ def test_amplification_checks(lib):
                dict(amp="layernorm", N=2, K=1, D=8192 + 64, V=[5003])):
         c, keep = tiny_cfg(**kw)._c()
         assert lib.ngram_embed_workspace_size(P(c), 16) == 0, kw
-        assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, FAKE, 1 << 20, 0) == -1
+        assert lib.ngram_embed_prefill(P(c), None, FAKE, FAKE, 1, 16, FAKE, None, FAKE, 1 << 20, 0) == -1
     c, keep = ln._c()
     T, keep2 = _tables_c(4)
     assert lib.ngram_embed_project(P(c), P(T), FAKE, FAKE, 5, FAKE, 0) == -1
@@ -254,7 +254,7 @@ def test_amplification_checks(lib):
     arr = (ctypes.c_void_p * 4)(*([FAKE] * 4))
     for wt, bs in ((FAKE + 2, None), (None, FAKE + 8)):
         Tb = g._CTables(FAKE, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), FAKE, wt, bs)
-        assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, FAKE, ws_need,
+        assert lib.ngram_embed_prefill(P(c), P(Tb), FAKE, FAKE, 1, 16, FAKE, None, FAKE, ws_need,
                                        0) == -3
 
 
@@ -302,7 +302,7 @@ def test_zero_sized_calls_enqueue_nothing(lib):
     T, keep2 = _tables_c(4)
     P = ctypes.byref
     ws = g.ngram_embed_workspace_size(cfg, 0)
-    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 0, 0, FAKE, FAKE, ws, 0) == 0
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 0, 0, FAKE, None, FAKE, ws, 0) == 0
     assert lib.ngram_embed_hash(P(c), FAKE, FAKE, 0, 0, FAKE, None, 0) == 0
     assert lib.ngram_embed_gather(P(c), P(T), FAKE, 0, FAKE, 0) == 0
     assert lib.ngram_embed_project(P(c), P(T), FAKE, FAKE, 0, FAKE, 0) == 0
@@ -325,3 +325,155 @@ def test_host_validation_under_sanitizers(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "all passed" in res.stdout
+
+
+def test_prefill_cache_argument_checks(lib):
+    """cache_or_null of ngram_embed_prefill: one slot per sequence, aligned ring and len."""
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    P = ctypes.byref
+    ws = g.ngram_embed_workspace_size(cfg, 16)
+    other = g._CCache(FAKE, FAKE, 3)                        # 3 slots for 2 sequences
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 2, 16, FAKE, P(other), FAKE, ws,
+                                   0) == -1
+    bad_len = g._CCache(FAKE, FAKE + 4, 2)                  # int64 lengths, 4-byte aligned
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 2, 16, FAKE, P(bad_len), FAKE, ws,
+                                   0) == -3
+    bad_ring = g._CCache(FAKE + 2, FAKE, 2)
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 2, 16, FAKE, P(bad_ring), FAKE, ws,
+                                   0) == -3
+    # the workspace is still checked first
+    ok = g._CCache(FAKE, FAKE, 2)
+    assert lib.ngram_embed_prefill(P(c), P(T), FAKE, FAKE, 2, 16, FAKE, P(ok), FAKE, ws - 1,
+                                   0) == -4
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks every tensor before its address crosses the C ABI (no GPU needed:
+    dtype and shape are checked before the device). int64 token ids, torch's default integer
+    type, would otherwise be read as pairs of int32."""
+    torch = pytest.importorskip("torch")
+
+    class OnDevice:
+        """A host tensor that reports a CUDA device, so that the checks after the device
+        check of one argument are reached (every call below still fails a check before any
+        pointer is passed to the library)."""
+        def __init__(self, t):
+            self._t = t
+            self.is_cuda = True
+
+        def __getattr__(self, k):
+            v = getattr(self._t, k)
+            if k in ("long", "float", "int", "t", "__getitem__"):
+                return lambda *a: OnDevice(v(*a))
+            return v
+
+        def __getitem__(self, i):
+            return OnDevice(self._t[i])
+
+    _zeros = torch.zeros
+
+    def zeros(*a, **kw):
+        return OnDevice(_zeros(*a, **kw))
+
+    def tensor(*a, **kw):
+        return OnDevice(torch.tensor(*a, **kw))
+
+    def full(*a, **kw):
+        return OnDevice(torch.full(*a, **kw))
+
+    cfg = tiny_cfg()
+    E0 = zeros((1000, 64), dtype=torch.bfloat16)
+    E = [zeros((v, 16), dtype=torch.bfloat16) for v in cfg.V]
+    W = zeros((64, 64), dtype=torch.bfloat16)
+    tables = g.Tables(E0, E, W)
+    tok32 = zeros(16, dtype=torch.int32)
+    cu = tensor([0, 16], dtype=torch.int32)
+    out = zeros((16, 64), dtype=torch.bfloat16)
+    ws = zeros(g.ngram_embed_workspace_size(cfg, 16), dtype=torch.uint8)
+
+    def rejects(match, f, *a, **kw):
+        with pytest.raises(ValueError, match=match):
+            f(*a, **kw)
+
+    rejects("tokens must have dtype torch.int32", g.ngram_embed_prefill, cfg, tables,
+            tok32.long(), cu, out, ws)
+    rejects("cu_seqlens must have dtype", g.ngram_embed_prefill, cfg, tables, tok32,
+            cu.long(), out, ws)
+    rejects(r"out must have shape \(16, 64\)", g.ngram_embed_prefill, cfg, tables, tok32, cu,
+            out[:15], ws)
+    rejects("out must have dtype", g.ngram_embed_prefill, cfg, tables, tok32, cu,
+            out.float(), ws)
+    rejects("out must be contiguous", g.ngram_embed_prefill, cfg, tables, tok32, cu,
+            OnDevice(_zeros((64, 16), dtype=torch.bfloat16).t()), ws)
+    rejects("out must be on a CUDA", g.ngram_embed_prefill, cfg, tables, tok32, cu,
+            out._t, ws)
+    rejects(r"E\[2\] needs 6007 rows", g.ngram_embed_prefill, cfg,
+            g.Tables(E0, E[:2] + [E[2][:100]] + E[3:], W), tok32, cu, out, ws)
+    rejects(r"W must have shape \(64, 64\)", g.ngram_embed_prefill, cfg,
+            g.Tables(E0, E, W[:32]), tok32, cu, out, ws)
+    rejects("E0 must have dtype", g.ngram_embed_project, cfg, g.Tables(E0.float(), E, W),
+            zeros((16, 4), dtype=torch.int32), tok32, out)
+    rejects("idx needs at least 64 elements", g.ngram_embed_project, cfg, tables,
+            zeros(63, dtype=torch.int32), tok32, out)
+    rejects("tok needs at least 16 elements", g.ngram_embed_project, cfg, tables,
+            zeros(64, dtype=torch.int32), tok32[:8], out)
+    rejects("idx needs at least", g.ngram_embed_hash, cfg, tok32, cu,
+            zeros(10, dtype=torch.int32))
+    # decode: per-sequence arrays must have one entry per cache slot
+    cache = g.Cache(zeros((4, 2), dtype=torch.int32), zeros(4, dtype=torch.int64))
+    new = zeros((4, 5), dtype=torch.int32)
+    n4 = full((4,), 5, dtype=torch.int32)
+    dout = zeros((4, 5, 64), dtype=torch.bfloat16)
+    rejects(r"new_tokens must have shape \(4, \*\)", g.ngram_embed_decode, cfg, tables, cache,
+            new[:3], n4, dout, ws)
+    rejects(r"n_new must have shape \(4,\)", g.ngram_embed_decode, cfg, tables, cache, new,
+            n4[:2], dout, ws)
+    rejects(r"n_commit must have shape \(4,\)", g.ngram_embed_decode, cfg, tables, cache, new,
+            n4, dout, ws, n_commit=n4[:3])
+    rejects(r"out must have shape \(4, 5, 64\)", g.ngram_embed_decode, cfg, tables, cache, new,
+            n4, dout[:, :4], ws)
+    rejects(r"cache.len must have dtype torch.int64", g.ngram_embed_decode, cfg, tables,
+            g.Cache(cache.ring, cache.len.int()), new, n4, dout, ws)
+    rejects(r"cache.ring must have shape \(4, 2\)", g.ngram_embed_decode, cfg, tables,
+            g.Cache(cache.ring[:, :1], cache.len), new, n4, dout, ws)
+    rejects("cu_seqlens must have cache.nseq", g.ngram_cache_init, cfg, cache, tok32, cu)
+    rejects(r"n_accept must have shape \(4,\)", g.ngram_cache_commit, cfg, cache, new, n4[:1])
+    rejects("one slot per sequence", g.ngram_embed_prefill, cfg, tables, tok32, cu, out, ws,
+            cache=cache)
+    rejects(r"slots must have shape \(4,\)", g.ngram_embed_decode_rows, cfg, tables, cache,
+            new, n4, dout, ws, slots=n4[:2])
+    rejects(r"dE\[0\] must have shape \(5003, 16\)", g.ngram_embed_backward, cfg, tables,
+            tok32, cu, out, None, [zeros((5003, 8))] * 4, None, ws)
+    rejects("dW must have dtype torch.float32", g.ngram_embed_backward, cfg, tables, tok32, cu,
+            out, None, None, W, ws)
+
+
+def test_lds_dma_m0_is_an_operand():
+    """The projection's LDS-DMA loads take their LDS address in m0 as an asm input operand
+    ("{m0}"), so the compiler writes m0 itself and keeps no other value there across them.
+    Checked on the gfx950 assembly of this repository's source: no reserved-register clobber
+    warning, every DMA load preceded by an m0 write and the hazard nop, and no instruction that
+    reads m0 for another purpose (movrel, sendmsg) in the projection kernels."""
+    from gram_embedding_layer_amd import build
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not installed")
+    cmd = [build.hipcc(), f"--offload-arch={build.ARCH}", "-O3", "-std=c++17",
+           "--cuda-device-only", "-S", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", f"-I{build.INCLUDE}", f"-I{build.CSRC}", "-o", "-",
+           os.path.join(build.CSRC, "project.hip")]
+    res = subprocess.run(cmd, capture_output=True, text=True, check=True)
+    assert "reserved registers" not in res.stderr
+    lines = [ln.strip() for ln in res.stdout.splitlines()]
+    dma = [i for i, ln in enumerate(lines) if ln.startswith("global_load_lds_dwordx4")]
+    assert dma, "no LDS-DMA loads found"
+    for i in dma:
+        assert lines[i - 1] == "s_nop 0", lines[i - 3:i + 1]
+        prev = [ln for ln in lines[max(0, i - 40):i] if "m0" in ln and not ln.startswith(";")]
+        # the compiler's own write of the operand (s_mov, or an address computed into m0)
+        assert prev and prev[-1].split()[0].startswith("s_") and \
+            prev[-1].split()[1].rstrip(",") == "m0", lines[i - 5:i + 1]
+    body = "\n".join(lines)
+    for op in ("s_movrel", "v_movrel", "s_sendmsg"):
+        assert op not in body, op

@@ -63,6 +63,17 @@ int main() {
   amp.amp = NGRAM_AMP_SCALE;
   amp.amp_scale = 8.0f;
   EXPECT(ngram::describe(&amp, &L) == NGRAM_OK && L.scale == 8.0f);
+  // the sentinel selects sqrt(D), computed on the library's side (D = 64: exactly 8)
+  amp.amp_scale = NGRAM_AMP_SCALE_SQRT_D;
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_OK && L.scale == 8.0f);
+  amp.D = 3072;
+  amp.K = 4;                       // S = 8: d = 384
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_OK && L.scale == __builtin_sqrtf(3072.0f) &&
+         L.scale > 55.42f && L.scale < 55.43f);
+  amp.D = 64;
+  amp.K = 2;
+  amp.amp_scale = -2.5f;           // any other finite factor is used as given
+  EXPECT(ngram::describe(&amp, &L) == NGRAM_OK && L.scale == -2.5f);
   amp.amp_scale = __builtin_nanf("");
   EXPECT(ngram::describe(&amp, &L) == NGRAM_EINVAL);
   amp.amp_scale = __builtin_inff();
