@@ -48,15 +48,55 @@ def rel_l2(out, ref):
     return float(np.linalg.norm(out - ref) / (n if n > 0 else 1.0))
 
 
+# Element by element (bf16 outputs): the kernel computes v = (E_0 row + product) * scale in
+# fp32 and rounds v once to bf16, which moves it by at most half an ulp: for v in
+# [2^e, 2^(e+1)) an ulp of bf16's 8 significant bits is 2^(e-7), so |out - v| <= 2^-8 |v|.
+# The fp32 accumulation of a 3072-term product (MFMA products are exact; the sums round) is
+# about 2^-24 * sqrt(3072 / 16) * |acc| ~ 1e-5 of the output's RMS, so |v - ref| is bounded by
+# ELEM_C * rms(ref) with a tenfold margin, and
+#     |out - ref| <= 2^-8 |ref| + ELEM_C * rms(ref)     (rms over the compared values).
+ELEM_C = 1e-4
+# Per row: the relative L2 of each row alone; a row error that a norm over many rows would
+# dilute shows here. The element bound above caps it at about 2^-8; bf16 rounding alone gives
+# ~1.6e-3 on average.
+ROW_TOL = {"f32": 1e-5, "bf16": 3e-3}
+
+
+def row_rel_l2(out, ref):
+    """Relative L2 error of every row (rows with a zero reference use norm 1)."""
+    out2 = out.reshape(-1, out.shape[-1]) if out.ndim else out
+    ref2 = ref.reshape(-1, ref.shape[-1]) if ref.ndim else ref
+    num = np.sqrt(np.sum((out2 - ref2) ** 2, axis=1))
+    den = np.sqrt(np.sum(ref2 * ref2, axis=1))
+    return num / np.where(den > 0, den, 1.0)
+
+
 def assert_close(out, ref, dtype, what=""):
+    """Relative L2 over everything compared (the targets in TOL), relative L2 of every row
+    (ROW_TOL), every element within the bf16 rounding bound (bf16), and max |error|."""
     rl2_tol, abs_tol = TOL[dtype]
-    rl2 = rel_l2(out, ref)
-    mabs = float(np.max(np.abs(out - ref))) if out.size else 0.0
-    print(f"  {what}: rel_l2={rl2:.3e} max_abs={mabs:.3e}", flush=True)
+    assert out.shape == ref.shape, (what, out.shape, ref.shape)
     assert np.all(np.isfinite(out))
+    err = np.abs(out - ref)
+    rl2 = rel_l2(out, ref)
+    mabs = float(err.max()) if out.size else 0.0
+    rows = row_rel_l2(out, ref) if out.size else np.zeros(0)
+    rmax = float(rows.max()) if rows.size else 0.0
+    msg = f"  {what}: rel_l2={rl2:.3e} max_abs={mabs:.3e} worst_row_rel_l2={rmax:.3e}"
+    if dtype == "bf16" and out.size:
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        excess = err - (2.0 ** -8 * np.abs(ref) + ELEM_C * rms)
+        worst = int(np.argmax(excess))
+        msg += f" elems={out.size} worst_elem_margin={float(excess.flat[worst]):.2e}"
+    print(msg, flush=True)
     assert rl2 <= rl2_tol, (what, rl2)
     if abs_tol is not None:
         assert mabs <= abs_tol, (what, mabs)
+    assert rmax <= ROW_TOL[dtype], (what, "row", int(np.argmax(rows)), rmax)
+    if dtype == "bf16" and out.size:
+        assert float(excess.flat[worst]) <= 0.0, (
+            what, "element", np.unravel_index(worst, out.shape), float(out.flat[worst]),
+            float(ref.flat[worst]))
 
 
 def packed(seqs):

@@ -8,7 +8,7 @@ tests; gradients relative L2 <= 1e-5 (fp32 sums of exact inputs). Covered: every
 small cases (ragged, empty and one-token sequences, N = 1, 2, 3, 5, fp32 and bf16), ids
 outside the vocabulary, both amplifications, decode with the N-gram cache (one-shot and
 row windows), the stand-alone gather, the backward, and the ~30B-parameter basic-form layer
-at its 64K-token shape (sampled rows)."""
+at its 64K-token shape (every row)."""
 import numpy as np
 import pytest
 
@@ -221,10 +221,10 @@ def test_basic_backward_matches_oracle(lib, name, w, lengths, scale):
         assert r <= 1e-5, (nm, r)
 
 
-def test_basic_30b_prefill_sampled(lib):
+def test_basic_30b_prefill_every_row(lib):
     """The basic form with ~30B parameters (3 tables of 3.2M x 3072 bf16, 59 GB) at the
-    64K-token shape: hash indices of every position bit for bit, embeddings of every
-    sequence start and end plus 1024 seeded rows."""
+    64K-token shape: hash indices of every position bit for bit, every embedding row element
+    by element."""
     w = WL.workload("prefill_64k_basic_30b")
     E0, E, _ = WL.device_tables(w)
     cfg = cfg_of(w)
@@ -234,11 +234,9 @@ def test_basic_30b_prefill_sampled(lib):
     idx = oracle.hash_indices(w.V0, w.N, 1, w.V, tokens, cu)
     _, got_idx = ws_indices(ws, cfg, T)
     np.testing.assert_array_equal(got_idx, idx)
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([cu[:-1], cu[:-1] + 1, cu[1:] - 1,
-                                     rng.choice(T, 1024, replace=False)]))
-    got = to_f64(out[torch.as_tensor(rows, device="cuda")])
-    assert_close(got, expected(w, E0, E, tokens, idx, rows), "bf16", "basic 30b")
+    got = to_f64(out)
+    del out
+    assert_close(got, expected(w, E0, E, tokens, idx, np.arange(T)), "bf16", "basic 30b")
     assert g.ngram_embed_read_error_flag(ws) == 0
-    del E0, E, out, ws
+    del E0, E, ws, got
     torch.cuda.empty_cache()

@@ -289,3 +289,65 @@ def test_decode_graph_replays(lib):
         del junk
         assert torch.equal(outs.view(torch.int16), ref.view(torch.int16)), rep
         assert torch.equal(cache.ring, ref_ring) and torch.equal(cache.len, ref_len), rep
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 6])
+def test_prefill_fills_the_cache(lib, N):
+    """ngram_embed_prefill with a cache fills it in the same call exactly as ngram_cache_init
+    does (lengths and the last N-1 ids, pad id 0 before short sequences, empty sequences
+    included), and its outputs are those of the call without a cache; decoding on from that
+    cache follows the decode oracle."""
+    w = decode_workload(N=N, K=1, D=480)       # S = 0, 1, 3, 5 all divide 480
+    cfg = cfg_of(w)
+    E0, E, W = WL.host_tables(w)
+    E0, E, W = E0.cuda(), [e.cuda() for e in E], W.cuda()
+    tables = g.Tables(E0, E, W)
+    rng = np.random.default_rng(N)
+    hists = [rng.integers(0, w.V0, size=L).astype(np.int32) for L in (0, 1, N - 1, 37, 2, 0, 300)]
+    tokens, cu = packed(hists)
+    T = len(tokens)
+    outs, caches = [], []
+    for with_cache in (False, True):
+        cache = g.Cache(torch.full((len(hists), max(N - 1, 0)), -5, dtype=torch.int32,
+                                   device="cuda"),
+                        torch.full((len(hists),), -9, dtype=torch.int64, device="cuda"))
+        out = torch.empty((T, w.D), dtype=torch.bfloat16, device="cuda")
+        ws = g.alloc_workspace(cfg, T)
+        g.ngram_embed_prefill(cfg, tables, dev(tokens), dev(cu), out, ws,
+                              cache=cache if with_cache else None)
+        torch.cuda.synchronize()
+        assert g.ngram_embed_read_error_flag(ws) == 0
+        outs.append(out)
+        caches.append(cache)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = init_cache(cfg, hists)
+    assert torch.equal(caches[1].len, ref.len)
+    assert torch.equal(caches[1].ring, ref.ring)
+    check_cache(cfg, caches[1], [list(h) for h in hists])
+    # one decode step on the prefill-filled cache against the oracle
+    nseq, tmax = len(hists), 5
+    new = rng.integers(0, w.V0, size=(nseq, tmax)).astype(np.int32)
+    n_new = np.full(nseq, tmax, np.int32)
+    ws = g.alloc_workspace(cfg, nseq * tmax)
+    out = decode_step(cfg, tables, caches[1], new, n_new, n_new, ws, torch.bfloat16)
+    orc = oracle.DecodeOracle(w.V0, w.D, w.N, w.K, w.V, hists)
+    _, embs = orc.step([list(r) for r in new], device_fetch(E0, E), w_blocks(W, w.S))
+    assert_close(to_f64(out).reshape(nseq * tmax, w.D), np.concatenate(embs), "bf16",
+                 f"decode after prefill N={N}")
+
+
+def test_prefill_cache_only_when_no_tokens(lib):
+    """A batch of empty sequences still fills the cache (lengths 0, pad ids)."""
+    w = decode_workload(N=3, K=2, D=256)
+    cfg = cfg_of(w)
+    E0, E, W = WL.host_tables(w)
+    tables = g.Tables(E0.cuda(), [e.cuda() for e in E], W.cuda())
+    cache = g.Cache(torch.full((3, 2), 4, dtype=torch.int32, device="cuda"),
+                    torch.full((3,), 11, dtype=torch.int64, device="cuda"))
+    out = torch.empty((0, w.D), dtype=torch.bfloat16, device="cuda")
+    ws = g.alloc_workspace(cfg, 0)
+    g.ngram_embed_prefill(cfg, tables, torch.zeros(0, dtype=torch.int32, device="cuda"),
+                          dev(np.zeros(4, np.int32)), out, ws, cache=cache)
+    torch.cuda.synchronize()
+    assert int(cache.len.abs().sum().item()) == 0
+    assert int(cache.ring.abs().sum().item()) == 0

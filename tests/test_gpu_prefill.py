@@ -2,9 +2,10 @@
 ABI, against the CPU oracle on the same seeded inputs.
 
 Hash indices must match bit for bit; gathered rows byte for byte; embeddings within the
-tolerances in gpu_helpers.TOL. Small cases run the oracle on every row (several tiles and a
-ragged tail); the full-size workloads check every index and a sample of embedding rows
-(sequence starts, where the pad id enters, plus seeded random rows)."""
+tolerances in gpu_helpers (relative L2 overall and per row, and for bf16 every element within
+the one-rounding bound). Every case compares every row: the small ones (several tiles and a
+ragged tail, each tile shape of the matrix-core kernel) and the full-size workloads in the
+launch configuration the benchmark times."""
 import json
 import os
 
@@ -149,12 +150,8 @@ def test_prefill_parity_small(lib, name, w, lengths):
     tokens, cu = packed(seqs)
     T = len(tokens)
     out, ws = run_prefill(cfg, E0, E, W, tokens, cu, E0.dtype)
-    rows = np.arange(T) if T <= 3000 else np.unique(np.concatenate(
-        [cu[:-1][np.diff(cu) > 0], cu[:-1][np.diff(cu) > 0] + 1, cu[1:] - 1,
-         np.random.default_rng(0).choice(T, 1500, replace=False)]))
-    rows = rows[(rows >= 0) & (rows < T)]
-    _, e = oracle_rows(w, E0, E, W, tokens, cu, rows)
-    assert_close(to_f64(out)[rows], e, w.dtype, name)
+    _, e = oracle_rows(w, E0, E, W, tokens, cu, np.arange(T))     # every row
+    assert_close(to_f64(out), e, w.dtype, name)
     assert g.ngram_embed_read_error_flag(ws) == 0
 
 
@@ -201,22 +198,24 @@ def test_prefill_parity_workload(lib, request, name):
     # every index, bit for bit (prefill leaves them in the workspace)
     _, idx_off = g.ngram_embed_workspace_layout(cfg, T)
     got_idx = ws[idx_off:idx_off + T * w.S * 4].view(torch.int32).cpu().numpy().reshape(T, w.S)
-    rng = np.random.default_rng(1)
-    starts = cu[:-1]
-    rows = np.unique(np.concatenate([starts, starts + 1, starts + 2, cu[1:] - 1,
-                                     rng.choice(T, 512, replace=False)]))
-    idx, e = oracle_rows(w, E0, E, W, tokens, cu, rows)
+    # every row of the launch the benchmark times, element by element (the oracle contracts
+    # the whole batch in float64)
+    idx, e = oracle_rows(w, E0, E, W, tokens, cu, np.arange(T))
     np.testing.assert_array_equal(got_idx, idx)
-    assert_close(to_f64(out[torch.as_tensor(rows, device="cuda")]), e, "bf16", name)
-    # the stand-alone gather agrees byte for byte with torch indexing on sampled rows
+    got = to_f64(out)
+    del out
+    assert_close(got, e, "bf16", name)
+    del got, e
+    # the stand-alone gather agrees byte for byte with torch indexing on every row
     G = torch.empty((T, w.D), dtype=torch.bfloat16, device="cuda")
     g.ngram_embed_gather(cfg, g.Tables(E0, E, W), ws[idx_off:].view(torch.int32), G)
     torch.cuda.synchronize()
-    fetch = device_fetch(E0, E)
-    want_g = np.concatenate([fetch(s, idx[rows, s]) for s in range(w.S)], axis=1)
-    np.testing.assert_array_equal(to_f64(G[torch.as_tensor(rows, device="cuda")]), want_g)
+    for s in range(w.S):
+        want = E[s].index_select(0, torch.as_tensor(idx[:, s], device="cuda"))
+        assert torch.equal(G[:, s * w.d:(s + 1) * w.d].view(torch.int16),
+                           want.view(torch.int16)), s
     assert g.ngram_embed_read_error_flag(ws) == 0
-    del E0, E, W, out, ws, G
+    del E0, E, W, ws, G
     torch.cuda.empty_cache()
 
 
