@@ -29,11 +29,14 @@ __all__ = [
     "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
     "ngram_embed_clear_error_flag", "ngram_embed_status_string", "alloc_workspace",
     "ngram_embed_backward_workspace_size", "ngram_embed_backward", "alloc_backward_workspace",
+    "ngram_embed_decode_noalloc", "NGRAM_ESCRATCH", "NGRAM_NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libngram_embed.so")
 
 NGRAM_OK = 0
+NGRAM_ESCRATCH = -7                       # the step needs more than the fixed scratch
+NGRAM_NOALLOC_SCRATCH_BYTES = 16 << 20    # scratch of ngram_embed_decode_noalloc, per GPU
 NGRAM_F32, NGRAM_BF16 = 0, 1
 NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS, NGRAM_FLAG_BAD_COUNT = 1, 2, 4
 NGRAM_FLAG_BAD_SLOT = 8
@@ -117,6 +120,8 @@ def load():
         "ngram_embed_backward_workspace_size": (SZ, [cfgp, I64]),
         "ngram_embed_backward": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, P,
                                                 ctypes.POINTER(P), P, P, SZ, P]),
+        "ngram_embed_decode_noalloc": (ctypes.c_int, [cfgp, tabp, cachep, P, P, I32, P, P, P,
+                                                      P]),
         "ngram_embed_read_error_flag": (ctypes.c_int, [P, ctypes.POINTER(I32), P]),
         "ngram_embed_clear_error_flag": (ctypes.c_int, [P, P]),
         "ngram_embed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -523,6 +528,27 @@ def ngram_embed_decode(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_
         ctypes.byref(c), ctypes.byref(t), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
         int(new_tokens.shape[1]), _ptr(n_commit), _ptr(out), _ptr(ws),
         int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def ngram_embed_decode_noalloc(cfg: Config, tables: Tables, cache: Cache, new_tokens, n_new,
+                               out, n_commit=None, err_flags=None, stream=None):
+    """ngram_embed_decode without a workspace: the step's scratch is the library's fixed
+    per-GPU array (for callers that cannot allocate; calls overlapping on one GPU race).
+    err_flags: optional device int32 the step's flags are OR-ed into."""
+    fn = "ngram_embed_decode_noalloc"
+    _cache_arg(fn, cfg, cache)
+    _step_args(fn, cfg, cache.nseq, new_tokens, (n_new, n_commit), ("n_new", "n_commit?"))
+    if _shapes_ok(cfg):
+        _tables_arg(fn, cfg, tables)
+        _out_arg(fn, cfg, out, (cache.nseq, new_tokens.shape[1], cfg.D))
+    _arg(fn, "err_flags", err_flags, _i32(), min_numel=1, optional=True)
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    cc = cache._c()
+    _check(fn, load().ngram_embed_decode_noalloc(
+        ctypes.byref(c), ctypes.byref(t), ctypes.byref(cc), _ptr(new_tokens), _ptr(n_new),
+        int(new_tokens.shape[1]), _ptr(n_commit), _ptr(out), _ptr(err_flags),
+        _stream(stream)))
 
 
 def _layer_args(fn, cfg, tables, outs, out_shape):

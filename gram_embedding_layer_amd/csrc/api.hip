@@ -1,6 +1,7 @@
 // C-ABI entry points: host validation, then stream-ordered kernel launches.
 // Declarations and the contract of every function: include/ngram_embed.h.
 #include <algorithm>
+#include <atomic>
 
 #include "kernels.h"
 
@@ -142,6 +143,40 @@ int prefill_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables
                         st);
 }
 
+// Host checks of a decode step's pointers (the config, counts and scratch are checked by the
+// caller).
+int check_decode(const LayerDesc& L, const ngram_embed_tables* tables, int32_t nlayers,
+                 const ngram_cache* cache, const int32_t* new_tokens, const int32_t* n_new,
+                 const int32_t* n_commit, void* const* outs) {
+  const int rc = check_layers(L, tables, nlayers, outs);
+  if (rc != NGRAM_OK) return rc;
+  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
+      !ngram::aligned(n_new, 4))
+    return NGRAM_EALIGN;
+  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
+  if (n_commit != nullptr && !ngram::aligned(n_commit, 4)) return NGRAM_EALIGN;
+  return NGRAM_OK;
+}
+
+// The launches of a decode step, with the step's scratch (tokens, indices, unrounded rows)
+// laid out by `lay` from `base` and the flags OR-ed into `flags` (may be null).
+int decode_launch(const LayerDesc& L, const ngram_embed_tables* tables, int32_t nlayers,
+                  ngram_cache* cache, const int32_t* new_tokens, const int32_t* n_new,
+                  int32_t tmax, const int32_t* n_commit, void* const* outs, char* base,
+                  const ngram::WsLayout& lay, int32_t* flags, hipStream_t st) {
+  const int64_t rows = int64_t(cache->nseq) * tmax;
+  int32_t* tok = reinterpret_cast<int32_t*>(base + lay.tok_off);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + lay.idx_off);
+  // hash (and commit, when asked) in one kernel; the projection reads only tok/idx, so the
+  // cache may advance before it runs
+  ngram::DecodeArgs d{cache->ring, cache->len, nullptr, cache->nseq, new_tokens, n_new,
+                      n_commit, cache->nseq, tmax, 0, tmax, -1, tok, idx, flags};
+  const int rc = hip_status(ngram::launch_hash_decode(L, d, st));
+  if (rc != NGRAM_OK) return rc;
+  return project_layers(L, tables, nlayers, idx, tok, rows, outs, base, lay, ngram::RowMap{},
+                        st);
+}
+
 int decode_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                 int32_t nlayers, ngram_cache* cache, const int32_t* new_tokens,
                 const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
@@ -155,23 +190,44 @@ int decode_impl(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
   ngram::WsLayout lay;
   if ((rc = check_ws(L, ws, ws_bytes, rows, &lay)) != NGRAM_OK) return rc;
   if (rows == 0) return NGRAM_OK;
-  if ((rc = check_layers(L, tables, nlayers, outs)) != NGRAM_OK) return rc;
-  if (!ngram::aligned(cache->len, 8) || !ngram::aligned(new_tokens, 4) ||
-      !ngram::aligned(n_new, 4))
-    return NGRAM_EALIGN;
-  if (L.N > 1 && !ngram::aligned(cache->ring, 4)) return NGRAM_EALIGN;
-  if (n_commit != nullptr && !ngram::aligned(n_commit, 4)) return NGRAM_EALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  int32_t* tok = reinterpret_cast<int32_t*>(w + lay.tok_off);
-  int32_t* idx = reinterpret_cast<int32_t*>(w + lay.idx_off);
-  // hash (and commit, when asked) in one kernel; the projection reads only tok/idx, so the
-  // cache may advance before it runs
-  ngram::DecodeArgs d{cache->ring, cache->len, nullptr, cache->nseq, new_tokens, n_new,
-                      n_commit, cache->nseq, tmax, 0, tmax, -1, tok, idx, ws_flags(ws)};
-  rc = hip_status(ngram::launch_hash_decode(L, d, st));
+  rc = check_decode(L, tables, nlayers, cache, new_tokens, n_new, n_commit, outs);
   if (rc != NGRAM_OK) return rc;
-  return project_layers(L, tables, nlayers, idx, tok, rows, outs, ws, lay, ngram::RowMap{}, st);
+  return decode_launch(L, tables, nlayers, cache, new_tokens, n_new, tmax, n_commit, outs,
+                       static_cast<char*>(ws), lay, ws_flags(ws),
+                       static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ fixed scratch
+// The scratch of ngram_embed_decode_noalloc: one array per GPU, declared in device memory
+// (the code object's loader places it when the library is loaded on a device; it lives until
+// the process ends). In host code `scratch` names a host-side stand-in, not the device
+// array: only the address hipGetSymbolAddress returns for the current device is ever passed
+// to a kernel.
+static __device__ __align__(256) char scratch[NGRAM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<char*> g_scratch[kMaxScratchDevices];   // device address of `scratch`, per GPU
+
+// The current device's scratch (looked up once per device; the stream must be on it).
+int device_scratch(hipStream_t st, char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NGRAM_EHIP;
+  if (st != nullptr) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess) return NGRAM_EHIP;
+    if (int(sdev) != dev) return NGRAM_EINVAL;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return NGRAM_EINVAL;
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return NGRAM_EHIP;
+    p = static_cast<char*>(q);
+    g_scratch[dev].store(p, std::memory_order_release);   // the same address if two race
+  }
+  *out = p;
+  return NGRAM_OK;
 }
 
 }  // namespace
@@ -526,6 +582,33 @@ int ngram_embed_clear_error_flag(void* ws, void* stream) {
   return hip_status(ngram::launch_clear_flags(ws_flags(ws), static_cast<hipStream_t>(stream)));
 }
 
+int ngram_embed_decode_noalloc(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                               ngram_cache* cache, const int32_t* new_tokens,
+                               const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
+                               void* out, int32_t* err_flags, void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (cache == nullptr || cache->nseq < 0) return NGRAM_EINVAL;
+  if (tmax < 1 || tmax > NGRAM_MAX_DECODE_TOKENS) return NGRAM_EINVAL;
+  const int64_t rows = int64_t(cache->nseq) * tmax;
+  ngram::WsLayout lay;
+  if (!ngram::ws_layout(L, rows, &lay)) return NGRAM_EINVAL;
+  if (lay.total > NGRAM_NOALLOC_SCRATCH_BYTES) return NGRAM_ESCRATCH;
+  if (rows == 0) return NGRAM_OK;
+  void* outs[1] = {out};
+  rc = check_decode(L, tables, 1, cache, new_tokens, n_new, n_commit, outs);
+  if (rc != NGRAM_OK) return rc;
+  if (err_flags != nullptr && !ngram::aligned(err_flags, 4)) return NGRAM_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = nullptr;
+  if ((rc = device_scratch(st, &base)) != NGRAM_OK) return rc;
+  // nothing in the scratch is read before this step writes it (tokens and indices by the
+  // hash kernel, the unrounded rows by the projection), so no clearing is needed
+  return decode_launch(L, tables, 1, cache, new_tokens, n_new, tmax, n_commit, outs, base,
+                       lay, err_flags, st);
+}
+
 const char* ngram_embed_status_string(int status) {
   switch (status) {
     case NGRAM_OK: return "ok";
@@ -535,6 +618,8 @@ const char* ngram_embed_status_string(int status) {
     case NGRAM_EWORKSPACE: return "workspace missing, misaligned or too small";
     case NGRAM_EOVERFLOW: return "V0 * max V_{n,k} exceeds the exact 64-bit hash range";
     case NGRAM_EHIP: return "HIP runtime error at launch";
+    case NGRAM_ESCRATCH:
+      return "the step needs more than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -30,7 +30,8 @@
  *  - N = 1 is accepted: there are no sub-tables and e_i = E_0(t_i).
  *  - All matrices are row-major. "device" pointers are HIP device memory, "host" pointers
  *    are ordinary host memory read only during the call. The library allocates no memory
- *    and keeps no state between calls; the caller owns every buffer.
+ *    and keeps no state between calls; the caller owns every buffer (the one exception is
+ *    the fixed scratch array of ngram_embed_decode_noalloc, declared by the library).
  *  - Every entry point that takes a stream only enqueues work on that stream (a hipStream_t,
  *    or NULL for the null stream) and returns without waiting, except
  *    ngram_embed_read_error_flag, which waits for the stream.
@@ -58,7 +59,9 @@ enum {
   NGRAM_EALIGN = -3,     /* a required pointer is NULL or misaligned */
   NGRAM_EWORKSPACE = -4, /* workspace missing, misaligned or too small */
   NGRAM_EOVERFLOW = -5,  /* V0 * max V_{n,k} does not fit the exact 64-bit hash */
-  NGRAM_EHIP = -6        /* the HIP runtime reported an error at launch */
+  NGRAM_EHIP = -6,       /* the HIP runtime reported an error at launch */
+  NGRAM_ESCRATCH = -7    /* the call needs more than the fixed scratch of
+                            ngram_embed_decode_noalloc (NGRAM_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* dtype of E_0, E_{n,k}, W and of every output */
@@ -335,6 +338,28 @@ int ngram_hash_stats(int64_t V0, int32_t n, const int32_t* tokens, const int32_t
                      int32_t nseq, int64_t ntok, const int64_t* vocab, int32_t nvocab,
                      int64_t* rows, int64_t* distinct, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* ---------------------------------------------------------------- allocation-free decode
+ * For callers that cannot allocate device memory or bring a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The same step as
+ * ngram_embed_decode (same kernels, same output bits, same cache update), with the scratch
+ * that the workspace would hold (each row's E_0 token and hash indices, and the unrounded
+ * rows of NGRAM_AMP_LAYERNORM) in a fixed array of NGRAM_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library declares statically: each GPU the library runs on holds one copy
+ * until the process ends. The call allocates nothing; it needs
+ * ngram_embed_workspace_size(cfg, cache->nseq * tmax) <= NGRAM_NOALLOC_SCRATCH_BYTES (for
+ * example 256 sequences x 5 ids of a 12-sub-table layer take 67 KB, 15.8 MB with the layer
+ * normalisation at D = 3072), else it returns NGRAM_ESCRATCH and enqueues nothing.
+ * err_flags: device int32 the step's flags are OR-ed into, or NULL. `stream` must belong to
+ * the current device (NGRAM_EINVAL otherwise). Every call on one GPU uses that GPU's one
+ * array and leaves its contents there: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller. Other arguments as in
+ * ngram_embed_decode. */
+#define NGRAM_NOALLOC_SCRATCH_BYTES (16u << 20)
+int ngram_embed_decode_noalloc(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                               ngram_cache* cache, const int32_t* new_tokens,
+                               const int32_t* n_new, int32_t tmax, const int32_t* n_commit,
+                               void* out, int32_t* err_flags, void* stream);
 
 /* ---------------------------------------------------------------- errors
  * Wait for `stream`, then copy the workspace's error flags to *flags (host). */

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "ngram_cache_commit", "ngram_embed_backward",
               "ngram_embed_backward_workspace_size"):
         assert n in names
-    assert len(names) == 21
+    assert len(names) == 22
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -59,7 +59,7 @@ def tiny_cfg(**kw):
 
 def test_status_strings(lib):
     assert g.ngram_embed_status_string(0) == "ok"
-    for s in range(-6, 0):
+    for s in range(-7, 0):
         assert g.ngram_embed_status_string(s) != "unknown status"
     assert g.ngram_embed_status_string(-99) == "unknown status"
 
@@ -477,3 +477,35 @@ def test_lds_dma_m0_is_an_operand():
     body = "\n".join(lines)
     for op in ("s_movrel", "v_movrel", "s_sendmsg"):
         assert op not in body, op
+
+
+def test_noalloc_decode_rejects_before_any_device_call(lib):
+    """The allocation-free decode checks its sizes against the fixed scratch (and every
+    argument) on the host before touching the device."""
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    P = ctypes.byref
+    per_row = 4 + 4 * cfg.S              # token and indices: 20 bytes per row
+    big = g._CCache(FAKE, FAKE, (g.NGRAM_NOALLOC_SCRATCH_BYTES // per_row) // 8 + 64)
+    assert lib.ngram_embed_decode_noalloc(P(c), P(T), P(big), FAKE, FAKE, 8, None, FAKE, None,
+                                          0) == g.NGRAM_ESCRATCH
+    assert g.ngram_embed_status_string(g.NGRAM_ESCRATCH) != "unknown status"
+    # the layer normalisation keeps fp32 rows: 64 columns x 4 bytes more per row
+    ln = tiny_cfg(amp="layernorm")
+    cl, keep3 = ln._c()
+    mid = g._CCache(FAKE, FAKE, (g.NGRAM_NOALLOC_SCRATCH_BYTES // (per_row + 256)) // 8 + 64)
+    assert lib.ngram_embed_decode_noalloc(P(cl), P(T), P(mid), FAKE, FAKE, 8, None, FAKE,
+                                          None, 0) == g.NGRAM_ESCRATCH
+    small = g._CCache(FAKE, FAKE, 4)
+    assert lib.ngram_embed_decode_noalloc(P(c), P(T), P(small), FAKE, FAKE, 9, None, FAKE,
+                                          None, 0) == -1                   # tmax > 8
+    assert lib.ngram_embed_decode_noalloc(P(c), P(T), P(small), FAKE + 2, FAKE, 5, None, FAKE,
+                                          None, 0) == -3                   # new_tokens
+    assert lib.ngram_embed_decode_noalloc(P(c), P(T), P(small), FAKE, FAKE, 5, None, FAKE,
+                                          FAKE + 1, 0) == -3               # err_flags
+    assert lib.ngram_embed_decode_noalloc(P(c), None, P(small), FAKE, FAKE, 5, None, FAKE,
+                                          None, 0) == -3                   # no tables
+    empty = g._CCache(FAKE, FAKE, 0)
+    assert lib.ngram_embed_decode_noalloc(P(c), P(T), P(empty), FAKE, FAKE, 5, None, FAKE,
+                                          None, 0) == 0
