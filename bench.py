@@ -30,9 +30,14 @@ sys.path.insert(0, ROOT)
 METRIC = "N-gram embed tokens/sec + achieved HBM GB/s (64K-tok prefill, spec decode)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector (the fp32 configuration's FMA path)
 WORKLOAD = "prefill_64k_30b"
 DECODE_WORKLOAD = "decode_spec5_30b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_64k_30b.txt")
+TRAFFIC_DECODE = os.path.join(ROOT, "profiles", "traffic_decode_spec5_30b.txt")
+TRAFFIC_BASIC = os.path.join(ROOT, "profiles", "traffic_prefill_64k_basic_30b.txt")
+# the three smaller configurations, timed as parity-sized calls of the same path
+CONFIG_LEGS = (("tiny_f32", 100), ("bf16_d1024", 20), ("bf16_d2048_n5k4", 20))
 
 
 def log(msg):
@@ -44,14 +49,15 @@ def source_digest(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def counter_traffic(kernel, source):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy of known size),
-    or None when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def counter_traffic(kernel, source, path=None):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary (default
+    the prefill one; FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy of
+    known size), or None when it is missing or was taken on a different kernel source."""
+    path = TRAFFIC_FILE if path is None else path
+    if not os.path.exists(path):
         return None
     kv = {}
-    for ln in open(TRAFFIC_FILE):
+    for ln in open(path):
         # "key: value" lines; keys may hold a colon themselves ("project.hip sha256[:16]")
         if ": " in ln and not ln.lstrip().startswith(("#", "|", "-")):
             k, v = ln.rsplit(": ", 1)
@@ -64,8 +70,15 @@ def counter_traffic(kernel, source):
         return None
 
 
+def blas_info():
+    from threadpoolctl import threadpool_info
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    return blas, int(threads)
+
+
 def cpu_baseline(w, E0, E, W, batches):
-    """The oracle as it stands, on whole benchmark batches (each 8 x 8192 tokens). Table
+    """The oracle as it stands, on whole benchmark batches ([batch, seqlen] token ids). Table
     rows the oracle asks for are copied from HBM first (not timed)."""
     import numpy as np
     import torch
@@ -84,10 +97,11 @@ def cpu_baseline(w, E0, E, W, batches):
         idx = oracle.hash_indices(w.V0, w.N, w.K, w.V, tokens, cu)
         t_hash += time.perf_counter() - t0
         c0 = time.perf_counter()
-        rows = {-1: E0.index_select(0, torch.as_tensor(tokens.astype(np.int64), device="cuda"))
+        rows = {-1: E0.index_select(0, torch.as_tensor(tokens.astype(np.int64),
+                                                       device=E0.device))
                 .float().cpu().numpy().astype(np.float64)}
         for s in range(w.S):
-            r = torch.as_tensor(idx[:, s], device="cuda")
+            r = torch.as_tensor(idx[:, s], device=E0.device)
             rows[s] = E[s].index_select(0, r).float().cpu().numpy().astype(np.float64)
         t_copy += time.perf_counter() - c0
 
@@ -112,7 +126,8 @@ def cpu_baseline(w, E0, E, W, batches):
         "unit": "tokens/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"{len(batches)} benchmark batches of 8 x 8192 tokens ({n} tokens); "
+        "sample": (f"{len(batches)} benchmark batch(es) of {batches[0].shape[0]} x "
+                   f"{batches[0].shape[1]} tokens ({n} tokens); "
                    f"python-int hash {t_hash:.2f} s on 1 thread + float64 contraction "
                    f"{t_embed:.2f} s on {blas_threads} BLAS threads; host copy of the named "
                    f"table rows {t_copy:.2f} s not timed"),
@@ -124,21 +139,69 @@ def cpu_baseline(w, E0, E, W, batches):
     }
 
 
-def profile_launches(g, cfg, tables, toks, cu, idx, out, stream):
-    """A few launches of each kernel plus a plain device copy of known size, for rocprofv3
-    counter passes (the copy calibrates FETCH_SIZE / WRITE_SIZE)."""
+def profile_launches(g, WL, cfg, tables, toks, cu, idx, out, stream, dev):
+    """A few launches of each kernel, in a fixed order, plus a plain device copy of known size,
+    for rocprofv3 counter passes (the copy calibrates FETCH_SIZE / WRITE_SIZE). Prints the
+    launch order as one JSON line, so that a pass's dispatches can be told apart."""
+    import numpy as np
     import torch
     T, D = out.shape
+    w = WL.workload(WORKLOAD)
+    order = []
     G = torch.empty_like(out)
     src = torch.empty_like(out).fill_(1.0)
+    sums = torch.empty(T, dtype=torch.int32, device=dev)
+    uni = [torch.as_tensor(WL.uniform_ids(np.random.default_rng([7, p]), w.V0, (T,))).to(dev)
+           for p in range(3)]
+    idx_u = torch.empty_like(idx)
     for k in range(3):
-        g.ngram_embed_hash(cfg, toks[k % len(toks)], cu, idx, None, stream=stream)
-        g.ngram_embed_project(cfg, tables, idx, toks[k % len(toks)], out, stream=stream)
+        g.ngram_embed_hash(cfg, toks[k], cu, idx, None, stream=stream)
+        g.ngram_embed_project(cfg, tables, idx, toks[k], out, stream=stream)
         g.ngram_embed_gather(cfg, tables, idx, G, stream=stream)
+        g.ngram_embed_gather_checksum(cfg, tables, idx, sums, stream=stream)
         G.copy_(src)               # plain copy: T*D*2 bytes read, the same written
+        g.ngram_embed_hash(cfg, uni[k], cu, idx_u, None, stream=stream)
+        g.ngram_embed_gather_checksum(cfg, tables, idx_u, sums, stream=stream)
+        order += ["hash", "project", "gather", "gather_lds", "copy", "hash (uniform ids)",
+                  "gather_lds (uniform ids)"]
+    # decode: 256 sequences x 5 ids on caches of 8192-token histories (no commit), and the
+    # draft-phase calls of one row per sequence
+    wd = WL.workload(DECODE_WORKLOAD)
+    nseq, tmax = wd.batch, wd.decode_new
+    hist = torch.as_tensor(WL.token_batch(wd, purpose=0).reshape(-1)).to(dev)
+    hcu = torch.as_tensor(np.arange(nseq + 1, dtype=np.int32) * wd.seqlen).to(dev)
+    cache = g.Cache.empty(cfg, nseq, device=dev)
+    g.ngram_cache_init(cfg, cache, hist, hcu, stream=stream)
+    new = torch.as_tensor(WL.token_batch(wd, purpose=1, batch=nseq, seqlen=tmax)).to(dev)
+    n_new = torch.full((nseq,), tmax, dtype=torch.int32, device=dev)
+    n_one = torch.ones((nseq,), dtype=torch.int32, device=dev)
+    dout = torch.empty((nseq, tmax, D), dtype=torch.bfloat16, device=dev)
+    dws = g.alloc_workspace(cfg, nseq * tmax, device=dev)
+    for k in range(3):
+        g.ngram_embed_decode(cfg, tables, cache, new, n_new, dout, dws, stream=stream)
+        g.ngram_embed_decode_rows(cfg, tables, cache, new, n_one, dout, dws, row_begin=0,
+                                  row_end=1, stream=stream)
+        order += ["decode hash", "decode project (1280 rows)", "draft-row hash",
+                  "draft-row project (256 rows)"]
     torch.cuda.synchronize()
-    print(json.dumps({"profile": "launched hash, project, gather and a copy of "
-                      f"{T * D * 2} bytes, 3 times each"}), flush=True)
+    del G, src, dout, dws
+    # the basic form (Eq. 1) at ~30B parameters: Zipf and uniform ids
+    wb = WL.workload("prefill_64k_basic_30b")
+    cb = g.Config(wb.N, wb.K, wb.D, wb.dtype, wb.V0, list(wb.V), form="basic")
+    E0b, Eb, _ = WL.device_tables(wb, device=dev)
+    tb = g.Tables(E0b, Eb, None)
+    btok = torch.as_tensor(WL.token_batch(wb, purpose=0).reshape(-1)).to(dev)
+    bcu = torch.as_tensor(np.arange(wb.batch + 1, dtype=np.int32) * wb.seqlen).to(dev)
+    buni = torch.as_tensor(WL.uniform_ids(np.random.default_rng([8, 0]), wb.V0, (wb.T,))).to(dev)
+    bidx = torch.empty((wb.T, wb.S), dtype=torch.int32, device=dev)
+    bout = torch.empty((wb.T, wb.D), dtype=torch.bfloat16, device=dev)
+    for k in range(3):
+        for name, t in (("basic_sum", btok), ("basic_sum (uniform ids)", buni)):
+            g.ngram_embed_hash(cb, t, bcu, bidx, None, stream=stream)
+            g.ngram_embed_project(cb, tb, bidx, t, bout, stream=stream)
+            order += ["basic hash", name]
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": f"copy bytes {T * D * 2}", "order": order}), flush=True)
 
 
 def main():
@@ -158,6 +221,8 @@ def main():
                     help="skip the hash-collision statistics timing")
     ap.add_argument("--no-basic", action="store_true",
                     help="skip the basic-form (Eq. 1) prefill timing")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the three smaller configurations (tiny fp32, D=1024, D=2048)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-batches", type=int, default=4,
                     help="benchmark batches of 64K tokens the CPU oracle is timed on")
@@ -194,7 +259,7 @@ def main():
     idx_rot = [torch.empty((T, w.S), dtype=torch.int32, device=dev) for _ in range(nrot)]
     stream = torch.cuda.current_stream(dev)
     if args.profile:
-        profile_launches(g, cfg, tables, toks, cu, idx_rot[0], out, stream)
+        profile_launches(g, WL, cfg, tables, toks, cu, idx_rot[0], out, stream, dev)
         return
 
     def step(k, ev=None):
@@ -237,6 +302,9 @@ def main():
                 "traffic": traffic, "kernel": "proj_mfma_kernel<256, 0, 256>",
                 "kernel_us": round(t_proj * 1e6, 1),
                 "algorithmic_hbm_GBps": round(alg_bytes_proj / t_proj / 1e9, 1)}
+    if traffic is not None:
+        roofline["counter_hbm_GBps"] = round(traffic / t_proj / 1e9, 1)
+        roofline["counter_hbm_frac"] = round(traffic / t_proj / 1e9 / HBM_PEAK_GBS, 4)
     log(f"step {ms_per_step:.3f} ms: hash {t_hash*1e6:.1f} us, project {t_proj*1e6:.1f} us "
         f"({tflops:.0f} TFLOP/s)")
 
@@ -259,8 +327,11 @@ def main():
               "read_GBps": round(read_b / t_g / 1e9, 1),
               "read_write_GBps": round(2 * read_b / t_g / 1e9, 1),
               "frac_of_hbm_peak": round(2 * read_b / t_g / 1e9 / HBM_PEAK_GBS, 4),
+              "read_only_frac_of_hbm_peak": round(read_b / t_g / 1e9 / HBM_PEAK_GBS, 4),
               "bytes_read": read_b, "bytes_written": read_b,
-              "traffic": counter_traffic("gather", "gather.hip")}
+              "traffic": counter_traffic("gather", "gather.hip"),
+              "note": ("HBM -> HBM copy through registers (G written back); the projection "
+                       "gathers into LDS instead: see gather_lds")}
     log(f"gather {t_g*1e6:.1f} us: {2*read_b/t_g/1e9:.0f} GB/s read+write")
     # control: uniform ids (no Zipf repeats, so no reuse of rows within a batch)
     uni = [torch.as_tensor(WL.uniform_ids(np.random.default_rng([7, p]), w.V0, (T,))).to(dev)
@@ -281,6 +352,8 @@ def main():
     log(f"gather, uniform ids: {t_u*1e6:.1f} us: {2*read_b/t_u/1e9:.0f} GB/s read+write")
     del G, uni
 
+    gather_lds = bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, args.steps)
+
     amp = None
     if not args.no_amp:
         amp = bench_amplification(g, w, tables, toks, cu, dev, stream, args.steps)
@@ -291,7 +364,8 @@ def main():
 
     decode = None
     if not args.no_decode:
-        decode = bench_decode(g, WL, cfg, tables, dev, stream, args.decode_steps)
+        decode = bench_decode(g, WL, cfg, tables, dev, stream, args.decode_steps,
+                              with_cpu=not args.no_cpu_baseline)
 
     basic = None
     if not args.no_basic:
@@ -304,6 +378,10 @@ def main():
     stats = None
     if not args.no_stats:
         stats = bench_hash_stats(g, WL, dev, stream, min(args.steps, 10))
+
+    configs = None
+    if not args.no_configs:
+        configs = bench_configs(g, WL, dev, stream, with_cpu=not args.no_cpu_baseline)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -325,6 +403,8 @@ def main():
         "kernels_us": {"hash": round(t_hash * 1e6, 1), "project": round(t_proj * 1e6, 1)},
         "roofline": roofline,
         "gather": gather,
+        "gather_lds": gather_lds,
+        "configs": configs,
         "amplification": amp,
         "backward": backward,
         "decode": decode,
@@ -434,8 +514,28 @@ def bench_basic(g, WL, dev, stream, steps):
                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "kernel": "basic_sum_kernel<unsigned short, unsigned short>",
                         "bytes_per_token": per_tok}}
+    # control: uniform ids (rows repeat far less, so fewer reads hit in cache)
+    uni = [torch.as_tensor(WL.uniform_ids(np.random.default_rng([8, p]), w.V0, (T,))).to(dev)
+           for p in range(4)]
+    idx_u = [torch.empty((T, w.S), dtype=torch.int32, device=dev) for _ in range(4)]
+    for p in range(4):
+        g.ngram_embed_hash(cfg, uni[p], cu, idx_u[p], ws, stream=stream)
+    for k in range(3):
+        g.ngram_embed_project(cfg, tables, idx_u[k % 4], uni[k % 4], out, stream=stream)
+    (t_u,) = time_launches(lambda k, e: (g.ngram_embed_project(
+        cfg, tables, idx_u[k % 4], uni[k % 4], out, stream=stream), e[1].record(stream)),
+        stream, steps)
+    gbs_u = T * per_tok / t_u / 1e9
+    res["uniform_ids_control"] = {"sum_us": round(t_u * 1e6, 1), "achieved_GBps": round(gbs_u, 1),
+                                  "frac": round(gbs_u / HBM_PEAK_GBS, 4)}
+    traffic = counter_traffic("basic_sum", "basic.hip", TRAFFIC_BASIC)
+    res["roofline"]["traffic"] = traffic
+    if traffic is not None:
+        res["roofline"]["counter_hbm_GBps"] = round(traffic / t_sum / 1e9, 1)
+        res["roofline"]["counter_hbm_frac"] = round(traffic / t_sum / 1e9 / HBM_PEAK_GBS, 4)
     log(f"basic form: step {wall*1e6:.0f} us, hash {t_hash*1e6:.1f} us, sum {t_sum*1e6:.1f} us "
-        f"({gbs:.0f} GB/s)")
+        f"({gbs:.0f} GB/s); uniform ids {t_u*1e6:.1f} us ({gbs_u:.0f} GB/s)")
+    del uni, idx_u
     del E0, E, tables, out, ws, idx
     torch.cuda.empty_cache()
     return res
@@ -636,7 +736,7 @@ def bench_backward(g, w, cfg, tables, toks, cu, dev, stream, steps):
     return res
 
 
-def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
+def bench_decode(g, WL, cfg, tables, dev, stream, nsteps, with_cpu=False):
     """Speculative-verify decode: 256 sequences with 8192-token histories in the device
     cache; each step proposes 5 ids per sequence (1 + 4 drafts), all committed. The loop is
     captured once as a HIP graph and replayed; the cache is restored before each replay."""
@@ -646,13 +746,15 @@ def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
     wd = WL.workload(DECODE_WORKLOAD)
     nseq, tmax = wd.batch, wd.decode_new
     log(f"decode: {nsteps} steps x {nseq} sequences x {tmax} ids")
-    hist = torch.as_tensor(WL.token_batch(wd, purpose=0).reshape(-1)).to(dev)
+    hist_host = WL.token_batch(wd, purpose=0)
+    hist = torch.as_tensor(hist_host.reshape(-1)).to(dev)
     cu = torch.as_tensor(np.arange(nseq + 1, dtype=np.int32) * wd.seqlen).to(dev)
     cache = g.Cache.empty(cfg, nseq, device=dev)
     g.ngram_cache_init(cfg, cache, hist, cu, stream=stream)
     ring0, len0 = cache.ring.clone(), cache.len.clone()
-    ids = torch.as_tensor(WL.token_batch(wd, purpose=1, batch=nsteps * nseq, seqlen=tmax)
-                          .reshape(nsteps, nseq, tmax)).to(dev)
+    ids_host = WL.token_batch(wd, purpose=1, batch=nsteps * nseq, seqlen=tmax).reshape(
+        nsteps, nseq, tmax)
+    ids = torch.as_tensor(ids_host).to(dev)
     n_new = torch.full((nseq,), tmax, dtype=torch.int32, device=dev)
     out = torch.empty((nseq, tmax, cfg.D), dtype=torch.bfloat16, device=dev)
     ws = g.alloc_workspace(cfg, nseq * tmax, device=dev)
@@ -661,16 +763,21 @@ def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
         g.ngram_embed_decode(cfg, tables, cache, ids[s], n_new, out, ws, n_commit=n_new,
                              stream=stream)
     torch.cuda.synchronize(dev)
+    # eager steps (host launch path included): best of three rounds of 50, so that a one-off
+    # stall (the freeing of the previous leg's buffers) is not read as the step time
     eager_steps = 50
-    cache.ring.copy_(ring0)
-    cache.len.copy_(len0)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for s in range(eager_steps):
-        g.ngram_embed_decode(cfg, tables, cache, ids[s], n_new, out, ws, n_commit=n_new,
-                             stream=stream)
-    torch.cuda.synchronize(dev)
-    eager_us = (time.perf_counter() - t0) / eager_steps * 1e6
+    rounds = []
+    for _ in range(3):
+        cache.ring.copy_(ring0)
+        cache.len.copy_(len0)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for s in range(eager_steps):
+            g.ngram_embed_decode(cfg, tables, cache, ids[s], n_new, out, ws, n_commit=n_new,
+                                 stream=stream)
+        torch.cuda.synchronize(dev)
+        rounds.append((time.perf_counter() - t0) / eager_steps * 1e6)
+    eager_us = min(rounds)
     graph = torch.cuda.CUDAGraph()
     cache.ring.copy_(ring0)
     cache.len.copy_(len0)
@@ -758,10 +865,191 @@ def bench_decode(g, WL, cfg, tables, dev, stream, nsteps):
                  "hbm_frac": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_TFLOPs": round(step_flops / t_step / 1e12, 1),
                  "mfma_frac": round(step_flops / t_step / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    cpu = None
+    if with_cpu:
+        # steps 0 and the last plus 32 seeded ones
+        rest = np.random.default_rng(5).choice(np.arange(1, max(2, nsteps - 1)),
+                                               size=min(32, max(0, nsteps - 2)), replace=False)
+        check = sorted({0, nsteps - 1, *[int(x) for x in rest]})
+        log(f"decode cpu baseline: oracle hash of {nsteps} steps, embeddings of {len(check)}")
+        cpu = cpu_baseline_decode(wd, tables.E0, tables.E, tables.W,
+                                  hist_host[:, wd.seqlen - (wd.N - 1):], ids_host, set(check))
+        log(f"decode cpu baseline {cpu['value']:.0f} tokens/s")
+    fractions["traffic_decode_projection"] = counter_traffic(
+        "decode_project", "project.hip", TRAFFIC_DECODE)
     return {"workload": DECODE_WORKLOAD, "steps": nsteps, "seqs": nseq, "ids_per_step": tmax,
             "tokens_per_s": round(toks / t, 1), "us_per_step_graph": round(t_step * 1e6, 2),
             "us_per_step_eager": round(eager_us, 2), "replays": len(times),
-            "roofline_fractions": fractions, "draft_phase": draft}
+            "roofline_fractions": fractions, "draft_phase": draft, "cpu_baseline": cpu}
+
+
+def time_launches(fn, stream, reps, nev=2):
+    """HIP events on the launch stream around each call of fn(k, ev) (fn records ev[1..]
+    between its launches); returns the mean of every interval, in seconds."""
+    import numpy as np
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(reps)]
+    for k in range(reps):
+        evs[k][0].record(stream)
+        fn(k, evs[k])
+    torch.cuda.synchronize()
+    return [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e-3
+            for i in range(nev - 1)]
+
+
+def bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, steps):
+    """Kernel 2 in the form the projection runs it: the sub-table rows of a 64K-token batch
+    from HBM straight into LDS with the projection's 16-byte-per-lane LDS loads, reduced
+    there to one checksum per row (4 bytes written per row). Zipf(1.1) ids (the workload)
+    and uniform ids (no repeats within a batch to hit in cache), four batches rotated."""
+    import numpy as np
+    import torch
+
+    T = int(toks[0].shape[0])
+    idx = [torch.empty((T, w.S), dtype=torch.int32, device=dev) for _ in toks]
+    uni = [torch.as_tensor(WL.uniform_ids(np.random.default_rng([7, p]), w.V0, (T,))).to(dev)
+           for p in range(len(toks))]
+    sums = torch.empty(T, dtype=torch.int32, device=dev)
+    read_b = T * w.S * w.d * 2
+    alg_b = read_b + T * w.S * 4 + T * 4            # rows, indices read, checksums written
+    res = {"kernel": "gather_lds_kernel", "loader": "global_load_lds_dwordx4 (HBM -> LDS)",
+           "bytes_read_rows": read_b, "bytes_algorithmic": alg_b,
+           "traffic": counter_traffic("gather_lds", "gather.hip")}
+    for name, ids in (("zipf", toks), ("uniform_ids_control", uni)):
+        for r in range(len(ids)):
+            g.ngram_embed_hash(cfg, ids[r], cu, idx[r], None, stream=stream)
+        for k in range(3):
+            g.ngram_embed_gather_checksum(cfg, tables, idx[k % len(idx)], sums, stream=stream)
+        (t,) = time_launches(lambda k, ev: (g.ngram_embed_gather_checksum(
+            cfg, tables, idx[k % len(idx)], sums, stream=stream), ev[1].record(stream)),
+            stream, steps)
+        res[name] = {"kernel_us": round(t * 1e6, 1),
+                     "read_GBps": round(read_b / t / 1e9, 1),
+                     "algorithmic_GBps": round(alg_b / t / 1e9, 1),
+                     "frac_of_hbm_peak": round(alg_b / t / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"gather into LDS, {name}: {t*1e6:.1f} us = {alg_b/t/1e9:.0f} GB/s "
+            f"({alg_b/t/1e9/HBM_PEAK_GBS:.1%} of HBM peak)")
+    res["frac_of_hbm_peak"] = res["zipf"]["frac_of_hbm_peak"]
+    return res
+
+
+def bench_configs(g, WL, dev, stream, with_cpu):
+    """The three smaller configurations through the same entry points the 30B layer uses
+    (hash, then the fused gather + projection), each on its own seeded batch: tokens/s, the
+    kernels' HIP-event times, and both rooflines (algorithmic bytes and flops per call); the
+    CPU oracle on the same whole batch beside each."""
+    import numpy as np
+    import torch
+
+    out = {}
+    for name, reps in CONFIG_LEGS:
+        torch.cuda.empty_cache()
+        w = WL.workload(name)
+        cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+        if w.dtype == "f32":
+            E0, E, W = WL.host_tables(w)
+            E0, E, W = E0.to(dev), [e.to(dev) for e in E], W.to(dev)
+        else:
+            E0, E, W = WL.device_tables(w, device=dev)
+        tables = g.Tables(E0, E, W)
+        tok2d = WL.token_batch(w)
+        T = w.T
+        toks = torch.as_tensor(tok2d.reshape(-1)).to(dev)
+        cu = torch.as_tensor(np.arange(w.batch + 1, dtype=np.int32) * w.seqlen).to(dev)
+        out_t = torch.empty((T, w.D), dtype=E0.dtype, device=dev)
+        ws = g.alloc_workspace(cfg, T, device=dev)
+        _, idx_off = g.ngram_embed_workspace_layout(cfg, T)
+        idx = ws[idx_off:].view(torch.int32)
+        for _ in range(5):
+            g.ngram_embed_prefill(cfg, tables, toks, cu, out_t, ws, stream=stream)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+
+        def step(k, ev):
+            g.ngram_embed_hash(cfg, toks, cu, idx, ws, stream=stream)
+            ev[1].record(stream)
+            g.ngram_embed_project(cfg, tables, idx, toks, out_t, stream=stream)
+            ev[2].record(stream)
+        t_hash, t_proj = time_launches(step, stream, reps, nev=3)
+        wall = (time.perf_counter() - t0) / reps
+        if g.ngram_embed_read_error_flag(ws, stream=stream) != 0:
+            raise RuntimeError(f"device error flags set in the {name} prefill")
+        esz = w.esz
+        flops = 2.0 * T * w.D * w.D
+        alg = (T * (w.S * w.d * esz + 2 * w.D * esz + w.S * 4 + 4) + w.D * w.D * esz
+               + T * 4 * (1 + w.S))
+        t = t_hash + t_proj
+        peak_f = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        res = {"dtype": w.dtype, "V0": w.V0, "D": w.D, "N": w.N, "K": w.K, "tokens": T,
+               "reps": reps, "ids": w.ids,
+               "tokens_per_s": round(T / t, 1), "us_per_call": round(t * 1e6, 2),
+               "us_per_call_host_wall": round(wall * 1e6, 2),
+               "kernels_us": {"hash": round(t_hash * 1e6, 2), "project": round(t_proj * 1e6, 2)},
+               "bytes_algorithmic": int(alg), "flops": flops,
+               "hbm_GBps": round(alg / t / 1e9, 1),
+               "hbm_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+               "TFLOPs": round(flops / t / 1e12, 2),
+               "compute_peak_TFLOPs": peak_f,
+               "compute_frac": round(flops / t / 1e12 / peak_f, 4)}
+        if with_cpu:
+            res["cpu_baseline"] = cpu_baseline(w, E0, E, W, [tok2d])
+        log(f"{name}: {t*1e6:.1f} us per call ({T / t / 1e6:.1f} M tokens/s; "
+            f"{res['hbm_frac']:.1%} of HBM, {res['compute_frac']:.1%} of compute peak)"
+            + (f"; oracle {res['cpu_baseline']['value']:.0f} tokens/s" if with_cpu else ""))
+        out[name] = res
+        del E0, E, W, tables, out_t, ws, idx
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_decode(wd, E0, E, W, hist_tail, ids, check_steps):
+    """The decode oracle on the benchmark's own decode run: every hash index of every step
+    (the histories' last N-1 ids, then each step's ids committed in turn) and the embeddings
+    of the rows of `check_steps`; the time of the whole run at the measured rate per step is
+    reported as extrapolated."""
+    import numpy as np
+    import torch
+
+    import oracle
+    nsteps, nseq, tmax = ids.shape
+    orc = oracle.DecodeOracle(wd.V0, wd.D, wd.N, wd.K, wd.V, [list(h) for h in hist_tail])
+    kept = {}
+    t0 = time.perf_counter()
+    for s in range(nsteps):
+        step_ids = [list(r) for r in ids[s]]
+        idxs = orc.step_indices(step_ids)
+        if s in check_steps:
+            kept[s] = np.concatenate(idxs)
+        orc.commit(step_ids, [tmax] * nseq)
+    t_hash = time.perf_counter() - t0
+    Wh = W.float().cpu().numpy().astype(np.float64)
+    Wb = [Wh[:, q * wd.d:(q + 1) * wd.d] for q in range(wd.S)]
+    t_embed = t_copy = 0.0
+    for s in sorted(kept):
+        tok = ids[s].reshape(-1)
+        c0 = time.perf_counter()
+        rows = {-1: E0.index_select(0, torch.as_tensor(tok.astype(np.int64), device=E0.device))
+                .float().cpu().numpy().astype(np.float64)}
+        for q in range(wd.S):
+            rows[q] = E[q].index_select(0, torch.as_tensor(kept[s][:, q], device=E0.device)
+                                        ).float().cpu().numpy().astype(np.float64)
+        t_copy += time.perf_counter() - c0
+        t1 = time.perf_counter()
+        oracle.embed_from_indices(wd.D, wd.N, wd.K, tok, kept[s], lambda q, r, rows=rows: rows[q],
+                                  Wb)
+        t_embed += time.perf_counter() - t1
+    per_step = t_hash / nsteps + t_embed / len(kept)
+    blas, threads = blas_info()
+    return {"value": round(nseq * tmax / per_step, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"hash indices of all {nsteps} steps x {nseq} sequences x {tmax} ids "
+                       f"({t_hash:.2f} s, python ints, 1 thread); float64 embeddings of "
+                       f"{len(kept)} of the steps ({t_embed:.2f} s, {threads} BLAS threads); "
+                       f"the {nsteps}-step run at that rate is extrapolated"),
+            "seconds": {"hash_all_steps": round(t_hash, 3),
+                        "embeddings_sampled_steps": round(t_embed, 3),
+                        "row_copy_not_timed": round(t_copy, 3),
+                        "whole_run_extrapolated": round(per_step * nsteps, 2)}}
 
 
 if __name__ == "__main__":

@@ -25,7 +25,7 @@ __all__ = [
     "NGRAM_FORM_FINAL", "NGRAM_FORM_BASIC", "FORMS", "ngram_hash_stats_workspace_size",
     "ngram_hash_stats",
     "ngram_embed_workspace_size", "ngram_embed_workspace_layout", "ngram_embed_hash",
-    "ngram_embed_gather", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
+    "ngram_embed_gather", "ngram_embed_gather_checksum", "ngram_embed_project", "ngram_embed_prefill", "ngram_cache_init",
     "ngram_embed_decode", "ngram_cache_commit", "ngram_embed_read_error_flag",
     "ngram_embed_clear_error_flag", "ngram_embed_status_string", "alloc_workspace",
     "ngram_embed_backward_workspace_size", "ngram_embed_backward", "alloc_backward_workspace",
@@ -100,6 +100,7 @@ def load():
                                                         ctypes.POINTER(SZ)]),
         "ngram_embed_hash": (ctypes.c_int, [cfgp, P, P, I32, I64, P, P, P]),
         "ngram_embed_gather": (ctypes.c_int, [cfgp, tabp, P, I64, P, P]),
+        "ngram_embed_gather_checksum": (ctypes.c_int, [cfgp, tabp, P, I64, P, P]),
         "ngram_embed_project": (ctypes.c_int, [cfgp, tabp, P, P, I64, P, P]),
         "ngram_embed_prefill": (ctypes.c_int, [cfgp, tabp, P, P, I32, I64, P, cachep, P,
                                                 SZ, P]),
@@ -445,6 +446,21 @@ def ngram_embed_gather(cfg: Config, tables: Tables, idx, G, stream=None):
     t, keep2 = tables._c()
     _check(fn, load().ngram_embed_gather(
         ctypes.byref(c), ctypes.byref(t), _ptr(idx), int(G.shape[0]), _ptr(G), _stream(stream)))
+
+
+def ngram_embed_gather_checksum(cfg: Config, tables: Tables, idx, sums, stream=None):
+    """sums [nrows] (uint32 stored in an int32 tensor) = the checksum of each gathered row as
+    it lands in LDS: sum_k w_k (2k + 1) mod 2^32 over the row's 32-bit words."""
+    fn = "ngram_embed_gather_checksum"
+    if _shapes_ok(cfg):
+        _tables_arg(fn, cfg, tables)
+    _arg(fn, "sums", sums, _i32(), shape=(None,))
+    _arg(fn, "idx", idx, _i32(), min_numel=sums.shape[0] * max(cfg.S, 0))
+    c, keep = cfg._c()
+    t, keep2 = tables._c()
+    _check(fn, load().ngram_embed_gather_checksum(
+        ctypes.byref(c), ctypes.byref(t), _ptr(idx), int(sums.shape[0]), _ptr(sums),
+        _stream(stream)))
 
 
 def ngram_embed_project(cfg: Config, tables: Tables, idx, tok, out, stream=None):

@@ -282,6 +282,20 @@ int ngram_embed_gather(const ngram_embed_config* cfg, const ngram_embed_tables* 
                                          static_cast<hipStream_t>(stream)));
 }
 
+int ngram_embed_gather_checksum(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                                const int32_t* idx, int64_t nrows, uint32_t* sums,
+                                void* stream) {
+  LayerDesc L;
+  int rc = ngram::describe(cfg, &L);
+  if (rc != NGRAM_OK) return rc;
+  if (nrows < 0) return NGRAM_EINVAL;
+  if (nrows == 0 || L.S == 0) return NGRAM_OK;
+  if ((rc = check_tables(L, tables, false)) != NGRAM_OK) return rc;
+  if (!ngram::aligned(idx, 4) || !ngram::aligned(sums, 4)) return NGRAM_EALIGN;
+  return hip_status(ngram::launch_gather_lds(L, tables->E, idx, nrows, sums,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int ngram_embed_project(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                         const int32_t* idx, const int32_t* tok, int64_t nrows, void* out,
                         void* stream) {

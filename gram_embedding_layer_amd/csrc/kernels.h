@@ -92,6 +92,12 @@ hipError_t launch_clear_flags(int32_t* flags, hipStream_t st);
 hipError_t launch_gather(const LayerDesc& L, const void* const* E, const int32_t* idx,
                          int64_t nrows, void* G, hipStream_t st);
 
+// kernel 2 into LDS: the gather the projection performs (global_load_lds_dwordx4), each
+// gathered row reduced where it lands to sums[r] = sum_k w_k (2k + 1) mod 2^32 over its
+// 32-bit words
+hipError_t launch_gather_lds(const LayerDesc& L, const void* const* E, const int32_t* idx,
+                             int64_t nrows, uint32_t* sums, hipStream_t st);
+
 // kernels 2+3: fused gather + projection + E_0 epilogue (times the output factor); with
 // f32out, `out` is fp32 [nrows, D] and holds the unrounded rows
 hipError_t launch_project(const LayerDesc& L, const void* E0, const void* const* E,

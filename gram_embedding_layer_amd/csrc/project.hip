@@ -30,6 +30,7 @@
 
 #include "bf16.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace ngram {
 namespace {
@@ -107,21 +108,6 @@ template <int BM, int BN> struct Tile {
                 "the slice buffers and the tile's indices must fit the LDS");
 };
 
-typedef __attribute__((address_space(3))) char lds_char;
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
-// (global_load_lds_dwordx4). Written as asm so that its completion is waited for only by
-// the explicit vmcnt waits below (the compiler would otherwise drain every load in flight
-// before each LDS read); it has no register result. The LDS address is an input operand
-// bound to m0 ("{m0}"), so the compiler itself writes m0 before the instruction and knows
-// that m0 holds this value: nothing of its own can be lost. The s_nop covers the one wait
-// state an LDS DMA needs after an m0 write.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\t"
-               "global_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "{m0}"(lds_addr) : "memory");
-}
-
 // Wait until at most N of this wave's global loads are in flight (they complete in issue
 // order), then meet the other waves. The memory clobber keeps LDS accesses on their side.
 template <int N>
@@ -135,22 +121,22 @@ __device__ __forceinline__ void wait_loads_and_meet() {
 // memory), WGM along rows x 8/WGM along outputs; each wave owns a WM x WN block of
 // 32x32 matrix-core tiles.
 // (16 waves of 64x64 outputs, 4 per SIMD in 122 VGPRs, measured the same: 1214 vs 1212 us.)
-template <int BM> struct WaveGrid {
+template <int BM, int BN> struct WaveGrid {
   static constexpr int NW = 8;   // waves per block
   static constexpr int WGM = BM >= 128 ? 4 : 2;
 };
 
 template <int BM, int OM, int BN>
-__global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(const ProjArgs a) {
+__global__ __launch_bounds__((WaveGrid<BM, BN>::NW * 64), 1) void proj_mfma_kernel(const ProjArgs a) {
   constexpr int NST = Tile<BM, BN>::NST;
   constexpr int BK = Tile<BM, BN>::BK;
   constexpr int RB = BK * 2;             // bytes of one row per slice
   constexpr int CPR = RB / 16;           // 16-byte chunks per row per slice
   constexpr int RPL = 1024 / RB;         // rows per wave load (64 lanes x 16 bytes)
   constexpr int KS = BK / 16;            // 16-deep k-steps per slice
-  constexpr int NW = WaveGrid<BM>::NW;
+  constexpr int NW = WaveGrid<BM, BN>::NW;
   constexpr int NT = NW * 64;            // threads per block
-  constexpr int WGM = WaveGrid<BM>::WGM;
+  constexpr int WGM = WaveGrid<BM, BN>::WGM;
   constexpr int WGN = NW / WGM;
   constexpr int AR = BM / NW;            // A rows each wave loads
   constexpr int BR = BN / NW;            // W rows each wave loads
@@ -234,7 +220,7 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
   auto pchunk_b = [&](int q) __attribute__((always_inline)) {
     return (lane % CPR) ^ swz(w * BR + q * RPL + prow);
   };
-  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)lds));
+  const uint32_t lds0 = lds_address(lds);
   const int layer = blockIdx.z;
   const uint16_t* const* E = reinterpret_cast<const uint16_t* const*>(a.E) + layer * a.S;
   const uint16_t* W = static_cast<const uint16_t*>(a.W[layer]);
@@ -370,7 +356,8 @@ __global__ __launch_bounds__(WaveGrid<BM>::NW * 64, 1) void proj_mfma_kernel(con
     // waves meet: slice k is complete in LDS and every wave is past slice k-1, whose buffer
     // the load of slice k+NST-1 reuses.
     const int ahead = NST - 2 < NK - 1 - k ? NST - 2 : NK - 1 - k;
-    if (NST >= 4 && ahead >= 2) wait_loads_and_meet<(NST >= 4 ? 2 : 0) * PER_SLICE>();
+    if (NST >= 5 && ahead >= 3) wait_loads_and_meet<(NST >= 5 ? 3 : 0) * PER_SLICE>();
+    else if (NST >= 4 && ahead >= 2) wait_loads_and_meet<(NST >= 4 ? 2 : 0) * PER_SLICE>();
     else if (NST >= 3 && ahead >= 1) wait_loads_and_meet<(NST >= 3 ? 1 : 0) * PER_SLICE>();
     else wait_loads_and_meet<0>();
     const char* sp = lds + (k % NST) * STAGE;
@@ -674,7 +661,7 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int osz, hipStream_t st) {
     a.tiles_n = a.N / BN;
     const int64_t blocks = int64_t(a.tiles_m) * a.tiles_n * (OM == kOutPartial ? a.splits : 1);
     hipLaunchKernelGGL((proj_mfma_kernel<BM, OM, BN>), dim3(unsigned(blocks), 1, unsigned(a.layers)),
-                       dim3(WaveGrid<BM>::NW * 64), 0, st, a);
+                       dim3(WaveGrid<BM, BN>::NW * 64), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

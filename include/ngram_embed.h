@@ -177,6 +177,18 @@ int ngram_embed_hash(const ngram_embed_config* cfg, const int32_t* tokens,
 int ngram_embed_gather(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
                        const int32_t* idx, int64_t nrows, void* G, void* stream);
 
+/* The same gather in the form the projection performs it (kernel 2 into on-chip memory):
+ * each sub-table row goes from HBM straight into LDS (16 bytes per lane, the projection's
+ * A-loader instruction) and is reduced where it lands to one checksum per gathered row,
+ *   sums[r] = sum_k w_k * (2k + 1)  mod 2^32,
+ * w_k the 32-bit words (little-endian) of row r of the G that ngram_embed_gather writes.
+ * Only sums [nrows] (device uint32, 4-byte aligned) is written, so the call moves the
+ * gather's HBM reads alone; indices are clamped as in ngram_embed_gather. For measuring the
+ * gather's HBM -> LDS rate, and for checking byte for byte what the LDS loads deliver. */
+int ngram_embed_gather_checksum(const ngram_embed_config* cfg, const ngram_embed_tables* tables,
+                                const int32_t* idx, int64_t nrows, uint32_t* sums,
+                                void* stream);
+
 /* ---------------------------------------------------------------- kernels 2+3: projection
  * out[r, :] = ( E_0[tok[r], :] + sum_s W_{n,k} E_{n,k}[idx[r*S + s], :] ) / (S + 1)
  * (times amp_scale with NGRAM_AMP_SCALE; NGRAM_AMP_LAYERNORM returns NGRAM_EINVAL here)

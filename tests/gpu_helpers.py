@@ -123,3 +123,22 @@ def oracle_rows(w, E0, E, W, tokens, cu, rows):
     e = oracle.embed_from_indices(w.D, w.N, w.K, tokens[rows], idx[rows],
                                   device_fetch(E0, E), w_blocks(W, w.S))
     return idx, e
+
+
+def row_checksums(words):
+    """sum_k w_k (2k + 1) mod 2^32 of every row of a uint32 array [rows, M] (the checksum that
+    ngram_embed_gather_checksum takes of each gathered row where it lands)."""
+    w = np.asarray(words, dtype=np.uint32).astype(np.uint64)
+    k = 2 * np.arange(w.shape[1], dtype=np.uint64) + 1
+    return ((w * k).sum(axis=1) % (1 << 32)).astype(np.uint32)
+
+
+def gathered_words(E, idx):
+    """The gathered rows [E_s[idx[:, s]] for every s] as uint32 words, by torch indexing of the
+    device tables (not the library)."""
+    import torch
+    parts = [E[s].index_select(0, torch.as_tensor(np.asarray(idx[:, s], dtype=np.int64),
+                                                  device=E[s].device))
+             for s in range(len(E))]
+    G = torch.cat(parts, dim=1).contiguous()
+    return G.view(torch.int32).cpu().numpy().view(np.uint32)

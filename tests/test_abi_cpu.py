@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "ngram_cache_commit", "ngram_embed_backward",
               "ngram_embed_backward_workspace_size"):
         assert n in names
-    assert len(names) == 22
+    assert len(names) == 23
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -451,7 +451,7 @@ def test_binding_rejects_bad_tensors():
 
 
 def test_lds_dma_m0_is_an_operand():
-    """The projection's LDS-DMA loads take their LDS address in m0 as an asm input operand
+    """The LDS-DMA loads (projection, LDS gather) take their LDS address in m0 as an asm input operand
     ("{m0}"), so the compiler writes m0 itself and keeps no other value there across them.
     Checked on the gfx950 assembly of this repository's source: no reserved-register clobber
     warning, every DMA load preceded by an m0 write and the hazard nop, and no instruction that
@@ -459,13 +459,15 @@ def test_lds_dma_m0_is_an_operand():
     from gram_embedding_layer_amd import build
     if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
         pytest.skip("hipcc not installed")
-    cmd = [build.hipcc(), f"--offload-arch={build.ARCH}", "-O3", "-std=c++17",
-           "--cuda-device-only", "-S", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", f"-I{build.INCLUDE}", f"-I{build.CSRC}", "-o", "-",
-           os.path.join(build.CSRC, "project.hip")]
-    res = subprocess.run(cmd, capture_output=True, text=True, check=True)
-    assert "reserved registers" not in res.stderr
-    lines = [ln.strip() for ln in res.stdout.splitlines()]
+    lines = []
+    for src in ("project.hip", "gather.hip"):
+        cmd = [build.hipcc(), f"--offload-arch={build.ARCH}", "-O3", "-std=c++17",
+               "--cuda-device-only", "-S", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", f"-I{build.INCLUDE}", f"-I{build.CSRC}", "-o", "-",
+               os.path.join(build.CSRC, src)]
+        res = subprocess.run(cmd, capture_output=True, text=True, check=True)
+        assert "reserved registers" not in res.stderr, src
+        lines += [ln.strip() for ln in res.stdout.splitlines()]
     dma = [i for i, ln in enumerate(lines) if ln.startswith("global_load_lds_dwordx4")]
     assert dma, "no LDS-DMA loads found"
     for i in dma:
@@ -509,3 +511,19 @@ def test_noalloc_decode_rejects_before_any_device_call(lib):
     empty = g._CCache(FAKE, FAKE, 0)
     assert lib.ngram_embed_decode_noalloc(P(c), P(T), P(empty), FAKE, FAKE, 5, None, FAKE,
                                           None, 0) == 0
+
+
+def test_gather_checksum_argument_checks(lib):
+    cfg = tiny_cfg()
+    c, keep = cfg._c()
+    T, keep2 = _tables_c(4)
+    P = ctypes.byref
+    assert lib.ngram_embed_gather_checksum(P(c), P(T), FAKE, -1, FAKE, 0) == -1
+    assert lib.ngram_embed_gather_checksum(P(c), P(T), FAKE, 0, FAKE, 0) == 0
+    assert lib.ngram_embed_gather_checksum(P(c), P(T), FAKE + 2, 8, FAKE, 0) == -3
+    assert lib.ngram_embed_gather_checksum(P(c), P(T), FAKE, 8, FAKE + 1, 0) == -3
+    Tb, k3 = _tables_c(4, sub=FAKE + 8)
+    assert lib.ngram_embed_gather_checksum(P(c), P(Tb), FAKE, 8, FAKE, 0) == -3
+    bad = tiny_cfg(D=62)
+    cb, k4 = bad._c()
+    assert lib.ngram_embed_gather_checksum(P(cb), P(T), FAKE, 8, FAKE, 0) == -1

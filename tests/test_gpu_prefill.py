@@ -15,8 +15,8 @@ import pytest
 import gram_embedding_layer_amd as g
 import oracle
 import workloads as WL
-from tests.gpu_helpers import (assert_close, cfg_of, device_fetch, oracle_rows, packed,
-                               to_f64, w_blocks)
+from tests.gpu_helpers import (assert_close, cfg_of, device_fetch, gathered_words,
+                               oracle_rows, packed, row_checksums, to_f64, w_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -214,8 +214,15 @@ def test_prefill_parity_workload(lib, request, name):
         want = E[s].index_select(0, torch.as_tensor(idx[:, s], device="cuda"))
         assert torch.equal(G[:, s * w.d:(s + 1) * w.d].view(torch.int16),
                            want.view(torch.int16)), s
+    del G
+    # the gather into LDS (the projection's loader) delivers every byte of every row
+    sums = torch.empty(T, dtype=torch.int32, device="cuda")
+    g.ngram_embed_gather_checksum(cfg, g.Tables(E0, E, W), ws[idx_off:].view(torch.int32), sums)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sums.cpu().numpy().view(np.uint32),
+                                  row_checksums(gathered_words(E, idx)))
     assert g.ngram_embed_read_error_flag(ws) == 0
-    del E0, E, W, ws, G
+    del E0, E, W, ws
     torch.cuda.empty_cache()
 
 
@@ -306,3 +313,32 @@ def test_out_of_range_indices_are_clamped(lib):
     e = oracle.embed_from_indices(w.D, w.N, w.K, tok, fixed.astype(np.int64),
                                   device_fetch(E0, E), w_blocks(W, w.S))
     assert_close(to_f64(outs[1]), e, "bf16", "clamped")
+
+
+# Each path of the LDS gather: batches of whole rows (1, 2 and 4 KB rows, 16 sub-tables),
+# rows longer than a wave's 10 KB buffer taken in pieces (the basic form's 3 x 6 KB rows),
+# fp32 rows, ragged batch sizes, indices past their table (clamped as ngram_embed_gather).
+LDS_CASES = [
+    ("f32_d64", small_workload("f32", D=64), 257),
+    ("bf16_d1024", small_workload("bf16", D=1024, N=3, K=2, V0=32000), 1001),
+    ("bf16_d2048_s16", small_workload("bf16", D=2048, N=5, K=4, V0=131072), 333),
+    ("bf16_d3072_s12", small_workload("bf16", D=3072, N=4, K=4, V0=131072), 4097),
+    ("basic_d3072", WL.Workload("basic_lds", "bf16", 5000, 3072, 4, 1,
+                                tuple(WL.mid_gap_primes(5000, 15000, 3)), 1, 1, "uniform", 12,
+                                form="basic"), 130),
+]
+
+
+@pytest.mark.parametrize("name,w,T", LDS_CASES, ids=[c[0] for c in LDS_CASES])
+def test_gather_checksum_every_row(lib, name, w, T):
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V), form=w.form)
+    E0, E, W = host_to_dev_tables(w)
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.integers(0, v, size=T) for v in w.V], axis=1).astype(np.int32)
+    idx[::97, 0] = w.V[0] + 3                     # past the table: clamped to its last row
+    sums = torch.full((T,), 7, dtype=torch.int32, device="cuda")
+    g.ngram_embed_gather_checksum(cfg, g.Tables(E0, E, W), dev(idx), sums)
+    torch.cuda.synchronize()
+    ref_idx = np.minimum(idx, np.asarray(w.V) - 1)
+    want = row_checksums(gathered_words(E, ref_idx))
+    np.testing.assert_array_equal(sums.cpu().numpy().view(np.uint32), want)
