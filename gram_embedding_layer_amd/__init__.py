@@ -20,7 +20,7 @@ __all__ = [
     "LIB_PATH", "NgramError", "Config", "Tables", "Cache", "load",
     "NGRAM_OK", "NGRAM_F32", "NGRAM_BF16", "AMP_MODES",
     "NGRAM_FLAG_BAD_TOKEN", "NGRAM_FLAG_BAD_SEQLENS", "NGRAM_FLAG_BAD_COUNT",
-    "NGRAM_FLAG_BAD_SLOT", "ngram_embed_decode_rows", "ngram_cache_init_slots",
+    "NGRAM_FLAG_BAD_SLOT", "NGRAM_FLAG_DUP_SLOT", "ngram_embed_decode_rows", "ngram_cache_init_slots",
     "ngram_cache_commit_slots", "ngram_embed_prefill_layers", "ngram_embed_decode_layers",
     "NGRAM_FORM_FINAL", "NGRAM_FORM_BASIC", "FORMS", "ngram_hash_stats_workspace_size",
     "ngram_hash_stats",
@@ -40,6 +40,7 @@ NGRAM_NOALLOC_SCRATCH_BYTES = 16 << 20    # scratch of ngram_embed_decode_noallo
 NGRAM_F32, NGRAM_BF16 = 0, 1
 NGRAM_FLAG_BAD_TOKEN, NGRAM_FLAG_BAD_SEQLENS, NGRAM_FLAG_BAD_COUNT = 1, 2, 4
 NGRAM_FLAG_BAD_SLOT = 8
+NGRAM_FLAG_DUP_SLOT = 16
 NGRAM_MAX_DECODE_TOKENS = 8
 # amp_scale value that makes the library use sqrt(D) (NGRAM_AMP_SCALE_SQRT_D)
 NGRAM_AMP_SCALE_SQRT_D = 0.0

@@ -46,6 +46,26 @@ __device__ __forceinline__ bool position_context(const int32_t* __restrict__ tok
   return true;
 }
 
+// Whether batch entry b's slot already appears at an earlier entry (slots of one call must be
+// distinct; a repeated slot would have two entries read and append to one ring at once).
+// Every thread of the block calls it (it meets the others at barriers): the block reads
+// slots[0, bmax) tile by tile into `tile` (nthreads ints) and the `nparts` threads of an
+// entry share the comparisons with the entries below b (thread `part` takes every nparts-th).
+// bmax: one past the block's last entry. Inactive threads pass b = 0.
+__device__ __forceinline__ bool slot_seen_before(const int32_t* __restrict__ slots, int32_t bmax,
+                                                 int32_t b, int32_t slot, int part, int nparts,
+                                                 int32_t* tile, int nthreads) {
+  bool seen = false;
+  for (int32_t t0 = 0; t0 < bmax; t0 += nthreads) {
+    __syncthreads();                                   // the previous tile is read
+    const int32_t q = t0 + int32_t(threadIdx.x);
+    tile[threadIdx.x] = q < bmax ? slots[q] : -1;
+    __syncthreads();
+    for (int k = part; k < nthreads && t0 + k < b; k += nparts) seen |= tile[k] == slot;
+  }
+  return seen;
+}
+
 // One thread per (position, sub-table): thread g hashes sub-table g % S of position g / S, so
 // a position's S hashes run side by side (a thread per position left one wave per SIMD
 // working through ~36 dependent 64-bit Horner steps) and the index writes are contiguous.
@@ -94,6 +114,21 @@ __global__ __launch_bounds__(kDecThreads) void hash_decode_kernel(const LayerDes
   const int j = a.row_begin + jj;
   const bool active = int(threadIdx.x) < epb * tpe && b < a.nbatch;
   const bool lead = within == 0;                   // the entry's flags and commit
+  // with a slot map: an entry whose slot an earlier entry already uses is ignored (no rows
+  // written, no commit), so no ring is read and appended to by two entries at once
+  bool dup = false;
+  if (a.slots != nullptr) {
+    __shared__ int32_t tile[kDecThreads];
+    __shared__ int32_t seen[kDecThreads];          // per entry of the block (epb <= 512)
+    const int le = int(threadIdx.x) / tpe;
+    if (int(threadIdx.x) < epb) seen[threadIdx.x] = 0;
+    const int32_t bmax = min(a.nbatch, int32_t(blockIdx.x + 1) * epb);
+    const bool hit = slot_seen_before(a.slots, bmax, active ? b : 0, active ? a.slots[b] : -1,
+                                      within, tpe, tile, kDecThreads);
+    if (active && hit) seen[le] = 1;
+    __syncthreads();
+    dup = active && seen[le] != 0;
+  }
   DecodeEntry<NMAX> e{};
   int acc = 0;
   if (active) {
@@ -102,8 +137,10 @@ __global__ __launch_bounds__(kDecThreads) void hash_decode_kernel(const LayerDes
     if (a.n_commit != nullptr && lead) acc = a.n_commit[b];
     if (lead && a.flags != nullptr) {
       if (!e.slot_ok) atomicOr(a.flags, NGRAM_FLAG_BAD_SLOT);
+      else if (dup) atomicOr(a.flags, NGRAM_FLAG_DUP_SLOT);
       if (e.bad_count) atomicOr(a.flags, NGRAM_FLAG_BAD_COUNT);
     }
+    if (dup) e.slot_ok = false;
     const int64_t r = int64_t(b) * a.width + jj;
     uint32_t id;
     if (!entry_row(e, j, &id)) {
@@ -131,8 +168,17 @@ __global__ __launch_bounds__(kThreads) void cache_init_kernel(
     const int32_t* __restrict__ slots, int32_t nslots, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ cu, int32_t nbatch, int64_t ntok, int32_t* __restrict__ flags) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
+  const int slot = b < nbatch ? (slots != nullptr ? slots[b] : b) : -1;
+  if (slots != nullptr) {                          // a slot used by an earlier entry: ignored
+    __shared__ int32_t tile[kThreads];
+    const int32_t bmax = min(nbatch, int32_t(blockIdx.x + 1) * kThreads);
+    if (slot_seen_before(slots, bmax, b < nbatch ? b : 0, slot, 0, 1, tile, kThreads) &&
+        b < nbatch && slot >= 0 && slot < nslots) {
+      if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_DUP_SLOT);
+      return;
+    }
+  }
   if (b >= nbatch) return;
-  const int slot = slots != nullptr ? slots[b] : b;
   if (slot < 0 || slot >= nslots) {
     if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_SLOT);
     return;
@@ -157,8 +203,17 @@ __global__ __launch_bounds__(kThreads) void cache_commit_kernel(
     const int32_t* __restrict__ n_accept, int32_t nbatch, int32_t tmax,
     int32_t* __restrict__ flags) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
+  const int slot = b < nbatch ? (slots != nullptr ? slots[b] : b) : -1;
+  if (slots != nullptr) {                          // a slot used by an earlier entry: ignored
+    __shared__ int32_t tile[kThreads];
+    const int32_t bmax = min(nbatch, int32_t(blockIdx.x + 1) * kThreads);
+    if (slot_seen_before(slots, bmax, b < nbatch ? b : 0, slot, 0, 1, tile, kThreads) &&
+        b < nbatch && slot >= 0 && slot < nslots) {
+      if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_DUP_SLOT);
+      return;
+    }
+  }
   if (b >= nbatch) return;
-  const int slot = slots != nullptr ? slots[b] : b;
   if (slot < 0 || slot >= nslots) {
     if (flags != nullptr) atomicOr(flags, NGRAM_FLAG_BAD_SLOT);
     return;

@@ -72,7 +72,8 @@ enum {
   NGRAM_FLAG_BAD_TOKEN = 1,   /* a token id outside [0, V0) was hashed */
   NGRAM_FLAG_BAD_SEQLENS = 2, /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_nseq = ntok */
   NGRAM_FLAG_BAD_COUNT = 4,   /* n_new or n_accept outside [0, tmax] */
-  NGRAM_FLAG_BAD_SLOT = 8     /* a cache slot outside [0, cache->nseq) */
+  NGRAM_FLAG_BAD_SLOT = 8,    /* a cache slot outside [0, cache->nseq) */
+  NGRAM_FLAG_DUP_SLOT = 16    /* a cache slot that an earlier batch entry of the call uses */
 };
 
 /* Embedding amplification (section 3.2.4): what is applied to e_i before it is written.
@@ -253,7 +254,10 @@ int ngram_cache_commit(const ngram_embed_config* cfg, ngram_cache* cache,
  * The cache is a pool of cache->nseq slots. Batch entry b (0 <= b < nbatch) uses slot
  * slots[b] (device int32 [nbatch]; NULL means slot b, and then nbatch <= cache->nseq).
  * Slots of one call must be distinct. An out-of-range slot sets NGRAM_FLAG_BAD_SLOT in the
- * workspace (or err_flags) and the entry is ignored (no rows written, no commit).
+ * workspace (or err_flags) and the entry is ignored (no rows written, no commit); so does a
+ * slot that an earlier entry of the call (smaller b) uses, with NGRAM_FLAG_DUP_SLOT (the
+ * earlier entry is served as usual). The check compares each entry with the earlier ones
+ * (quadratic in nbatch, negligible at batch sizes of thousands).
  *
  * ngram_embed_decode_rows computes, for each batch entry b, the rows j in
  * [row_begin, min(row_end, n_new[b])) exactly as ngram_embed_decode would (same bits), and

@@ -180,3 +180,82 @@ def test_draft_rows_30b_spec_shape(lib, tables_30b):
     torch.cuda.synchronize()
     assert torch.equal(bits(out), bits(ref))
     assert g.ngram_embed_read_error_flag(ws) == 0
+
+
+def test_duplicate_slots_are_flagged_and_skipped(lib):
+    """A slot that an earlier batch entry of the call already uses: the later entry is
+    ignored (no rows, no commit, NGRAM_FLAG_DUP_SLOT), the earlier one is served exactly as in
+    a call without the repeat; the same for commit_slots and init_slots."""
+    w, cfg, tables, hists, new, n_new = setup_small(nseq=6)
+    nseq, tmax = new.shape
+    slots = np.array([3, 1, 3, 0, 1, 5], dtype=np.int32)       # entries 2 and 4 repeat
+    keep = [0, 1, 3, 5]
+    # reference: the same call without the repeated entries
+    ref_cache = fresh_cache(cfg, hists)
+    ws = g.alloc_workspace(cfg, nseq * tmax)
+    ref = torch.full((len(keep), tmax, w.D), 2.5, dtype=torch.bfloat16, device="cuda")
+    g.ngram_embed_decode_rows(cfg, tables, ref_cache, dev(new[keep]), dev(n_new[keep]), ref, ws,
+                              slots=dev(slots[keep]), n_commit=dev(n_new[keep]))
+    torch.cuda.synchronize()
+    assert g.ngram_embed_read_error_flag(ws) == 0
+    cache = fresh_cache(cfg, hists)
+    ws2 = g.alloc_workspace(cfg, nseq * tmax)
+    out = torch.full((nseq, tmax, w.D), 2.5, dtype=torch.bfloat16, device="cuda")
+    g.ngram_embed_decode_rows(cfg, tables, cache, dev(new), dev(n_new), out, ws2,
+                              slots=dev(slots), n_commit=dev(n_new))
+    torch.cuda.synchronize()
+    fl = g.ngram_embed_read_error_flag(ws2)
+    assert fl & g.NGRAM_FLAG_DUP_SLOT and not fl & g.NGRAM_FLAG_BAD_SLOT
+    for i, b in enumerate(keep):
+        assert torch.equal(bits(out[b]), bits(ref[i])), b
+    for b in (2, 4):
+        assert bool((out[b] == 2.5).all()), b                   # nothing written
+    assert torch.equal(cache.len, ref_cache.len) and torch.equal(cache.ring, ref_cache.ring)
+    # commit_slots: the repeat is flagged and not appended
+    c1, c2 = fresh_cache(cfg, hists), fresh_cache(cfg, hists)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.ngram_cache_commit_slots(cfg, c1, dev(slots), dev(new), dev(n_new), err_flags=flags)
+    g.ngram_cache_commit_slots(cfg, c2, dev(slots[keep]), dev(new[keep]), dev(n_new[keep]))
+    torch.cuda.synchronize()
+    assert int(flags.item()) == g.NGRAM_FLAG_DUP_SLOT
+    assert torch.equal(c1.len, c2.len) and torch.equal(c1.ring, c2.ring)
+    # init_slots: the first sequence given a slot fills it
+    seqs = [np.arange(L, dtype=np.int32) + 7 * L for L in (5, 9, 2, 4, 1, 6)]
+    tok, cu = packed(seqs)
+    d1, d2 = fresh_cache(cfg, hists), fresh_cache(cfg, hists)
+    flags.zero_()
+    g.ngram_cache_init_slots(cfg, d1, dev(slots), dev(tok), dev(cu), err_flags=flags)
+    tk, ck = packed([seqs[i] for i in keep])
+    g.ngram_cache_init_slots(cfg, d2, dev(slots[keep]), dev(tk), dev(ck))
+    torch.cuda.synchronize()
+    assert int(flags.item()) == g.NGRAM_FLAG_DUP_SLOT
+    assert torch.equal(d1.len, d2.len) and torch.equal(d1.ring, d2.ring)
+
+
+def test_duplicate_check_across_blocks(lib):
+    """Repeats far apart in a large batch (the check runs over every earlier entry, across
+    the kernels' blocks): only the later copies are dropped."""
+    w = small_workload("bf16", D=256, N=3, K=2, V0=500)
+    E0, E, W = host_to_dev_tables(w)
+    cfg = g.Config(w.N, w.K, w.D, w.dtype, w.V0, list(w.V))
+    tables = g.Tables(E0, E, W)
+    nbatch, pool = 3000, 4000
+    rng = np.random.default_rng(8)
+    slots = rng.permutation(pool)[:nbatch].astype(np.int32)
+    dups = [(10, 2999), (700, 1500), (2048, 2049)]            # (earlier, later) entries
+    for a_, b_ in dups:
+        slots[b_] = slots[a_]
+    new = rng.integers(0, w.V0, size=(nbatch, 2)).astype(np.int32)
+    n_new = np.full(nbatch, 2, np.int32)
+    cache = g.Cache.empty(cfg, pool)
+    ws = g.alloc_workspace(cfg, nbatch * 2)
+    out = torch.full((nbatch, 2, w.D), 9.0, dtype=torch.bfloat16, device="cuda")
+    g.ngram_embed_decode_rows(cfg, tables, cache, dev(new), dev(n_new), out, ws,
+                              slots=dev(slots), n_commit=dev(n_new))
+    torch.cuda.synchronize()
+    assert g.ngram_embed_read_error_flag(ws) & g.NGRAM_FLAG_DUP_SLOT
+    written = (out != 9.0).flatten(1).any(dim=1).cpu().numpy()
+    later = {b_ for _, b_ in dups}
+    assert all(written[b] == (b not in later) for b in range(nbatch))
+    lens = cache.len.cpu().numpy()
+    assert int((lens == 2).sum()) == nbatch - len(dups)       # one commit per distinct slot
