@@ -27,6 +27,7 @@
 // Blocks are numbered so that the 32 blocks resident on one XCD at a time cover 4 row
 // tiles x 8 output tiles, which keeps their A rows and W panels in that XCD's L2.
 #include <algorithm>
+#include <atomic>
 
 #include "bf16.h"
 #include "kernels.h"
@@ -673,39 +674,60 @@ hipError_t run_mfma(ProjArgs a, int64_t nrows, int osz, hipStream_t st) {
 struct Route {
   int bm, bn;
 };
+// Compute units of the current device (the number of blocks one round of tiles occupies).
+int device_cus() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int dev = 0;
+  n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  cached.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 Route mfma_route(const ProjArgs& a, int32_t dtype, int om, int64_t nrows) {
   if (!(dtype == NGRAM_BF16 && a.N % kBN == 0 && a.d % kBK == 0 && a.K % kBK == 0))
     return {0, 0};
-  // Big batches: 256-row tiles (fewest re-reads of W); small batches (decode) use
-  // shorter tiles so that enough blocks exist to occupy the 256 CUs. A tile keeps its
-  // rows' hash indices (and E_0 tokens) in LDS.
-  const int64_t tiles_n = a.N / kBN;
-  const int64_t sp = om == kOutPartial ? a.splits : 1;
+  // A tile keeps its rows' hash indices (and E_0 tokens) in LDS.
   const int per_row = a.S + (om != kOutPartial ? 1 : 0);   // int32 per row
   const bool f256 = 256 * per_row * 4 <= IdxLds<256>::bytes;
   const bool f128 = 128 * per_row * 4 <= IdxLds<128>::bytes;
   const bool f64 = 64 * per_row * 4 <= IdxLds<64>::bytes;
-  const bool big = ((nrows + 255) / 256) * tiles_n * sp >= 512;
-  const bool mid = ((nrows + 127) / 128) * tiles_n * sp >= 256;
-  const int bm = big && f256 ? 256 : (big || mid) && f128 ? 128 : f64 ? 64 : f128 ? 128
-               : f256 ? 256 : 0;
-  if (om != kOutPartial) {
-    // a batch too small for 128 x 256 tiles to fill the chip (a decode step) takes 128 x 128
-    // tiles when those are enough blocks, rather than 64 x 256: the same blocks move less
-    // through L2 (each W panel is read by half as many row tiles, each gathered row by
-    // twice as many output tiles). 1280 rows of the 30B layer: 46.1 vs 48.7 us per step.
-    if (!big && !mid && f128 && a.N % 128 == 0 &&
-        ((nrows + 127) / 128) * (a.N / 128) * sp >= 192)
-      return {128, 128};
-    // fewer rows still (a draft-phase call: one row per sequence): 64 x 128 tiles when
-    // 64 x 256 tiles would leave the chip short of blocks. Each block's 48 slices then move
-    // 24 KB instead of 40 KB and twice as many CUs work: 256 rows of the 30B layer, 33.4 vs
-    // 43.4 us per call (64 x 64 tiles with 4 waves: 32.5 us, not worth another wave grid).
-    if (!big && !mid && bm == 64 && a.N % 128 == 0 &&
-        ((nrows + 63) / 64) * (a.N / 256) * sp < 192)
-      return {64, 128};
+  if (om == kOutPartial) {
+    // split contractions (the backward's dW): 256-row tiles once the ranges give 512 blocks
+    const int64_t tiles_n = a.N / kBN;
+    const bool big = ((nrows + 255) / 256) * tiles_n * a.splits >= 512;
+    const bool mid = ((nrows + 127) / 128) * tiles_n * a.splits >= 256;
+    const int bm = big && f256 ? 256 : (big || mid) && f128 ? 128 : f64 ? 64 : f128 ? 128
+                 : f256 ? 256 : 0;
+    return {bm, kBN};
   }
-  return {bm, kBN};
+  // The loads into LDS bound these kernels, and each CU takes its blocks one after another,
+  // so pick the tile whose busiest CU loads the fewest bytes: rounds of blocks over the CUs
+  // times (BM + BN) rows of the contraction per block. Larger tiles win ties. (Each output's
+  // sum order does not depend on the tile, so the choice never changes a bit.) The 30B
+  // layer's shapes: 64K rows -> 256 x 256 (12 rounds); 1280 decode rows -> 128 x 128 (240
+  // blocks, one round); 256 draft-phase rows -> 64 x 128; 16K rows of D = 1024 -> 256 x 256
+  // (one round of 256 blocks: 1 MB per CU, where two rounds of 128 x 256 took 1.5 MB).
+  static constexpr int kCand[5][2] = {{256, 256}, {128, 256}, {64, 256}, {128, 128}, {64, 128}};
+  const int64_t cus = device_cus();
+  Route best{0, 0};
+  int64_t best_cost = 0;
+  for (const auto& c : kCand) {
+    const bool fits = c[0] == 256 ? f256 : c[0] == 128 ? f128 : f64;
+    if (!fits || a.N % c[1] != 0) continue;
+    const int64_t blocks = ((nrows + c[0] - 1) / c[0]) * (a.N / c[1]) * a.layers;
+    const int64_t cost = ((blocks + cus - 1) / cus) * (c[0] + c[1]);
+    if (best.bm == 0 || cost < best_cost) {
+      best = {c[0], c[1]};
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 template <int OM>

@@ -121,9 +121,10 @@ def test_gather_bytes_exact(lib, w):
 
 
 # Small configurations: every row against the oracle. Row counts pick each tile shape of
-# the matrix-core kernel (D=1024 has 4 output tiles of 256): 64 x 128 (bm64: too few rows for
-# 64 x 256 tiles to fill the chip), 128 x 256, 256 x 256; 64 x 256 where 32 sub-tables'
-# indices do not fit a 128-row tile (s32); and ragged tails.
+# the matrix-core kernel (the tile whose busiest CU loads the fewest bytes; D=1024 has 4
+# output tiles of 256): 64 x 128 (bm64), 128 x 256 (bm128), 256 x 256 (bm256), 128 x 128
+# (n5k4); 64 x 256 where 32 sub-tables' indices do not fit a 128-row tile and 64 x 128 tiles
+# would take two rounds of the CUs (s32); and ragged tails.
 SMALL = [
     ("tiny_f32_full", WL.workload("tiny_f32"), None),
     ("f32_odd", small_workload("f32", D=96, N=4, K=2), (50, 1, 0, 201)),
@@ -133,7 +134,7 @@ SMALL = [
     ("bf16_mfma_bm256", small_workload("bf16", D=1024, N=3, K=2, V0=32000),
      (16384, 16384, 999)),
     ("bf16_mfma_n5k4", small_workload("bf16", D=2048, N=5, K=4, V0=131072), (1000, 37)),
-    ("bf16_mfma_bm64_s32", small_workload("bf16", D=2048, N=3, K=16, V0=4000), (1500, 1, 700)),
+    ("bf16_mfma_bm64_s32", small_workload("bf16", D=2048, N=3, K=16, V0=4000), (900, 1, 500)),
 ]
 
 
