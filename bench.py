@@ -528,6 +528,10 @@ def bench_basic(g, WL, dev, stream, steps):
     gbs_u = T * per_tok / t_u / 1e9
     res["uniform_ids_control"] = {"sum_us": round(t_u * 1e6, 1), "achieved_GBps": round(gbs_u, 1),
                                   "frac": round(gbs_u / HBM_PEAK_GBS, 4)}
+    tr_u = counter_traffic("basic_sum_uniform", "basic.hip", TRAFFIC_BASIC)
+    if tr_u is not None:
+        res["uniform_ids_control"]["traffic"] = tr_u
+        res["uniform_ids_control"]["counter_hbm_frac"] = round(tr_u / t_u / 1e9 / HBM_PEAK_GBS, 4)
     traffic = counter_traffic("basic_sum", "basic.hip", TRAFFIC_BASIC)
     res["roofline"]["traffic"] = traffic
     if traffic is not None:
@@ -877,6 +881,8 @@ def bench_decode(g, WL, cfg, tables, dev, stream, nsteps, with_cpu=False):
         log(f"decode cpu baseline {cpu['value']:.0f} tokens/s")
     fractions["traffic_decode_projection"] = counter_traffic(
         "decode_project", "project.hip", TRAFFIC_DECODE)
+    draft["traffic_row_call_projection"] = counter_traffic("draft_project", "project.hip",
+                                                           TRAFFIC_DECODE)
     return {"workload": DECODE_WORKLOAD, "steps": nsteps, "seqs": nseq, "ids_per_step": tmax,
             "tokens_per_s": round(toks / t, 1), "us_per_step_graph": round(t_step * 1e6, 2),
             "us_per_step_eager": round(eager_us, 2), "replays": len(times),
@@ -914,7 +920,8 @@ def bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, steps):
     alg_b = read_b + T * w.S * 4 + T * 4            # rows, indices read, checksums written
     res = {"kernel": "gather_lds_kernel", "loader": "global_load_lds_dwordx4 (HBM -> LDS)",
            "bytes_read_rows": read_b, "bytes_algorithmic": alg_b,
-           "traffic": counter_traffic("gather_lds", "gather.hip")}
+           "traffic": counter_traffic("gather_lds", "gather.hip"),
+           "traffic_uniform_ids": counter_traffic("gather_lds_uniform", "gather.hip")}
     for name, ids in (("zipf", toks), ("uniform_ids_control", uni)):
         for r in range(len(ids)):
             g.ngram_embed_hash(cfg, ids[r], cu, idx[r], None, stream=stream)
@@ -927,6 +934,9 @@ def bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, steps):
                      "read_GBps": round(read_b / t / 1e9, 1),
                      "algorithmic_GBps": round(alg_b / t / 1e9, 1),
                      "frac_of_hbm_peak": round(alg_b / t / 1e9 / HBM_PEAK_GBS, 4)}
+        tr = res["traffic" if name == "zipf" else "traffic_uniform_ids"]
+        if tr is not None:
+            res[name]["counter_hbm_frac"] = round(tr / t / 1e9 / HBM_PEAK_GBS, 4)
         log(f"gather into LDS, {name}: {t*1e6:.1f} us = {alg_b/t/1e9:.0f} GB/s "
             f"({alg_b/t/1e9/HBM_PEAK_GBS:.1%} of HBM peak)")
     res["frac_of_hbm_peak"] = res["zipf"]["frac_of_hbm_peak"]

@@ -8,18 +8,24 @@ import bench
 def test_counter_traffic_reads_committed_summary():
     """The summary's byte counts are returned while its stored source digests match the
     sources, for both kernels it covers."""
-    kv = {}
-    for ln in open(bench.TRAFFIC_FILE):
-        if ln.startswith(("project", "gather")) and "bytes_per_launch" in ln:
-            name, val = ln.split(" hbm_bytes_per_launch: ")
-            kv[name] = float(val)
-    assert set(kv) == {"project", "gather"}
-    for kernel, src in (("project", "project.hip"), ("gather", "gather.hip")):
-        stored = [ln.rsplit(": ", 1)[1].strip() for ln in open(bench.TRAFFIC_FILE)
-                  if ln.startswith(f"{src} sha256[:16]: ")]
-        assert len(stored) == 1
-        want = kv[kernel] if stored[0] == bench.source_digest(src) else None
-        assert bench.counter_traffic(kernel, src) == want
+    cases = {bench.TRAFFIC_FILE: (("project", "project.hip"), ("gather", "gather.hip"),
+                                  ("gather_lds", "gather.hip"), ("gather_lds_uniform", "gather.hip")),
+             bench.TRAFFIC_DECODE: (("decode_project", "project.hip"),
+                                    ("draft_project", "project.hip")),
+             bench.TRAFFIC_BASIC: (("basic_sum", "basic.hip"), ("basic_sum_uniform", "basic.hip"))}
+    for path, kernels in cases.items():
+        kv = {}
+        for ln in open(path):
+            if "hbm_bytes_per_launch" in ln and not ln.startswith("#"):
+                name, val = ln.split(" hbm_bytes_per_launch: ")
+                kv[name] = float(val)
+        assert set(kv) == {k for k, _ in kernels}, path
+        for kernel, src in kernels:
+            stored = [ln.rsplit(": ", 1)[1].strip() for ln in open(path)
+                      if ln.startswith(f"{src} sha256[:16]: ")]
+            assert len(stored) == 1
+            want = kv[kernel] if stored[0] == bench.source_digest(src) else None
+            assert bench.counter_traffic(kernel, src, path) == want
 
 
 def test_counter_traffic_rejects_other_source(tmp_path, monkeypatch):
