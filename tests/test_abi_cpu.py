@@ -468,7 +468,7 @@ def test_lds_dma_m0_is_an_operand():
         res = subprocess.run(cmd, capture_output=True, text=True, check=True)
         assert "reserved registers" not in res.stderr, src
         lines += [ln.strip() for ln in res.stdout.splitlines()]
-    dma = [i for i, ln in enumerate(lines) if ln.startswith("global_load_lds_dwordx4")]
+    dma = [i for i, ln in enumerate(lines) if ln.startswith("global_load_lds_dword")]
     assert dma, "no LDS-DMA loads found"
     for i in dma:
         assert lines[i - 1] == "s_nop 0", lines[i - 3:i + 1]

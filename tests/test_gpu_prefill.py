@@ -324,6 +324,10 @@ LDS_CASES = [
     ("bf16_d1024", small_workload("bf16", D=1024, N=3, K=2, V0=32000), 1001),
     ("bf16_d2048_s16", small_workload("bf16", D=2048, N=5, K=4, V0=131072), 333),
     ("bf16_d3072_s12", small_workload("bf16", D=3072, N=4, K=4, V0=131072), 4097),
+    # more groups of 5 rows than waves (2048): several groups per wave, a ragged last group
+    ("bf16_d3072_s12_multi", small_workload("bf16", D=3072, N=4, K=4, V0=131072), 24003),
+    ("bf16_d3072_s12_one_row", small_workload("bf16", D=3072, N=4, K=4, V0=131072), 1),
+    ("bf16_d1024_three_rows", small_workload("bf16", D=1024, N=3, K=2, V0=32000), 3),
     ("basic_d3072", WL.Workload("basic_lds", "bf16", 5000, 3072, 4, 1,
                                 tuple(WL.mid_gap_primes(5000, 15000, 3)), 1, 1, "uniform", 12,
                                 form="basic"), 130),
