@@ -907,7 +907,8 @@ def bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, steps):
     """Kernel 2 in the form the projection runs it: the sub-table rows of a 64K-token batch
     from HBM straight into LDS with the projection's 16-byte-per-lane LDS loads, reduced
     there to one checksum per row (4 bytes written per row). Zipf(1.1) ids (the workload)
-    and uniform ids (no repeats within a batch to hit in cache), four batches rotated."""
+    and uniform ids (no repeats within a batch to hit in cache), four batches rotated; and
+    contiguous rows, the loader's ceiling on this layout (a control, not the workload)."""
     import numpy as np
     import torch
 
@@ -922,8 +923,16 @@ def bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, steps):
            "bytes_read_rows": read_b, "bytes_algorithmic": alg_b,
            "traffic": counter_traffic("gather_lds", "gather.hip"),
            "traffic_uniform_ids": counter_traffic("gather_lds_uniform", "gather.hip")}
-    for name, ids in (("zipf", toks), ("uniform_ids_control", uni)):
-        for r in range(len(ids)):
+    # the loader's own ceiling: every sub-table read as one contiguous run of rows (row
+    # r + k T of each sub-table in batch k, so the four batches share no line)
+    seq = [torch.stack([torch.arange(k * T, (k + 1) * T, dtype=torch.int32, device=dev)] * w.S,
+                       dim=1).contiguous() for k in range(len(toks))]
+    for name, ids in (("zipf", toks), ("uniform_ids_control", uni),
+                      ("sequential_rows_control", None)):
+        if ids is None:
+            for r in range(len(seq)):
+                idx[r].copy_(seq[r])
+        for r in range(len(ids) if ids is not None else 0):
             g.ngram_embed_hash(cfg, ids[r], cu, idx[r], None, stream=stream)
         for k in range(3):
             g.ngram_embed_gather_checksum(cfg, tables, idx[k % len(idx)], sums, stream=stream)
@@ -934,7 +943,7 @@ def bench_gather_lds(g, WL, w, cfg, tables, toks, cu, dev, stream, steps):
                      "read_GBps": round(read_b / t / 1e9, 1),
                      "algorithmic_GBps": round(alg_b / t / 1e9, 1),
                      "frac_of_hbm_peak": round(alg_b / t / 1e9 / HBM_PEAK_GBS, 4)}
-        tr = res["traffic" if name == "zipf" else "traffic_uniform_ids"]
+        tr = {"zipf": res["traffic"], "uniform_ids_control": res["traffic_uniform_ids"]}.get(name)
         if tr is not None:
             res[name]["counter_hbm_frac"] = round(tr / t / 1e9 / HBM_PEAK_GBS, 4)
         log(f"gather into LDS, {name}: {t*1e6:.1f} us = {alg_b/t/1e9:.0f} GB/s "
