@@ -1,13 +1,15 @@
-// Kernel 2 (stand-alone form): G[r, s*d : (s+1)*d] = E_{n,k}[idx[r, s], :].
+// Kernel 2 alone: the row reads G[r, s*d : (s+1)*d] = E_{n,k}[idx[r, s], :].
 //
 // This is the row read of the final form in section A2 of the deep-notes page on "Scaling
 // Embeddings Outperforms Scaling Experts in Language Models": every position reads one
 // d-wide row from each of the (N-1)K sub-tables, so the traffic is (N-1)K*d = D elements
 // per position whatever the table sizes (section 4.1: lookup cost follows the token count).
-// The projection kernel performs the same reads straight into LDS; this kernel writes them
-// to HBM and is the bandwidth probe of the gather.
+// The projection kernel performs these reads straight into LDS. Two stand-alone forms:
+// gather_kernel writes G to HBM (ngram_embed_gather), and gather_lds_kernel lands the rows
+// in LDS with the projection's loader and keeps one checksum per row
+// (ngram_embed_gather_checksum), the bandwidth probe of the gather as the path runs it.
 //
-// Layout on MI355X: idx [rows, S] and G [rows, S*d] list the (row, sub-table) pairs in the
+// Layout of the HBM form on MI355X: idx [rows, S] and G [rows, S*d] list the (row, sub-table) pairs in the
 // same order, so G is a flat array of pair segments: 16-byte chunk `item` of G is chunk
 // item % cpr of pair item / cpr. Consecutive lanes take consecutive chunks: every table row
 // is read as one contiguous piece and every write is fully sequential. Stores are

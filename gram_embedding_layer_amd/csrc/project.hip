@@ -9,12 +9,13 @@
 // the only dense work on the path. Both operands are contiguous along the contraction
 // axis, which is the layout the matrix cores want.
 //
-// bf16 path (D % 256 == 0, d % 64 == 0): tiles of BM rows x 256 outputs, 64-deep slices.
+// bf16 path (D % 256 == 0, d % 64 == 0): tiles of BM rows x BN outputs (BN = 256, or 128
+// for small batches), 64-deep slices.
 // A 64-deep slice never straddles two sub-tables, so for each of the BM rows the A-loader
 // reads one 128-byte piece (a full L2 line) of one sub-table row straight from HBM into
 // LDS (global_load_lds_dwordx4; no gathered copy of the batch is ever written). W slices
-// travel the same way. Slices sit in XOR-swizzled LDS buffers (2 for 256-row tiles, 3 for
-// shorter ones); the loads of the next slice fly while 8 waves (2 per SIMD) multiply the
+// travel the same way. Slices sit in XOR-swizzled LDS buffers (2 for 256-row tiles, 3 or 4
+// for shorter ones); the loads of the next slice fly while 8 waves (2 per SIMD) multiply the
 // current one with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Waits and barriers are
 // explicit, so loads stay in flight across them. The epilogue adds the E_0 row, scales by
 // 1/(S+1) (times the output factor of the scale amplification, section 3.2.4) in fp32 and
