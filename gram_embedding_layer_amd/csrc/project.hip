@@ -98,14 +98,15 @@ template <int BM> struct IdxLds {
 
 // Contraction depth of one slice (BK = 64: a full 128-byte L2 line of each row per load)
 // and LDS slice buffers (NST; 160 KB of LDS per CU): 256-row tiles double-buffer, shorter
-// tiles keep two slices in flight, 64 x 128 tiles (the smallest batches) three: 256 rows of
-// the 30B layer, 29.8 vs 33.1 us per call (four in flight: 31.3 us; 128 x 128 decode tiles
-// gain nothing from a third: 43.4 vs 43.2 us per step). Measured on the 64K-token batch and
+// tiles keep two slices in flight, 64-row tiles of 128 or 64 outputs (the smallest batches)
+// three: 256 rows of the 30B layer in 64 x 128 tiles, 29.8 vs 33.1 us per call (four in
+// flight: 31.3 us; 64 x 64 tiles: 26.8 vs 24.4 us; 128 x 128 decode tiles gain nothing from
+// a third: 43.4 vs 43.2 us per step). Measured on the 64K-token batch and
 // not adopted: 32-deep slices with four buffers (twice the barriers, half-line loads): 1365
 // vs 1251 us; for small batches, 128-deep slices (two buffers): slower by 12-14%.
 template <int BM, int BN> struct Tile {
   static constexpr int BK = 64;
-  static constexpr int NST = BM >= 256 ? 2 : (BM == 64 && BN == 128) ? 4 : 3;
+  static constexpr int NST = BM >= 256 ? 2 : (BM == 64 && BN <= 128) ? 4 : 3;
   static_assert(NST * (BM + BN) * BK * 2 + IdxLds<BM>::bytes <= 163840,
                 "the slice buffers and the tile's indices must fit the LDS");
 };
@@ -120,11 +121,14 @@ __device__ __forceinline__ void wait_loads_and_meet() {
 }
 
 // Wave grid of a tile: 8 waves (2 per SIMD, so one can issue while the other waits on
-// memory), WGM along rows x 8/WGM along outputs; each wave owns a WM x WN block of
-// 32x32 matrix-core tiles.
+// memory), all loading; the NWC that multiply lie WGM along rows x NWC/WGM along outputs,
+// each owning a WM x WN block of 32x32 matrix-core tiles.
 // (16 waves of 64x64 outputs, 4 per SIMD in 122 VGPRs, measured the same: 1214 vs 1212 us.)
 template <int BM, int BN> struct WaveGrid {
   static constexpr int NW = 8;   // waves per block
+  // waves that multiply: 64 x 64 tiles (the smallest batches) have four 32 x 32 blocks, and
+  // the other four waves only load (a CU's load rate grows with the waves issuing loads)
+  static constexpr int NWC = BM == 64 && BN == 64 ? 4 : NW;
   static constexpr int WGM = BM >= 128 ? 4 : 2;
 };
 
@@ -139,7 +143,8 @@ __global__ __launch_bounds__((WaveGrid<BM, BN>::NW * 64), 1) void proj_mfma_kern
   constexpr int NW = WaveGrid<BM, BN>::NW;
   constexpr int NT = NW * 64;            // threads per block
   constexpr int WGM = WaveGrid<BM, BN>::WGM;
-  constexpr int WGN = NW / WGM;
+  constexpr int NWC = WaveGrid<BM, BN>::NWC;
+  constexpr int WGN = NWC / WGM;
   constexpr int AR = BM / NW;            // A rows each wave loads
   constexpr int BR = BN / NW;            // W rows each wave loads
   constexpr int WM = BM / WGM;           // rows per wave
@@ -189,7 +194,8 @@ __global__ __launch_bounds__((WaveGrid<BM, BN>::NW * 64), 1) void proj_mfma_kern
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w / WGN, wn = w % WGN;
+  const bool mult = NWC == NW || w < NWC;   // this wave multiplies (else it only loads)
+  const int wm = mult ? w / WGN : 0, wn = mult ? w % WGN : 0;
 
   // -- hash indices of the tile's rows (rows past the batch repeat the last row), and the
   //    rows' E_0 tokens for the epilogue (-1 past the batch; 0 without E_0)
@@ -363,7 +369,12 @@ __global__ __launch_bounds__((WaveGrid<BM, BN>::NW * 64), 1) void proj_mfma_kern
     else if (NST >= 3 && ahead >= 1) wait_loads_and_meet<(NST >= 3 ? 1 : 0) * PER_SLICE>();
     else wait_loads_and_meet<0>();
     const char* sp = lds + (k % NST) * STAGE;
-    if constexpr (kInterleave) {
+    if (!mult) {
+      if (loads) {
+#pragma unroll
+        for (int q = 0; q < PER_SLICE; ++q) dma(q);
+      }
+    } else if constexpr (kInterleave) {
       // the first k-step's fragments in the order its ops use them, so the first op waits
       // for two reads rather than five (1131-1132 vs 1137-1146 us, bitwise equal)
 #pragma unroll
@@ -413,32 +424,35 @@ __global__ __launch_bounds__((WaveGrid<BM, BN>::NW * 64), 1) void proj_mfma_kern
   // waves meet (1094-1101 vs 1102-1107 us, bitwise equal)
   ev_t ev_all[OM != kOutPartial ? TI : 1][NIT];
   if constexpr (OM != kOutPartial) {
-    const int n = n0 + wn * WN + ec * VO;
-    int32_t tka[TI][NIT];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) tka[i][it] = stok[wm * WM + i * 32 + it * RPI + er];
-    if (E0 != nullptr) {
-      // rows with an invalid token read row 0 (their outputs are zeros or not written)
+    if (mult) {   // load-only waves write no outputs
+      const int n = n0 + wn * WN + ec * VO;
+      int32_t tka[TI][NIT];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int32_t tk = uint32_t(tka[i][it]) < uint32_t(a.V0) ? tka[i][it] : 0;
-          ev_all[i][it] = *reinterpret_cast<const ev_t*>(E0 + int64_t(tk) * a.N + n);
-        }
-    } else {
+        for (int it = 0; it < NIT; ++it) tka[i][it] = stok[wm * WM + i * 32 + it * RPI + er];
+      if (E0 != nullptr) {
+        // rows with an invalid token read row 0 (their outputs are zeros or not written)
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) ev_all[i][it] = ev_t{};
+          for (int it = 0; it < NIT; ++it) {
+            const int32_t tk = uint32_t(tka[i][it]) < uint32_t(a.V0) ? tka[i][it] : 0;
+            ev_all[i][it] = *reinterpret_cast<const ev_t*>(E0 + int64_t(tk) * a.N + n);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) ev_all[i][it] = ev_t{};
+      }
     }
   }
   // Every wave is done with the slice buffers before any stages its results there. No slice
   // load is in flight (the last slice waited for all of them), so the waves meet after their
   // LDS reads only; a __syncthreads would also wait for the E_0 requests above.
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (!mult) return;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -712,9 +726,12 @@ Route mfma_route(const ProjArgs& a, int32_t dtype, int om, int64_t nrows) {
   // times (BM + BN) rows of the contraction per block. Larger tiles win ties. (Each output's
   // sum order does not depend on the tile, so the choice never changes a bit.) The 30B
   // layer's shapes: 64K rows -> 256 x 256 (12 rounds); 1280 decode rows -> 128 x 128 (240
-  // blocks, one round); 256 draft-phase rows -> 64 x 128; 16K rows of D = 1024 -> 256 x 256
+  // blocks, one round); 256 draft-phase rows -> 64 x 64 (192 blocks of 0.79 MB, where 96
+  // blocks of 64 x 128 loaded 1.18 MB each: 24.4 vs 30.1 us per call, since the four
+  // load-only waves keep a CU's load rate that of eight); 16K rows of D = 1024 -> 256 x 256
   // (one round of 256 blocks: 1 MB per CU, where two rounds of 128 x 256 took 1.5 MB).
-  static constexpr int kCand[5][2] = {{256, 256}, {128, 256}, {64, 256}, {128, 128}, {64, 128}};
+  static constexpr int kCand[6][2] = {{256, 256}, {128, 256}, {64, 256}, {128, 128}, {64, 128},
+                                      {64, 64}};
   const int64_t cus = device_cus();
   Route best{0, 0};
   int64_t best_cost = 0;
@@ -739,6 +756,7 @@ hipError_t dispatch(Route r, const ProjArgs& a, int64_t nrows, int osz, hipStrea
   if constexpr (OM != kOutPartial) {
     if (r.bm == 128 && r.bn == 128) return run_mfma<128, OM, 128>(a, nrows, osz, st);
     if (r.bm == 64 && r.bn == 128) return run_mfma<64, OM, 128>(a, nrows, osz, st);
+    if (r.bm == 64 && r.bn == 64) return run_mfma<64, OM, 64>(a, nrows, osz, st);
   }
   return hipErrorInvalidValue;
 }

@@ -122,13 +122,15 @@ def test_gather_bytes_exact(lib, w):
 
 # Small configurations: every row against the oracle. Row counts pick each tile shape of
 # the matrix-core kernel (the tile whose busiest CU loads the fewest bytes; D=1024 has 4
-# output tiles of 256): 64 x 128 (bm64), 128 x 256 (bm128), 256 x 256 (bm256), 128 x 128
-# (n5k4); 64 x 256 where 32 sub-tables' indices do not fit a 128-row tile and 64 x 128 tiles
-# would take two rounds of the CUs (s32); and ragged tails.
+# output tiles of 256): 64 x 64 with its load-only waves (bm64_bn64: 12 row tiles x 16 output
+# tiles, one round of the CUs), 64 x 128 (bm64), 128 x 256 (bm128), 256 x 256 (bm256),
+# 128 x 128 (n5k4); 64 x 256 where 32 sub-tables' indices do not fit a 128-row tile and
+# 64 x 128 tiles would take two rounds of the CUs (s32); and ragged tails.
 SMALL = [
     ("tiny_f32_full", WL.workload("tiny_f32"), None),
     ("f32_odd", small_workload("f32", D=96, N=4, K=2), (50, 1, 0, 201)),
     ("bf16_generic_d32", small_workload("bf16", D=128, N=3, K=2), (300, 2, 77)),
+    ("bf16_mfma_bm64_bn64", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (300, 1, 0, 450)),
     ("bf16_mfma_bm64", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (700, 1, 0, 1301)),
     ("bf16_mfma_bm128", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (4000, 4100, 3)),
     ("bf16_mfma_bm256", small_workload("bf16", D=1024, N=3, K=2, V0=32000),
