@@ -78,6 +78,7 @@ def run(cfg, tables, tokens, cu, dtype):
 CASES = [
     ("f32_generic", small_workload("f32", D=96, N=4, K=2), (50, 1, 0, 201)),
     ("bf16_generic_d32", small_workload("bf16", D=128, N=3, K=2), (300, 2, 77)),
+    ("bf16_mfma_bm64_bn64", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (300, 1, 0, 450)),
     ("bf16_mfma_bm64", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (700, 1, 0, 1301)),
     ("bf16_mfma_bm128", small_workload("bf16", D=1024, N=3, K=2, V0=32000), (4000, 4100, 3)),
     ("bf16_mfma_bm256", small_workload("bf16", D=1024, N=3, K=2, V0=32000),
