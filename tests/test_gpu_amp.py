@@ -89,6 +89,10 @@ CASES = [
     # D = 3072, fp32 past D = 1024): the parameters are loaded where they are used
     ("bf16_wide_d4096", small_workload("bf16", D=4096, N=3, K=2), (300, 7)),
     ("f32_wide_d2048", small_workload("f32", D=2048, N=2, K=1), (90, 3)),
+    # the widest rows of the pass: 24 and 32 vectors per lane (up to D = 8192)
+    ("f32_wide_d5120", small_workload("f32", D=5120, N=3, K=2), (20, 3)),
+    ("bf16_wide_d6144", small_workload("bf16", D=6144, N=3, K=2), (40, 7)),
+    ("bf16_wide_d8192", small_workload("bf16", D=8192, N=3, K=2), (30, 5)),
 ]
 MODES = [("scale", None, False), ("scale", -0.75, False), ("layernorm", None, False),
          ("layernorm", None, True)]
