@@ -1,5 +1,5 @@
-"""Host-side pieces of bench.py: the lookup of the committed HBM counter summary that fills
-the roofline's `traffic` field (no GPU needed)."""
+"""Host-side pieces of bench.py (no GPU needed): the lookup of the committed HBM counter
+summary that fills the roofline's `traffic` field, and the refusal of more than one GPU."""
 import os
 
 import bench
@@ -42,3 +42,15 @@ def test_counter_traffic_rejects_other_source(tmp_path, monkeypatch):
     assert bench.counter_traffic("project", "project.hip") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", os.path.join(str(tmp_path), "missing.txt"))
     assert bench.counter_traffic("gather", "gather.hip") is None
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    """`--gpus N` with N > 1 exits with a message (status 2) and touches no device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
